@@ -1,0 +1,106 @@
+"""Plain float64 CPU oracle of one Muon optimizer step.
+
+TEST INFRASTRUCTURE.  This module exists to check the GPU library; only the
+tests, the smoke check and the benchmark's CPU-baseline leg may use it.  It
+shares no code, constant table or helper with the GPU path, and the GPU
+path never imports it.
+
+What it computes follows "Muon: An optimizer for hidden layers in neural
+networks", the synthesis note on papers.chlience.com, section 4 (the
+algorithm definition): a momentum buffer accumulates the gradient, the
+momentum matrix is orthogonalised by a quintic Newton-Schulz iteration
+after Frobenius normalisation (working on the transpose when that makes the
+Gram matrix smaller), and the weights move against the orthogonalised
+direction scaled by the learning rate.
+
+Everything is float64; inputs are widened exactly.  Every matrix product is
+a plain numpy ``@``; there is no blocking, fusion or reordering.
+
+Readings where the page is silent (all listed again in the design notes):
+
+* Nesterov: the page says implementations often use a Nesterov-style
+  momentum but gives no formula.  Default: the Newton-Schulz input is the
+  momentum buffer itself.  With ``nesterov=True`` the input is
+  ``G + mu * B_new``.
+* The Frobenius normalisation divides by ``||M||_F + eps`` (eps = 1e-7); a
+  zero matrix therefore gives a zero direction.
+* Transpose exactly when rows > cols; a square matrix is not transposed.
+* ``scale`` is a caller-supplied per-matrix multiplier of the learning rate
+  (the "consistent update RMS" adjustment of the Moonlight results section
+  has no formula on the pages).
+
+Parity pins (tests/test_oracle_pins.py) tie every function here to
+mathematics rather than to itself: the SVD closed form of the iteration,
+transpose equivariance, singular vectors, the polynomial band, rank-one,
+partial-permutation and zero special cases, the momentum closed form and
+the update's linearity.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+# Tuned quintic coefficients (a, b, c), page 5, section 4.
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def momentum(B: np.ndarray, G: np.ndarray, mu: float, nesterov: bool = False
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """Momentum accumulation, section 4: ``B_t = mu * B_{t-1} + G_t``.
+
+    Returns ``(B_t, M)`` where ``M`` is the matrix handed to the
+    orthogonalisation: ``B_t`` itself, or ``G + mu * B_t`` for the
+    Nesterov-style reading.
+    """
+    B = np.asarray(B, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    B_new = mu * B + G
+    M = G + mu * B_new if nesterov else B_new
+    return B_new, M
+
+
+def frobenius_normalize(M: np.ndarray, eps: float = 1e-7) -> np.ndarray:
+    """Divide by the Frobenius norm plus eps (section 4, last paragraph)."""
+    M = np.asarray(M, dtype=np.float64)
+    return M / (np.sqrt(np.sum(M * M)) + eps)
+
+
+def newton_schulz(M: np.ndarray, steps: int = 5, eps: float = 1e-7,
+                  coeffs=NS_COEFFS) -> np.ndarray:
+    """Quintic Newton-Schulz orthogonalisation of one matrix (section 4).
+
+    Normalise by the Frobenius norm, work on the transpose when the matrix
+    has more rows than columns (so X X^T is the smaller Gram matrix), then
+    repeat ``steps`` times
+
+        A = X X^T
+        X = a X + b A X + c A A X
+
+    and map back to the input's orientation.  ``b A X + c A A X`` is formed
+    as ``(b A + c A A) X``, which is the same polynomial.
+    """
+    a, b, c = coeffs
+    X = frobenius_normalize(M, eps)
+    transposed = X.shape[0] > X.shape[1]
+    if transposed:
+        X = X.T.copy()
+    for _ in range(steps):
+        A = X @ X.T
+        P = b * A + c * (A @ A)
+        X = a * X + P @ X
+    return X.T.copy() if transposed else X
+
+
+def apply_update(W: np.ndarray, O: np.ndarray, lr: float, scale: float = 1.0) -> np.ndarray:
+    """Parameter update, section 4: ``W_{t+1} = W_t - lr * scale * O_t``."""
+    return np.asarray(W, dtype=np.float64) - (lr * scale) * np.asarray(O, dtype=np.float64)
+
+
+def muon_step(W: np.ndarray, G: np.ndarray, B: np.ndarray, mu: float, lr: float,
+              scale: float = 1.0, ns_steps: int = 5, nesterov: bool = False,
+              eps: float = 1e-7):
+    """One Muon step on one matrix.  Returns ``(W_new, B_new, O)`` in float64."""
+    B_new, M = momentum(B, G, mu, nesterov)
+    O = newton_schulz(M, ns_steps, eps)
+    return apply_update(W, O, lr, scale), B_new, O

@@ -1,0 +1,231 @@
+"""Pins of the CPU oracle to mathematics (no GPU).
+
+Each test fixes part of ``oracle.muon_oracle`` against something other than
+the oracle itself: the coefficients printed on the Muon synthesis note
+(page 5, section 4; ``tests/golden/ns_coefficients.txt``), the singular
+value decomposition, scalar iteration of the quintic, exact special cases
+and closed forms.  A dropped term, a wrong sign or coefficient, a missing
+transpose, the wrong norm or a wrong momentum recurrence fails at least one.
+"""
+import numpy as np
+import pytest
+
+from conftest import load_golden_coefficients
+from oracle import muon_oracle as orc
+from synth import signed_partial_permutation
+
+GOLD = load_golden_coefficients()
+A, B, C = GOLD["a"], GOLD["b"], GOLD["c"]
+EPS = 1e-7
+
+
+def p(x):
+    """The scalar quintic the iteration applies to every singular value."""
+    return A * x + B * x ** 3 + C * x ** 5
+
+
+def p_iter(x, k):
+    for _ in range(k):
+        x = p(x)
+    return x
+
+
+def svd_closed_form(M, steps, eps=EPS):
+    """U diag(p^k(s_i / (||M||_F + eps))) V^T, via numpy's SVD."""
+    U, s, Vt = np.linalg.svd(M, full_matrices=False)
+    nrm = np.sqrt(np.sum(M * M))
+    return (U * p_iter(s / (nrm + eps), steps)) @ Vt
+
+
+def rel(a, b):
+    d = np.linalg.norm(a - b)
+    n = np.linalg.norm(b)
+    return d / n if n > 0 else d
+
+
+# ------------------------------------------------------------------ coefficients
+def test_coefficients_match_page():
+    assert orc.NS_COEFFS == (A, B, C)
+    assert int(GOLD["steps"]) == 5
+
+
+def test_default_step_count_is_five():
+    rng = np.random.default_rng(7)
+    M = rng.standard_normal((6, 9))
+    assert np.allclose(orc.newton_schulz(M), orc.newton_schulz(M, steps=5), rtol=0, atol=0)
+
+
+# ------------------------------------------------------------------ SVD closed form
+SHAPES = [(1, 1), (1, 7), (7, 1), (2, 3), (3, 2), (5, 5), (8, 3), (3, 8), (17, 33), (33, 17), (16, 16)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("scale", [1e-3, 1.0, 1e3])
+@pytest.mark.parametrize("steps", [0, 1, 2, 5, 6])
+def test_ns_equals_svd_closed_form(shape, scale, steps):
+    rng = np.random.default_rng([shape[0], shape[1], steps, int(np.log10(scale)) + 5])
+    M = scale * rng.standard_normal(shape)
+    O = orc.newton_schulz(M, steps)
+    ref = svd_closed_form(M, steps)
+    assert O.shape == M.shape
+    assert rel(O, ref) <= 1e-12
+
+
+def test_eps_is_part_of_the_normalisation():
+    # A matrix of Frobenius norm 1e-6: eps shifts every s_i by ~9 %, far
+    # outside round-off, so dropping eps (or using another) fails here.
+    rng = np.random.default_rng(11)
+    M = rng.standard_normal((4, 6))
+    M *= 1e-6 / np.linalg.norm(M)
+    O = orc.newton_schulz(M, 5)
+    assert rel(O, svd_closed_form(M, 5, eps=EPS)) <= 1e-12
+    assert rel(O, svd_closed_form(M, 5, eps=0.0)) > 1e-3
+
+
+def test_normalisation_is_frobenius_not_spectral():
+    rng = np.random.default_rng(12)
+    M = rng.standard_normal((6, 10))
+    X = orc.frobenius_normalize(M, 0.0)
+    assert abs(np.sum(X * X) - 1.0) <= 1e-14
+    X_eps = orc.frobenius_normalize(M, EPS)
+    nrm = np.sqrt(np.sum(M * M))
+    assert np.allclose(X_eps, M / (nrm + EPS), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------ invariants
+@pytest.mark.parametrize("shape", [(9, 4), (4, 9), (12, 12)])
+def test_transpose_equivariance(shape):
+    rng = np.random.default_rng(list(shape))
+    M = rng.standard_normal(shape)
+    assert rel(orc.newton_schulz(M.T, 5), orc.newton_schulz(M, 5).T) <= 1e-12
+
+
+@pytest.mark.parametrize("shape", [(10, 6), (6, 10), (8, 8)])
+def test_singular_vectors_preserved(shape):
+    rng = np.random.default_rng([3] + list(shape))
+    # Well separated singular values so the SVD basis is unique.
+    k = min(shape)
+    U, _ = np.linalg.qr(rng.standard_normal((shape[0], k)))
+    V, _ = np.linalg.qr(rng.standard_normal((shape[1], k)))
+    s = np.linspace(1.0, 0.1, k)
+    M = (U * s) @ V.T
+    O = orc.newton_schulz(M, 5)
+    D = U.T @ O @ V
+    off = D - np.diag(np.diag(D))
+    assert np.max(np.abs(off)) <= 1e-12
+    expect = p_iter(s / (np.sqrt(np.sum(s * s)) + EPS), 5)
+    assert np.allclose(np.diag(D), expect, rtol=1e-12, atol=1e-13)
+
+
+def test_band_after_five_steps():
+    # p maps [0.6818, 1.2024] into itself, and every s >= 1.505e-3 enters it
+    # within five steps; so every singular value of the output lies in the
+    # band whenever the input's smallest normalised singular value does.
+    rng = np.random.default_rng(5)
+    for shape in [(32, 48), (48, 32), (40, 40)]:
+        M = rng.standard_normal(shape)
+        nrm = np.sqrt(np.sum(M * M))
+        smin = np.linalg.svd(M, compute_uv=False).min() / nrm
+        assert smin >= 1.505e-3
+        sv = np.linalg.svd(orc.newton_schulz(M, 5), compute_uv=False)
+        assert sv.min() >= 0.6818 - 1e-9 and sv.max() <= 1.2024 + 1e-9
+    xs = np.linspace(0.6818, 1.2024, 20001)
+    ys = p(xs)
+    assert ys.min() >= 0.6818 - 1e-6 and ys.max() <= 1.2024
+
+
+# ------------------------------------------------------------------ special cases
+def test_rank_one():
+    rng = np.random.default_rng(21)
+    u = rng.standard_normal(13)
+    v = rng.standard_normal(7)
+    M = 1e3 * np.outer(u, v)
+    O = orc.newton_schulz(M, 5)
+    uh = u / np.linalg.norm(u)
+    vh = v / np.linalg.norm(v)
+    s = np.linalg.norm(M) / (np.linalg.norm(M) + EPS)
+    assert rel(O, p_iter(s, 5) * np.outer(uh, vh)) <= 1e-12
+    # Values of the composed polynomial at 1, for the record.
+    seq = [p_iter(1.0, k) for k in range(6)]
+    assert np.allclose(seq, [1.0, 0.701, 1.113620, 0.720706, 1.089974, 0.696436], atol=5e-7)
+
+
+@pytest.mark.parametrize("j,value", [(3, 0.688140), (4, 1.070524), (5, 1.132924), (6, 0.902526)])
+def test_signed_partial_permutation(j, value):
+    # 4^j entries of +-1 in distinct rows and columns: all 4^j singular values
+    # equal 1, ||M||_F = 2^j, so O = p^5(2^-j) * M exactly (up to eps).
+    n = 4 ** j
+    M = signed_partial_permutation(n + 3, n + 9, n, [j, 1]).astype(np.float64)
+    O = orc.newton_schulz(M, 5)
+    expect = p_iter(2.0 ** j / (2.0 ** j + EPS) * 2.0 ** -j, 5)
+    assert abs(expect - value) <= 5e-7
+    assert rel(O, expect * M) <= 1e-12
+    assert np.all(O[M == 0] == 0.0)
+
+
+def test_scaled_orthogonal():
+    rng = np.random.default_rng(8)
+    Q, _ = np.linalg.qr(rng.standard_normal((6, 6)))
+    O = orc.newton_schulz(3.0 * Q, 5)
+    s = 3.0 / (3.0 * np.sqrt(6.0) + EPS)
+    assert rel(O, p_iter(s, 5) * Q) <= 1e-12
+
+
+def test_one_by_one():
+    for x in [-2.5, 1e-4, 7.0]:
+        O = orc.newton_schulz(np.array([[x]]), 5)
+        assert abs(O[0, 0] - np.sign(x) * p_iter(abs(x) / (abs(x) + EPS), 5)) <= 1e-14
+
+
+def test_zero_matrix():
+    Z = np.zeros((5, 8))
+    O = orc.newton_schulz(Z, 5)
+    assert np.all(O == 0.0)
+    W = np.arange(40.0).reshape(5, 8)
+    W2, B2, O2 = orc.muon_step(W, Z, Z, mu=0.95, lr=0.02)
+    assert np.all(W2 == W) and np.all(B2 == 0) and np.all(O2 == 0)
+
+
+def test_zero_steps_is_normalisation():
+    rng = np.random.default_rng(9)
+    M = rng.standard_normal((5, 3))
+    O = orc.newton_schulz(M, 0)
+    assert np.allclose(O, M / (np.sqrt(np.sum(M * M)) + EPS), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------ momentum, update
+def test_momentum_closed_form_ten_steps():
+    rng = np.random.default_rng(10)
+    mu = 0.95
+    Gs = [rng.standard_normal((4, 6)) for _ in range(10)]
+    Bv = np.zeros((4, 6))
+    for G in Gs:
+        Bv, M = orc.momentum(Bv, G, mu)
+        assert M is Bv or np.array_equal(M, Bv)
+    closed = sum(mu ** (len(Gs) - 1 - t) * G for t, G in enumerate(Gs))
+    assert rel(Bv, closed) <= 1e-12
+
+
+def test_nesterov_input_closed_form():
+    rng = np.random.default_rng(13)
+    mu = 0.9
+    Gs = [rng.standard_normal((3, 5)) for _ in range(4)]
+    Bv = np.zeros((3, 5))
+    for G in Gs:
+        Bv, M = orc.momentum(Bv, G, mu, nesterov=True)
+    T = len(Gs)
+    buf = sum(mu ** (T - 1 - t) * G for t, G in enumerate(Gs))
+    assert rel(M, Gs[-1] + mu * buf) <= 1e-12
+    assert rel(Bv, buf) <= 1e-12
+
+
+def test_update_is_linear_in_direction():
+    rng = np.random.default_rng(14)
+    W = rng.standard_normal((7, 4))
+    G = rng.standard_normal((7, 4))
+    Bz = np.zeros((7, 4))
+    W2, B2, O = orc.muon_step(W, G, Bz, mu=0.95, lr=0.02, scale=0.5)
+    assert rel(W - W2, 0.02 * 0.5 * O) <= 1e-12
+    # First step from a zero buffer: the buffer is the gradient itself.
+    assert np.array_equal(B2, G)
+    assert rel(O, svd_closed_form(G, 5)) <= 1e-12
