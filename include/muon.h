@@ -1,0 +1,187 @@
+/*
+ * libmuon — one Muon optimizer step for a list of 2-D weight matrices on an
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What a step computes, per matrix, follows "Muon: An optimizer for hidden
+ * layers in neural networks" (synthesis note on papers.chlience.com),
+ * section 4, the algorithm definition:
+ *
+ *   B  <- mu * B + G                        momentum accumulation
+ *   M  =  B            (nesterov == 0)      input of the orthogonalisation
+ *   M  =  G + mu * B   (nesterov != 0)      Nesterov-style reading
+ *   X  =  M / (||M||_F + eps)               Frobenius normalisation
+ *   X  =  X^T when rows > cols              smaller Gram matrix
+ *   repeat ns_steps times (default 5):
+ *       A = X X^T;  P = b A + c A A;  X = a X + P X
+ *       (a, b, c) = (3.4445, -4.7750, 2.0315)
+ *   O  =  X, transposed back when rows > cols
+ *   W  <- W - lr * scale * O                parameter update
+ *
+ * Precision: G is float32 or bfloat16; W and B are float32 and updated in
+ * place in float32.  Every matrix product of the iteration runs on bf16
+ * matrix cores with float32 accumulation; A and P are stored as bf16; the
+ * iterate X is carried as a pair of bf16 values (high part and rounding
+ * residual) so that the linear term a*X keeps ~16 significant bits.
+ *
+ * Memory: every pointer passed to the step calls is a DEVICE pointer on the
+ * current HIP device, except the descriptor arrays themselves (mats, hp and
+ * the pointer/size arrays of muon_orthogonalize), which are HOST memory read
+ * only during the call.  All device memory is owned by the caller; the
+ * library allocates no device memory and keeps no pointer after a call
+ * returns (it keeps a small pinned host staging area for the descriptor
+ * table it uploads into the workspace).
+ *
+ * Ordering: work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns without waiting.  Results are visible after
+ * the caller synchronises the stream.  The caller keeps every buffer alive
+ * until then.  Two calls that share a workspace must be ordered on one
+ * stream (or synchronised) — the workspace holds the call's descriptor table
+ * and intermediates.
+ *
+ * Errors: all arguments are validated on the host before anything is
+ * enqueued, so an error return has no side effects.  A failing HIP launch
+ * returns MUON_ERR_HIP; muon_last_error() then holds the HIP message.
+ * Faults inside kernels surface at the caller's next synchronisation.
+ * NaN or Inf in G propagates into B, W; it is not masked.
+ */
+#ifndef MUON_H_
+#define MUON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = -1, /* null pointer, size < 1, bad hyper-parameter   */
+  MUON_ERR_UNSUPPORTED = -2, /* shape beyond the supported maximum            */
+  MUON_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned    */
+  MUON_ERR_ALIAS = -4,       /* W/G/B/workspace ranges overlap                */
+  MUON_ERR_ALIGN = -5,       /* a matrix base pointer is not 16-byte aligned  */
+  MUON_ERR_HIP = -6          /* a HIP runtime call or launch failed           */
+} muon_status_t;
+
+typedef enum muon_dtype { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
+
+/* One weight matrix.  W, G, B are dense row-major rows x cols arrays
+ * (leading dimension = cols), each 16-byte aligned, pairwise disjoint and
+ * disjoint from every other matrix's arrays and from the workspace.
+ * G has the dtype given by muon_hparams_t.g_dtype; W and B are float32.
+ * `scale` multiplies the learning rate for this matrix (the per-parameter
+ * update scale of the synthesis note's Moonlight results section; the
+ * pages give no formula, so the caller supplies it; 1.0 = plain Muon). */
+typedef struct muon_matrix {
+  float* W;
+  const void* G;
+  float* B;
+  int64_t rows;
+  int64_t cols;
+  float scale;
+} muon_matrix_t;
+
+/* Hyper-parameters shared by every matrix of a call.
+ * mu: momentum (finite); lr: learning rate (finite);
+ * eps: added to the Frobenius norm (finite, >= 0; 1e-7 is customary);
+ * ns_steps: Newton-Schulz iterations, 0..MUON_MAX_NS_STEPS (5 is the usual);
+ * nesterov: 0 = orthogonalise the momentum buffer, 1 = G + mu * B;
+ * g_dtype: MUON_F32 or MUON_BF16. */
+typedef struct muon_hparams {
+  float mu;
+  float lr;
+  float eps;
+  int32_t ns_steps;
+  int32_t nesterov;
+  int32_t g_dtype;
+} muon_hparams_t;
+
+#define MUON_MAX_NS_STEPS 64
+/* Largest supported dimension of a matrix (rows and cols each). */
+#define MUON_MAX_DIM 65536
+/* Largest supported short side (the Gram dimension min(rows, cols)). */
+#define MUON_MAX_GRAM 16384
+
+/* Bytes of device workspace muon_step needs for this list (0 if n == 0).
+ * Returns 0 and sets muon_last_error() when the arguments are invalid.
+ * The workspace must be 256-byte aligned. */
+size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp);
+
+/* One Muon step on `n` matrices (section 4 of the synthesis note, as above).
+ * Updates W and B in place; G is read only.  All matrices are processed by
+ * the same sequence of grouped launches (one launch per stage for the whole
+ * list), so same-shape matrices such as separate Q, K and V share each
+ * dispatch.  n == 0 is a no-op returning MUON_OK. */
+muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Orthogonalisation alone: O[i] = NS(M[i]) for float32 row-major inputs
+ * M[i] (rows[i] x cols[i]) into float32 outputs O[i] of the same shape,
+ * with the same normalisation, transpose rule and iteration as muon_step.
+ * For tests and measurement of the Newton-Schulz stage.  M and O are arrays
+ * of n device pointers held in host memory. */
+size_t muon_orthogonalize_workspace_bytes(const int64_t* rows, const int64_t* cols, int64_t n,
+                                          int32_t ns_steps);
+muon_status_t muon_orthogonalize(const float* const* M, float* const* O, const int64_t* rows,
+                                 const int64_t* cols, int64_t n, int32_t ns_steps, float eps,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-only description of how a call would be executed (no GPU needed).
+ * Fills `info`; if `per_matrix` is non-NULL it must hold n entries. */
+typedef struct muon_plan_info {
+  int64_t workspace_bytes;
+  int64_t launches;          /* kernel launches per call                    */
+  int64_t gram_tiles;        /* work-groups of one Gram launch              */
+  int64_t poly_tiles;        /* work-groups of one polynomial launch        */
+  int64_t bx_tiles;          /* work-groups of one BX + aX launch           */
+  int64_t ew_blocks;         /* work-groups of the momentum/norm launch     */
+  int32_t tile;              /* output tile edge of the matrix-core kernels */
+  int32_t reserved;
+} muon_plan_info_t;
+
+typedef struct muon_matrix_plan {
+  int32_t transposed; /* 1 when rows > cols: the iteration runs on M^T       */
+  int32_t m;          /* Gram side min(rows, cols)                           */
+  int32_t n;          /* long side max(rows, cols)                           */
+  int32_t m_pad;      /* m rounded up to the tile edge (zero padded)         */
+  int32_t n_pad;      /* n rounded up to the tile edge (zero padded)         */
+  int32_t reserved;
+  int64_t x_offset;   /* byte offset of the iterate buffers in the workspace */
+} muon_matrix_plan_t;
+
+muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                              muon_plan_info_t* info, muon_matrix_plan_t* per_matrix);
+
+/* Stage timing.  When enabled (per process), every launch the library makes
+ * is bracketed by HIP events on the stream it is launched on;
+ * muon_profile_read waits for the recorded events, adds their elapsed times
+ * per stage to `ms` and the launch counts to `launches` (arrays of
+ * MUON_STAGE_COUNT entries, caller-owned host memory), and clears them. */
+typedef enum muon_stage {
+  MUON_STAGE_MOMENTUM = 0, /* momentum + Frobenius partial sums        */
+  MUON_STAGE_NORM = 1,     /* per-matrix norm reduction                */
+  MUON_STAGE_PREP = 2,     /* normalise, transpose, split to bf16 pair */
+  MUON_STAGE_GRAM = 3,     /* A = X X^T (upper tiles + mirror)         */
+  MUON_STAGE_POLY = 4,     /* P = b A + c A A (upper tiles + mirror)   */
+  MUON_STAGE_BX = 5,       /* X = a X + P X                            */
+  MUON_STAGE_UPDATE = 6,   /* W -= lr * scale * O (or O store)         */
+  MUON_STAGE_UPLOAD = 7,   /* descriptor table copy                    */
+  MUON_STAGE_COUNT = 8
+} muon_stage_t;
+
+muon_status_t muon_profile_enable(int32_t on);
+muon_status_t muon_profile_read(double* ms, int64_t* launches);
+
+const char* muon_status_string(muon_status_t status);
+/* Message of the last error on the calling thread ("" if none). */
+const char* muon_last_error(void);
+int32_t muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H_ */

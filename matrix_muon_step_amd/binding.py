@@ -1,0 +1,302 @@
+"""ctypes binding of libmuon (include/muon.h).  Argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Tensors are
+torch tensors on the current HIP device; torch supplies device memory and the
+current stream, nothing else.  There is no fallback: if libmuon.so is absent
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import List, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon.so")
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARG = -1
+MUON_ERR_UNSUPPORTED = -2
+MUON_ERR_WORKSPACE = -3
+MUON_ERR_ALIAS = -4
+MUON_ERR_ALIGN = -5
+MUON_ERR_HIP = -6
+MUON_F32 = 0
+MUON_BF16 = 1
+MUON_MAX_NS_STEPS = 64
+MUON_MAX_DIM = 65536
+MUON_MAX_GRAM = 16384
+STAGES = ("momentum", "norm", "prep", "gram", "poly", "bx", "update", "upload")
+MUON_STAGE_COUNT = len(STAGES)
+
+
+class muon_matrix_t(ctypes.Structure):
+    _fields_ = [
+        ("W", ctypes.c_void_p),
+        ("G", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class muon_hparams_t(ctypes.Structure):
+    _fields_ = [
+        ("mu", ctypes.c_float),
+        ("lr", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("ns_steps", ctypes.c_int32),
+        ("nesterov", ctypes.c_int32),
+        ("g_dtype", ctypes.c_int32),
+    ]
+
+
+class muon_plan_info_t(ctypes.Structure):
+    _fields_ = [
+        ("workspace_bytes", ctypes.c_int64),
+        ("launches", ctypes.c_int64),
+        ("gram_tiles", ctypes.c_int64),
+        ("poly_tiles", ctypes.c_int64),
+        ("bx_tiles", ctypes.c_int64),
+        ("ew_blocks", ctypes.c_int64),
+        ("tile", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class muon_matrix_plan_t(ctypes.Structure):
+    _fields_ = [
+        ("transposed", ctypes.c_int32),
+        ("m", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("m_pad", ctypes.c_int32),
+        ("n_pad", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("x_offset", ctypes.c_int64),
+    ]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{muon_status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmuon.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m matrix_muon_step_amd.build`; there is no fallback path")
+                L = ctypes.CDLL(LIB_PATH)
+                P = ctypes.POINTER
+                L.muon_workspace_bytes.restype = ctypes.c_size_t
+                L.muon_workspace_bytes.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t)]
+                L.muon_step.restype = ctypes.c_int
+                L.muon_step.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                L.muon_orthogonalize_workspace_bytes.restype = ctypes.c_size_t
+                L.muon_orthogonalize_workspace_bytes.argtypes = [
+                    P(ctypes.c_int64), P(ctypes.c_int64), ctypes.c_int64, ctypes.c_int32]
+                L.muon_orthogonalize.restype = ctypes.c_int
+                L.muon_orthogonalize.argtypes = [
+                    P(ctypes.c_void_p), P(ctypes.c_void_p), P(ctypes.c_int64), P(ctypes.c_int64),
+                    ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                    ctypes.c_size_t, ctypes.c_void_p]
+                L.muon_plan_query.restype = ctypes.c_int
+                L.muon_plan_query.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
+                                              P(muon_plan_info_t), P(muon_matrix_plan_t)]
+                L.muon_profile_enable.restype = ctypes.c_int
+                L.muon_profile_enable.argtypes = [ctypes.c_int32]
+                L.muon_profile_read.restype = ctypes.c_int
+                L.muon_profile_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]
+                L.muon_status_string.restype = ctypes.c_char_p
+                L.muon_status_string.argtypes = [ctypes.c_int]
+                L.muon_last_error.restype = ctypes.c_char_p
+                L.muon_last_error.argtypes = []
+                L.muon_abi_version.restype = ctypes.c_int32
+                L.muon_abi_version.argtypes = []
+                _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- small helpers
+def muon_abi_version() -> int:
+    return int(lib().muon_abi_version())
+
+
+def muon_status_string(status: int) -> str:
+    return lib().muon_status_string(int(status)).decode()
+
+
+def muon_last_error() -> str:
+    return lib().muon_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != MUON_OK:
+        raise MuonError(status, muon_last_error())
+
+
+def hparams(mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False, g_dtype=MUON_F32) -> muon_hparams_t:
+    return muon_hparams_t(float(mu), float(lr), float(eps), int(ns_steps), int(bool(nesterov)), int(g_dtype))
+
+
+def raw_matrix_array(entries: Sequence[Tuple[int, int, int, int, int, float]]):
+    """Builds a muon_matrix_t[] from (W, G, B, rows, cols, scale) integer addresses."""
+    arr = (muon_matrix_t * max(1, len(entries)))()
+    for i, (w, g, b, r, c, s) in enumerate(entries):
+        arr[i] = muon_matrix_t(w, g, b, int(r), int(c), float(s))
+    return arr
+
+
+def _tensor_entries(matrices):
+    import torch
+
+    entries = []
+    g_dtype = None
+    for k, mt in enumerate(matrices):
+        W, G, B = mt[0], mt[1], mt[2]
+        scale = float(mt[3]) if len(mt) > 3 else 1.0
+        for name, t in (("W", W), ("G", G), ("B", B)):
+            if not t.is_cuda:
+                raise ValueError(f"matrix {k}: {name} must be a GPU tensor")
+            if t.dim() != 2 or not t.is_contiguous():
+                raise ValueError(f"matrix {k}: {name} must be a contiguous 2-D tensor")
+        if W.dtype != torch.float32 or B.dtype != torch.float32:
+            raise ValueError(f"matrix {k}: W and B must be float32")
+        if G.dtype == torch.float32:
+            gd = MUON_F32
+        elif G.dtype == torch.bfloat16:
+            gd = MUON_BF16
+        else:
+            raise ValueError(f"matrix {k}: G must be float32 or bfloat16")
+        if g_dtype is None:
+            g_dtype = gd
+        elif g_dtype != gd:
+            raise ValueError("all gradients of one call must share a dtype")
+        if W.shape != G.shape or W.shape != B.shape:
+            raise ValueError(f"matrix {k}: W, G and B shapes differ")
+        entries.append((W.data_ptr(), G.data_ptr(), B.data_ptr(), W.shape[0], W.shape[1], scale))
+    return entries, (MUON_F32 if g_dtype is None else g_dtype)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _alloc_workspace(nbytes: int, device):
+    import torch
+
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+# ---------------------------------------------------------------- entry points
+def muon_workspace_bytes(matrices, mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False) -> int:
+    entries, gd = _tensor_entries(matrices)
+    arr = raw_matrix_array(entries)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd)
+    nbytes = lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp))
+    if nbytes == 0 and entries:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+    return int(nbytes)
+
+
+def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
+              workspace=None, stream=None) -> None:
+    """One Muon step on a list of (W, G, B[, scale]) tensors; W, B updated in place."""
+    entries, gd = _tensor_entries(matrices)
+    if not entries:
+        return
+    arr = raw_matrix_array(entries)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd)
+    need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
+    if need == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+    if workspace is None:
+        workspace = _alloc_workspace(need, matrices[0][0].device)
+    _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                           workspace.numel() * workspace.element_size(), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def muon_orthogonalize_workspace_bytes(shapes: Sequence[Tuple[int, int]], ns_steps=5) -> int:
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(1, n))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(1, n))(*[int(s[1]) for s in shapes])
+    nbytes = lib().muon_orthogonalize_workspace_bytes(rows, cols, n, int(ns_steps))
+    if nbytes == 0 and n:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+    return int(nbytes)
+
+
+def muon_orthogonalize(Ms, Os=None, ns_steps=5, eps=1e-7, workspace=None, stream=None) -> List:
+    """O = NS(M) for a list of float32 matrices; returns the outputs."""
+    import torch
+
+    Ms = list(Ms)
+    if Os is None:
+        Os = [torch.empty_like(M) for M in Ms]
+    n = len(Ms)
+    if n == 0:
+        return []
+    for k, (M, O) in enumerate(zip(Ms, Os)):
+        if M.dtype != torch.float32 or O.dtype != torch.float32 or not M.is_cuda or not O.is_cuda:
+            raise ValueError(f"matrix {k}: M and O must be float32 GPU tensors")
+        if M.shape != O.shape or M.dim() != 2 or not M.is_contiguous() or not O.is_contiguous():
+            raise ValueError(f"matrix {k}: M and O must be contiguous 2-D tensors of one shape")
+    need = muon_orthogonalize_workspace_bytes([M.shape for M in Ms], ns_steps)
+    if workspace is None:
+        workspace = _alloc_workspace(need, Ms[0].device)
+    mp = (ctypes.c_void_p * n)(*[M.data_ptr() for M in Ms])
+    op = (ctypes.c_void_p * n)(*[O.data_ptr() for O in Os])
+    rows = (ctypes.c_int64 * n)(*[M.shape[0] for M in Ms])
+    cols = (ctypes.c_int64 * n)(*[M.shape[1] for M in Ms])
+    _check(lib().muon_orthogonalize(mp, op, rows, cols, n, int(ns_steps), float(eps),
+                                    ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(),
+                                    ctypes.c_void_p(_stream_handle(stream))))
+    return Os
+
+
+def muon_plan_query(shapes: Sequence[Tuple[int, int]], ns_steps=5, g_dtype=MUON_F32):
+    """Host-only plan of a step over matrices of these shapes (no GPU needed)."""
+    n = len(shapes)
+    arr = raw_matrix_array([(0, 0, 0, r, c, 1.0) for r, c in shapes])
+    hp = hparams(ns_steps=ns_steps, g_dtype=g_dtype)
+    info = muon_plan_info_t()
+    per = (muon_matrix_plan_t * max(1, n))()
+    _check(lib().muon_plan_query(arr, n, ctypes.byref(hp), ctypes.byref(info), per))
+    mats = [dict(transposed=p.transposed, m=p.m, n=p.n, m_pad=p.m_pad, n_pad=p.n_pad,
+                 x_offset=p.x_offset) for p in list(per)[:n]]
+    return {f: getattr(info, f) for f, _ in muon_plan_info_t._fields_ if f != "reserved"}, mats
+
+
+def muon_profile_enable(on: bool = True) -> None:
+    _check(lib().muon_profile_enable(int(bool(on))))
+
+
+def muon_profile_read():
+    """{stage: (milliseconds, launches)} accumulated since the last read."""
+    ms = (ctypes.c_double * MUON_STAGE_COUNT)()
+    cnt = (ctypes.c_int64 * MUON_STAGE_COUNT)()
+    _check(lib().muon_profile_read(ms, cnt))
+    return {STAGES[k]: (ms[k], cnt[k]) for k in range(MUON_STAGE_COUNT)}

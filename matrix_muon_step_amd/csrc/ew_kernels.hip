@@ -1,0 +1,296 @@
+// Bandwidth-bound stages of the Muon step on gfx950:
+//   momentum + Frobenius partial sums, per-matrix norm, normalise/transpose/
+//   split into the bf16 iterate pair, and the final parameter update.
+// The method's steps are those of the Muon synthesis note (papers.chlience.com),
+// section 4: momentum accumulation, Frobenius normalisation, transpose to the
+// smaller Gram side, and W <- W - lr * O.
+#include "muon_internal.h"
+
+namespace muon {
+
+namespace {
+
+__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
+  int lo = 0, hi = nmats - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- momentum
+// B <- mu * B + G;  M = B (or G + mu * B);  partials[block] = sum of M^2 over
+// the block's 4096 elements.  Orthogonalise-only mode: M is read from G.
+__global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __restrict__ descs,
+                                                            const int32_t* __restrict__ prefix,
+                                                            int nmats, float mu) {
+  const int blk = blockIdx.x;
+  const int mi = find_mat(prefix, nmats, blk);
+  const MatDesc& d = descs[mi];
+  const int local = blk - prefix[mi];
+  const int flags = d.flags;
+  const int64_t total = d.rows * d.cols;
+  const int64_t base = static_cast<int64_t>(local) * kMomChunk;
+  const int64_t end = (base + kMomChunk < total) ? base + kMomChunk : total;
+  const bool ortho = flags & kOrthoOnly;
+  const bool gbf = flags & kGBf16;
+  const bool nest = flags & kNesterov;
+  float* __restrict__ B = d.B;
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < kMomChunk / 1024; ++it) {
+    const int64_t e = base + (static_cast<int64_t>(it) * 256 + threadIdx.x) * 4;
+    if (e >= end) break;
+    float g[4], b[4];
+    const int cnt = (end - e >= 4) ? 4 : static_cast<int>(end - e);
+    if (cnt == 4) {
+      if (gbf) {
+        const uint2 gv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.G) + e);
+        g[0] = __uint_as_float(gv.x << 16);
+        g[1] = __uint_as_float(gv.x & 0xffff0000u);
+        g[2] = __uint_as_float(gv.y << 16);
+        g[3] = __uint_as_float(gv.y & 0xffff0000u);
+      } else {
+        const float4 gv = *reinterpret_cast<const float4*>(static_cast<const float*>(d.G) + e);
+        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+      }
+      if (!ortho) {
+        const float4 bv = *reinterpret_cast<const float4*>(B + e);
+        b[0] = bv.x; b[1] = bv.y; b[2] = bv.z; b[3] = bv.w;
+      }
+    } else {
+      for (int k = 0; k < 4; ++k) {
+        g[k] = 0.f; b[k] = 0.f;
+        if (k < cnt) {
+          g[k] = gbf ? bf16_bits_to_float(static_cast<const uint16_t*>(d.G)[e + k])
+                     : static_cast<const float*>(d.G)[e + k];
+          if (!ortho) b[k] = B[e + k];
+        }
+      }
+    }
+    float mval[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (ortho) {
+        mval[k] = g[k];
+      } else {
+        b[k] = fmaf(mu, b[k], g[k]);
+        mval[k] = nest ? fmaf(mu, b[k], g[k]) : b[k];
+      }
+    }
+    if (!ortho) {
+      if (cnt == 4) {
+        *reinterpret_cast<float4*>(B + e) = make_float4(b[0], b[1], b[2], b[3]);
+      } else {
+        for (int k = 0; k < cnt; ++k) B[e + k] = b[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = fmaf(mval[k], mval[k], acc);
+  }
+  __shared__ float red[4];
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) d.partials[local] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// ---------------------------------------------------------------- norm
+// One work-group per matrix: fixed-order float64 sum of the block partials,
+// then sigma = 1 / (sqrt(sum) + eps).
+__global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ descs, float eps) {
+  const MatDesc& d = descs[blockIdx.x];
+  const int nb = d.mom_blocks;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nb; i += 256) s += static_cast<double>(d.partials[i]);
+  __shared__ double red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double nrm = sqrt(red[0]);
+    d.sigma[0] = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
+  }
+}
+
+// ---------------------------------------------------------------- prep
+// X = sigma * M in the short-side-major padded layout (transposed when
+// rows > cols), split into bf16 high part and bf16 residual.  Padding is
+// written as zeros.  One 64x64 tile of X per work-group.
+__global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ descs,
+                                                   const int32_t* __restrict__ prefix, int nmats,
+                                                   float mu) {
+  const int blk = blockIdx.x;
+  const int mi = find_mat(prefix, nmats, blk);
+  const MatDesc& d = descs[mi];
+  const int local = blk - prefix[mi];
+  const int tpr = d.n_pad / kEwTile;
+  const int i0 = (local / tpr) * kEwTile;  // X rows (short side)
+  const int j0 = (local % tpr) * kEwTile;  // X cols (long side)
+  const int flags = d.flags;
+  const bool tr = flags & kTransposed;
+  const bool ortho = flags & kOrthoOnly;
+  const bool gbf = flags & kGBf16;
+  const bool nest = flags & kNesterov;
+  const int64_t rows = d.rows, cols = d.cols;
+  // Region of M (original orientation) that feeds this X tile.
+  const int64_t r0 = tr ? j0 : i0;
+  const int64_t c0 = tr ? i0 : j0;
+  const float sigma = d.sigma[0];
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  const int tx = threadIdx.x & 15;   // column group of 4
+  const int ty = threadIdx.x >> 4;   // 0..15
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rl = ty + 16 * k;
+    const int64_t r = r0 + rl;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows) {
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int64_t c = c0 + tx * 4 + c4;
+        if (c < cols) {
+          const int64_t e = r * cols + c;
+          float mval;
+          if (ortho) {
+            mval = static_cast<const float*>(d.G)[e];
+          } else {
+            const float bval = d.B[e];
+            if (nest) {
+              const float g = gbf ? bf16_bits_to_float(static_cast<const uint16_t*>(d.G)[e])
+                                  : static_cast<const float*>(d.G)[e];
+              mval = fmaf(mu, bval, g);
+            } else {
+              mval = bval;
+            }
+          }
+          v[c4] = mval;
+        }
+      }
+    }
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) tile[rl][tx * 4 + c4] = v[c4];
+  }
+  __syncthreads();
+  __bf16* __restrict__ xh = d.xhi[0];
+  __bf16* __restrict__ xl = d.xlo[0];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int il = ty + 16 * k;
+    __bf16 h[4], l[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int jl = tx * 4 + c4;
+      const float m = tr ? tile[jl][il] : tile[il][jl];
+      const float x = sigma * m;
+      h[c4] = static_cast<__bf16>(x);
+      l[c4] = static_cast<__bf16>(x - static_cast<float>(h[c4]));
+    }
+    const int64_t off = static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4;
+    uint2 hv, lv;
+    __builtin_memcpy(&hv, h, 8);
+    __builtin_memcpy(&lv, l, 8);
+    *reinterpret_cast<uint2*>(xh + off) = hv;
+    *reinterpret_cast<uint2*>(xl + off) = lv;
+  }
+}
+
+// ---------------------------------------------------------------- update
+// W <- W - (lr * scale) * O with O = X_hi + X_lo mapped back to rows x cols
+// (transposed when rows > cols).  Orthogonalise-only mode stores O instead.
+__global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__ descs,
+                                                     const int32_t* __restrict__ prefix, int nmats,
+                                                     int buf) {
+  const int blk = blockIdx.x;
+  const int mi = find_mat(prefix, nmats, blk);
+  const MatDesc& d = descs[mi];
+  const int local = blk - prefix[mi];
+  const int64_t rows = d.rows, cols = d.cols;
+  const int tpr = static_cast<int>((cols + kEwTile - 1) / kEwTile);
+  const int64_t r0 = static_cast<int64_t>(local / tpr) * kEwTile;
+  const int64_t c0 = static_cast<int64_t>(local % tpr) * kEwTile;
+  const bool tr = d.flags & kTransposed;
+  const bool ortho = d.flags & kOrthoOnly;
+  const int64_t i0 = tr ? c0 : r0;
+  const int64_t j0 = tr ? r0 : c0;
+  const __bf16* __restrict__ xh = d.xhi[buf];
+  const __bf16* __restrict__ xl = d.xlo[buf];
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  const int tx = threadIdx.x & 15;
+  const int ty = threadIdx.x >> 4;
+  // The padded iterate always covers the whole 64x64 tile: no masking here.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int il = ty + 16 * k;
+    const int64_t off = (i0 + il) * d.n_pad + j0 + tx * 4;
+    uint2 hv = *reinterpret_cast<const uint2*>(xh + off);
+    uint2 lv = *reinterpret_cast<const uint2*>(xl + off);
+    const float o0 = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
+    const float o1 = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
+    const float o2 = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
+    const float o3 = __uint_as_float(hv.y & 0xffff0000u) + __uint_as_float(lv.y & 0xffff0000u);
+    tile[il][tx * 4 + 0] = o0;
+    tile[il][tx * 4 + 1] = o1;
+    tile[il][tx * 4 + 2] = o2;
+    tile[il][tx * 4 + 3] = o3;
+  }
+  __syncthreads();
+  const float ls = d.lr_scale;
+  float* __restrict__ W = d.W;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rl = ty + 16 * k;
+    const int64_t r = r0 + rl;
+    if (r >= rows) continue;
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int cl = tx * 4 + c4;
+      const int64_t c = c0 + cl;
+      if (c >= cols) continue;
+      const float o = tr ? tile[cl][rl] : tile[rl][cl];
+      const int64_t e = r * cols + c;
+      if (ortho) W[e] = o;
+      else W[e] = fmaf(-ls, o, W[e]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(momentum_norm_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, mu);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const MatDesc* d, int nmats, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(nmats), dim3(256), 0, s, d, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(prep_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, mu);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(update_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, buf);
+  return hipGetLastError();
+}
+
+}  // namespace muon

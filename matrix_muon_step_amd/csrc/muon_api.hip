@@ -1,0 +1,625 @@
+// C ABI of libmuon: argument validation, execution plan, workspace layout,
+// descriptor upload and the grouped launch sequence of one Muon step
+// (Muon synthesis note on papers.chlience.com, section 4).
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+muon_status_t fail(muon_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// One matrix as the planner sees it (host side, before pointers are bound).
+struct Item {
+  float* W;
+  const void* G;   // gradient, or M in orthogonalise-only mode
+  float* B;
+  int64_t rows, cols;
+  float lr_scale;
+  int32_t flags;
+};
+
+struct Plan {
+  std::vector<MatDesc> descs;
+  std::vector<int32_t> pre_mom, pre_prep, pre_sym, pre_bx, pre_upd;
+  int64_t tot_mom = 0, tot_prep = 0, tot_sym = 0, tot_bx = 0, tot_upd = 0;
+  size_t table_bytes = 0;   // descriptors + prefix tables
+  size_t total_bytes = 0;
+  std::vector<int64_t> x_offset;
+  int ns_steps = 0;
+};
+
+struct Range {
+  uintptr_t lo, hi;
+  bool writable;
+  const char* what;
+  int64_t idx;
+};
+
+muon_status_t check_aliasing(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  uintptr_t max_end_any = 0, max_end_w = 0;
+  const Range* last_any = nullptr;
+  const Range* last_w = nullptr;
+  for (const Range& r : rs) {
+    if (r.lo == r.hi) continue;
+    if (r.lo < max_end_w) {
+      return fail(MUON_ERR_ALIAS, std::string("muon: ") + r.what + " of matrix " +
+                                      std::to_string(r.idx) + " overlaps " + last_w->what +
+                                      " of matrix " + std::to_string(last_w->idx));
+    }
+    if (r.writable && r.lo < max_end_any) {
+      return fail(MUON_ERR_ALIAS, std::string("muon: ") + r.what + " of matrix " +
+                                      std::to_string(r.idx) + " overlaps " + last_any->what +
+                                      " of matrix " + std::to_string(last_any->idx));
+    }
+    if (r.hi > max_end_any) { max_end_any = r.hi; last_any = &r; }
+    if (r.writable && r.hi > max_end_w) { max_end_w = r.hi; last_w = &r; }
+  }
+  return MUON_OK;
+}
+
+bool finite(float x) { return isfinite(x); }
+
+// Validates shapes and scalars of every item and fills the plan (offsets
+// relative to a workspace base of 0).  Pointer checks happen separately.
+muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan) {
+  const int64_t n = static_cast<int64_t>(items.size());
+  if (n > (1 << 20)) return fail(MUON_ERR_UNSUPPORTED, "muon: more than 2^20 matrices");
+  plan = Plan();
+  plan.ns_steps = ns_steps;
+  plan.descs.resize(n);
+  plan.x_offset.resize(n);
+  plan.pre_mom.resize(n + 1);
+  plan.pre_prep.resize(n + 1);
+  plan.pre_sym.resize(n + 1);
+  plan.pre_bx.resize(n + 1);
+  plan.pre_upd.resize(n + 1);
+
+  size_t off = 0;
+  off += align_up(sizeof(MatDesc) * n);
+  off += align_up(sizeof(int32_t) * 5 * (n + 1));
+  plan.table_bytes = off;
+
+  int64_t total_partials = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const Item& it = items[i];
+    if (it.rows < 1 || it.cols < 1)
+      return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has rows or cols < 1");
+    if (it.rows > MUON_MAX_DIM || it.cols > MUON_MAX_DIM)
+      return fail(MUON_ERR_UNSUPPORTED, "muon: matrix " + std::to_string(i) + " exceeds MUON_MAX_DIM");
+    const bool tr = it.rows > it.cols;
+    const int64_t m = tr ? it.cols : it.rows;
+    const int64_t nn = tr ? it.rows : it.cols;
+    if (m > MUON_MAX_GRAM)
+      return fail(MUON_ERR_UNSUPPORTED, "muon: matrix " + std::to_string(i) + " has min(rows, cols) > MUON_MAX_GRAM");
+    if (!finite(it.lr_scale))
+      return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a non-finite lr*scale");
+    MatDesc& d = plan.descs[i];
+    memset(&d, 0, sizeof(d));
+    d.rows = it.rows;
+    d.cols = it.cols;
+    d.m = static_cast<int32_t>(m);
+    d.n = static_cast<int32_t>(nn);
+    d.m_pad = static_cast<int32_t>(round_up(m, kTile));
+    d.n_pad = static_cast<int32_t>(round_up(nn, kTile));
+    d.flags = it.flags | (tr ? kTransposed : 0);
+    d.lr_scale = it.lr_scale;
+    const int64_t elems = it.rows * it.cols;
+    d.mom_blocks = static_cast<int32_t>((elems + kMomChunk - 1) / kMomChunk);
+    total_partials += d.mom_blocks;
+
+    const int64_t tm = d.m_pad / kTile, tn = d.n_pad / kTile;
+    plan.pre_mom[i] = static_cast<int32_t>(plan.tot_mom);
+    plan.pre_prep[i] = static_cast<int32_t>(plan.tot_prep);
+    plan.pre_sym[i] = static_cast<int32_t>(plan.tot_sym);
+    plan.pre_bx[i] = static_cast<int32_t>(plan.tot_bx);
+    plan.pre_upd[i] = static_cast<int32_t>(plan.tot_upd);
+    plan.tot_mom += d.mom_blocks;
+    plan.tot_prep += (d.m_pad / kEwTile) * (d.n_pad / kEwTile);
+    plan.tot_sym += tm * (tm + 1) / 2;
+    plan.tot_bx += tm * tn;
+    plan.tot_upd += ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
+    const int64_t lim = (int64_t{1} << 31) - 1;
+    if (plan.tot_mom > lim || plan.tot_prep > lim || plan.tot_bx > lim || plan.tot_upd > lim)
+      return fail(MUON_ERR_UNSUPPORTED, "muon: too many work-groups for one launch");
+  }
+  plan.pre_mom[n] = static_cast<int32_t>(plan.tot_mom);
+  plan.pre_prep[n] = static_cast<int32_t>(plan.tot_prep);
+  plan.pre_sym[n] = static_cast<int32_t>(plan.tot_sym);
+  plan.pre_bx[n] = static_cast<int32_t>(plan.tot_bx);
+  plan.pre_upd[n] = static_cast<int32_t>(plan.tot_upd);
+
+  // Partials and sigma.
+  const size_t partial_off = off;
+  off += align_up(sizeof(float) * total_partials);
+  const size_t sigma_off = off;
+  off += align_up(sizeof(float) * n);
+  int64_t pcur = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    MatDesc& d = plan.descs[i];
+    d.partials = reinterpret_cast<float*>(partial_off + sizeof(float) * pcur);
+    pcur += d.mom_blocks;
+    d.sigma = reinterpret_cast<float*>(sigma_off + sizeof(float) * i);
+  }
+  // Iterate and Gram buffers.
+  for (int64_t i = 0; i < n; ++i) {
+    MatDesc& d = plan.descs[i];
+    plan.x_offset[i] = static_cast<int64_t>(off);
+    const size_t xb = align_up(sizeof(__bf16) * static_cast<size_t>(d.m_pad) * d.n_pad);
+    const size_t gb = align_up(sizeof(__bf16) * static_cast<size_t>(d.m_pad) * d.m_pad);
+    d.xhi[0] = reinterpret_cast<__bf16*>(off); off += xb;
+    d.xlo[0] = reinterpret_cast<__bf16*>(off); off += xb;
+    if (ns_steps > 0) {
+      d.xhi[1] = reinterpret_cast<__bf16*>(off); off += xb;
+      d.xlo[1] = reinterpret_cast<__bf16*>(off); off += xb;
+      d.gram = reinterpret_cast<__bf16*>(off); off += gb;
+      d.poly = reinterpret_cast<__bf16*>(off); off += gb;
+    }
+  }
+  plan.total_bytes = off;
+  return MUON_OK;
+}
+
+template <class T>
+T* rebase(T* p, uintptr_t base) {
+  return p ? reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + base) : nullptr;
+}
+
+void bind_workspace(Plan& plan, uintptr_t base) {
+  for (MatDesc& d : plan.descs) {
+    d.partials = rebase(d.partials, base);
+    d.sigma = rebase(d.sigma, base);
+    for (int b = 0; b < 2; ++b) {
+      d.xhi[b] = rebase(d.xhi[b], base);
+      d.xlo[b] = rebase(d.xlo[b], base);
+    }
+    d.gram = rebase(d.gram, base);
+    d.poly = rebase(d.poly, base);
+  }
+}
+
+// ---------------------------------------------------------------- staging ring
+// Pinned host slots for the descriptor table; a slot is reused only after the
+// copy that last read it has completed (tracked by an event).
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+struct DeviceStaging {
+  int device = -1;
+  Slot slots[4];
+  int cursor = 0;
+};
+
+std::mutex g_staging_mu;
+std::vector<DeviceStaging> g_staging;
+
+hipError_t upload_table(const void* src, size_t bytes, void* dst, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  DeviceStaging* ds = nullptr;
+  for (auto& x : g_staging)
+    if (x.device == dev) ds = &x;
+  if (!ds) {
+    g_staging.emplace_back();
+    ds = &g_staging.back();
+    ds->device = dev;
+  }
+  Slot& sl = ds->slots[ds->cursor];
+  ds->cursor = (ds->cursor + 1) % 4;
+  if (sl.pending) {
+    e = hipEventSynchronize(sl.ev);
+    if (e != hipSuccess) return e;
+    sl.pending = false;
+  }
+  if (!sl.ev) {
+    e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  if (sl.cap < bytes) {
+    if (sl.host) hipHostFree(sl.host);
+    sl.host = nullptr;
+    sl.cap = 0;
+    const size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return e;
+    sl.cap = cap;
+  }
+  memcpy(sl.host, src, bytes);
+  e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(sl.ev, s);
+  if (e != hipSuccess) return e;
+  sl.pending = true;
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- profiling
+struct PendingEv {
+  int stage;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<PendingEv> g_prof_pending;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t run_stage(int stage, hipStream_t s, F&& f) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on) return f();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    a = prof_event();
+    b = prof_event();
+  }
+  if (a) hipEventRecord(a, s);
+  hipError_t e = f();
+  if (b) hipEventRecord(b, s);
+  if (a && b) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_pending.push_back({stage, a, b});
+  }
+  return e;
+}
+
+muon_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(MUON_ERR_HIP, std::string("muon: ") + where + ": " + hipGetErrorString(e));
+}
+
+// Launch sequence of one call.  The descriptor table is uploaded into the
+// workspace, then every stage is one grouped launch over all matrices.
+muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStream_t s) {
+  const int n = static_cast<int>(plan.descs.size());
+  const uintptr_t base = reinterpret_cast<uintptr_t>(workspace);
+  bind_workspace(plan, base);
+
+  std::vector<unsigned char> table(plan.table_bytes, 0);
+  memcpy(table.data(), plan.descs.data(), sizeof(MatDesc) * n);
+  const size_t pre_off = align_up(sizeof(MatDesc) * n);
+  int32_t* pre = reinterpret_cast<int32_t*>(table.data() + pre_off);
+  const std::vector<int32_t>* lists[5] = {&plan.pre_mom, &plan.pre_prep, &plan.pre_sym,
+                                          &plan.pre_bx, &plan.pre_upd};
+  for (int k = 0; k < 5; ++k) memcpy(pre + k * (n + 1), lists[k]->data(), sizeof(int32_t) * (n + 1));
+
+  const MatDesc* d_desc = reinterpret_cast<const MatDesc*>(base);
+  const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pre_off);
+  const int32_t* p_mom = d_pre;
+  const int32_t* p_prep = d_pre + (n + 1);
+  const int32_t* p_sym = d_pre + 2 * (n + 1);
+  const int32_t* p_bx = d_pre + 3 * (n + 1);
+  const int32_t* p_upd = d_pre + 4 * (n + 1);
+
+  hipError_t e;
+  e = run_stage(MUON_STAGE_UPLOAD, s, [&] { return upload_table(table.data(), table.size(), workspace, s); });
+  if (e != hipSuccess) return hip_fail(e, "descriptor upload");
+  e = run_stage(MUON_STAGE_MOMENTUM, s, [&] {
+    return launch_momentum(d_desc, p_mom, n, static_cast<int>(plan.tot_mom), mu, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "momentum launch");
+  e = run_stage(MUON_STAGE_NORM, s, [&] { return launch_norm(d_desc, n, eps, s); });
+  if (e != hipSuccess) return hip_fail(e, "norm launch");
+  e = run_stage(MUON_STAGE_PREP, s, [&] {
+    return launch_prep(d_desc, p_prep, n, static_cast<int>(plan.tot_prep), mu, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "prep launch");
+  int buf = 0;
+  for (int it = 0; it < plan.ns_steps; ++it) {
+    e = run_stage(MUON_STAGE_GRAM, s, [&] {
+      return launch_gram(d_desc, p_sym, n, static_cast<int>(plan.tot_sym), buf, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "gram launch");
+    e = run_stage(MUON_STAGE_POLY, s, [&] {
+      return launch_poly(d_desc, p_sym, n, static_cast<int>(plan.tot_sym), s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "poly launch");
+    e = run_stage(MUON_STAGE_BX, s, [&] {
+      return launch_bx(d_desc, p_bx, n, static_cast<int>(plan.tot_bx), buf, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "bx launch");
+    buf ^= 1;
+  }
+  e = run_stage(MUON_STAGE_UPDATE, s, [&] {
+    return launch_update(d_desc, p_upd, n, static_cast<int>(plan.tot_upd), buf, s);
+  });
+  if (e != hipSuccess) return hip_fail(e, "update launch");
+  return MUON_OK;
+}
+
+muon_status_t check_hparams(const muon_hparams_t* hp) {
+  if (!hp) return fail(MUON_ERR_INVALID_ARG, "muon: hp is NULL");
+  if (!finite(hp->mu) || !finite(hp->lr) || !finite(hp->eps) || hp->eps < 0.f)
+    return fail(MUON_ERR_INVALID_ARG, "muon: mu, lr and eps must be finite and eps >= 0");
+  if (hp->ns_steps < 0 || hp->ns_steps > MUON_MAX_NS_STEPS)
+    return fail(MUON_ERR_INVALID_ARG, "muon: ns_steps outside 0..MUON_MAX_NS_STEPS");
+  if (hp->nesterov != 0 && hp->nesterov != 1)
+    return fail(MUON_ERR_INVALID_ARG, "muon: nesterov must be 0 or 1");
+  if (hp->g_dtype != MUON_F32 && hp->g_dtype != MUON_BF16)
+    return fail(MUON_ERR_INVALID_ARG, "muon: unknown g_dtype");
+  return MUON_OK;
+}
+
+muon_status_t items_from_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                              bool check_ptrs, std::vector<Item>& items) {
+  muon_status_t st = check_hparams(hp);
+  if (st != MUON_OK) return st;
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "muon: n < 0");
+  if (n > 0 && !mats) return fail(MUON_ERR_INVALID_ARG, "muon: mats is NULL");
+  items.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    const muon_matrix_t& mt = mats[i];
+    if (check_ptrs) {
+      if (!mt.W || !mt.G || !mt.B)
+        return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a NULL W, G or B");
+      if ((reinterpret_cast<uintptr_t>(mt.W) | reinterpret_cast<uintptr_t>(mt.G) |
+           reinterpret_cast<uintptr_t>(mt.B)) & 15u)
+        return fail(MUON_ERR_ALIGN, "muon: matrix " + std::to_string(i) + " W, G or B is not 16-byte aligned");
+    }
+    if (!finite(mt.scale))
+      return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a non-finite scale");
+    Item& it = items[i];
+    it.W = mt.W;
+    it.G = mt.G;
+    it.B = mt.B;
+    it.rows = mt.rows;
+    it.cols = mt.cols;
+    it.lr_scale = hp->lr * mt.scale;
+    it.flags = (hp->g_dtype == MUON_BF16 ? kGBf16 : 0) | (hp->nesterov ? kNesterov : 0);
+  }
+  return MUON_OK;
+}
+
+muon_status_t check_workspace(const Plan& plan, void* ws, size_t ws_bytes) {
+  if (plan.total_bytes == 0) return MUON_OK;
+  if (!ws) return fail(MUON_ERR_WORKSPACE, "muon: workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MUON_ERR_WORKSPACE, "muon: workspace is not 256-byte aligned");
+  if (ws_bytes < plan.total_bytes)
+    return fail(MUON_ERR_WORKSPACE, "muon: workspace has " + std::to_string(ws_bytes) +
+                                        " bytes, needs " + std::to_string(plan.total_bytes));
+  return MUON_OK;
+}
+
+void fill_ptrs(Plan& plan, const std::vector<Item>& items) {
+  for (size_t i = 0; i < items.size(); ++i) {
+    plan.descs[i].W = items[i].W;
+    plan.descs[i].G = items[i].G;
+    plan.descs[i].B = items[i].B;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp) {
+  g_last_error.clear();
+  std::vector<Item> items;
+  if (items_from_step(mats, n, hp, false, items) != MUON_OK) return 0;
+  if (n == 0) return 0;
+  Plan plan;
+  if (make_plan(items, hp->ns_steps, plan) != MUON_OK) return 0;
+  return plan.total_bytes;
+}
+
+muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  std::vector<Item> items;
+  muon_status_t st = items_from_step(mats, n, hp, true, items);
+  if (st != MUON_OK) return st;
+  if (n == 0) return MUON_OK;
+  Plan plan;
+  st = make_plan(items, hp->ns_steps, plan);
+  if (st != MUON_OK) return st;
+  st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != MUON_OK) return st;
+  std::vector<Range> rs;
+  const size_t gsz = hp->g_dtype == MUON_BF16 ? 2 : 4;
+  for (int64_t i = 0; i < n; ++i) {
+    const uintptr_t e = static_cast<uintptr_t>(items[i].rows * items[i].cols);
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].W), reinterpret_cast<uintptr_t>(items[i].W) + 4 * e, true, "W", i});
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].B), reinterpret_cast<uintptr_t>(items[i].B) + 4 * e, true, "B", i});
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].G), reinterpret_cast<uintptr_t>(items[i].G) + gsz * e, false, "G", i});
+  }
+  rs.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + plan.total_bytes, true, "workspace", -1});
+  st = check_aliasing(rs);
+  if (st != MUON_OK) return st;
+  fill_ptrs(plan, items);
+  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream));
+}
+
+static muon_status_t ortho_items(const float* const* M, float* const* O, const int64_t* rows,
+                                 const int64_t* cols, int64_t n, int32_t ns_steps, bool check_ptrs,
+                                 std::vector<Item>& items) {
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "muon: n < 0");
+  if (ns_steps < 0 || ns_steps > MUON_MAX_NS_STEPS)
+    return fail(MUON_ERR_INVALID_ARG, "muon: ns_steps outside 0..MUON_MAX_NS_STEPS");
+  if (n > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "muon: rows or cols is NULL");
+  if (check_ptrs && n > 0 && (!M || !O)) return fail(MUON_ERR_INVALID_ARG, "muon: M or O is NULL");
+  items.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    Item& it = items[i];
+    it.W = check_ptrs ? O[i] : nullptr;
+    it.G = check_ptrs ? M[i] : nullptr;
+    it.B = nullptr;
+    it.rows = rows[i];
+    it.cols = cols[i];
+    it.lr_scale = 0.f;
+    it.flags = kOrthoOnly;
+    if (check_ptrs) {
+      if (!it.W || !it.G)
+        return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a NULL M or O");
+      if ((reinterpret_cast<uintptr_t>(it.W) | reinterpret_cast<uintptr_t>(it.G)) & 15u)
+        return fail(MUON_ERR_ALIGN, "muon: matrix " + std::to_string(i) + " M or O is not 16-byte aligned");
+    }
+  }
+  return MUON_OK;
+}
+
+size_t muon_orthogonalize_workspace_bytes(const int64_t* rows, const int64_t* cols, int64_t n,
+                                          int32_t ns_steps) {
+  g_last_error.clear();
+  std::vector<Item> items;
+  if (ortho_items(nullptr, nullptr, rows, cols, n, ns_steps, false, items) != MUON_OK) return 0;
+  if (n == 0) return 0;
+  Plan plan;
+  if (make_plan(items, ns_steps, plan) != MUON_OK) return 0;
+  return plan.total_bytes;
+}
+
+muon_status_t muon_orthogonalize(const float* const* M, float* const* O, const int64_t* rows,
+                                 const int64_t* cols, int64_t n, int32_t ns_steps, float eps,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!isfinite(eps) || eps < 0.f) return fail(MUON_ERR_INVALID_ARG, "muon: eps must be finite and >= 0");
+  std::vector<Item> items;
+  muon_status_t st = ortho_items(M, O, rows, cols, n, ns_steps, true, items);
+  if (st != MUON_OK) return st;
+  if (n == 0) return MUON_OK;
+  Plan plan;
+  st = make_plan(items, ns_steps, plan);
+  if (st != MUON_OK) return st;
+  st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != MUON_OK) return st;
+  std::vector<Range> rs;
+  for (int64_t i = 0; i < n; ++i) {
+    const uintptr_t e = static_cast<uintptr_t>(items[i].rows * items[i].cols);
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].W), reinterpret_cast<uintptr_t>(items[i].W) + 4 * e, true, "O", i});
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].G), reinterpret_cast<uintptr_t>(items[i].G) + 4 * e, false, "M", i});
+  }
+  rs.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + plan.total_bytes, true, "workspace", -1});
+  st = check_aliasing(rs);
+  if (st != MUON_OK) return st;
+  fill_ptrs(plan, items);
+  return execute(plan, workspace, 0.f, eps, static_cast<hipStream_t>(stream));
+}
+
+muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                              muon_plan_info_t* info, muon_matrix_plan_t* per_matrix) {
+  g_last_error.clear();
+  if (!info) return fail(MUON_ERR_INVALID_ARG, "muon: info is NULL");
+  std::vector<Item> items;
+  muon_status_t st = items_from_step(mats, n, hp, false, items);
+  if (st != MUON_OK) return st;
+  memset(info, 0, sizeof(*info));
+  info->tile = kTile;
+  if (n == 0) return MUON_OK;
+  Plan plan;
+  st = make_plan(items, hp->ns_steps, plan);
+  if (st != MUON_OK) return st;
+  info->workspace_bytes = static_cast<int64_t>(plan.total_bytes);
+  info->launches = 4 + 3 * static_cast<int64_t>(hp->ns_steps);  // kernels; the table copy is extra
+  info->gram_tiles = plan.tot_sym;
+  info->poly_tiles = plan.tot_sym;
+  info->bx_tiles = plan.tot_bx;
+  info->ew_blocks = plan.tot_mom;
+  if (per_matrix) {
+    for (int64_t i = 0; i < n; ++i) {
+      const MatDesc& d = plan.descs[i];
+      muon_matrix_plan_t& p = per_matrix[i];
+      p.transposed = (d.flags & kTransposed) ? 1 : 0;
+      p.m = d.m;
+      p.n = d.n;
+      p.m_pad = d.m_pad;
+      p.n_pad = d.n_pad;
+      p.reserved = 0;
+      p.x_offset = plan.x_offset[i];
+    }
+  }
+  return MUON_OK;
+}
+
+muon_status_t muon_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof_on = on != 0;
+  return MUON_OK;
+}
+
+muon_status_t muon_profile_read(double* ms, int64_t* launches) {
+  g_last_error.clear();
+  if (!ms || !launches) return fail(MUON_ERR_INVALID_ARG, "muon: ms or launches is NULL");
+  std::vector<PendingEv> pend;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    pend.swap(g_prof_pending);
+  }
+  for (int k = 0; k < MUON_STAGE_COUNT; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  muon_status_t st = MUON_OK;
+  for (const PendingEv& p : pend) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(p.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, p.a, p.b);
+    if (e != hipSuccess && st == MUON_OK) st = hip_fail(e, "profile read");
+    ms[p.stage] += t;
+    launches[p.stage] += 1;
+  }
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  for (const PendingEv& p : pend) {
+    g_prof_pool.push_back(p.a);
+    g_prof_pool.push_back(p.b);
+  }
+  return st;
+}
+
+const char* muon_status_string(muon_status_t status) {
+  switch (status) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE";
+    case MUON_ERR_ALIAS: return "MUON_ERR_ALIAS";
+    case MUON_ERR_ALIGN: return "MUON_ERR_ALIGN";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+  }
+  return "MUON_ERR_UNKNOWN";
+}
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+int32_t muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal definitions shared by the host planner and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Output tile edge of the matrix-core kernels; every iterate / Gram buffer is
+// zero padded to a multiple of it, so the GEMM kernels never bounds-check.
+constexpr int kTile = 128;
+// Tile edge of the layout kernels (normalise/transpose, update).
+constexpr int kEwTile = 64;
+// Elements per work-group of the momentum/norm kernel.
+constexpr int kMomChunk = 4096;
+
+enum GFlags : int32_t {
+  kTransposed = 1,  // rows > cols: iterate on M^T
+  kGBf16 = 2,       // gradient stored as bfloat16
+  kNesterov = 4,    // orthogonalise G + mu * B
+  kOrthoOnly = 8,   // muon_orthogonalize: read M, write O, no momentum/update
+};
+
+// One matrix of a call, as the kernels see it (lives in the workspace).
+struct MatDesc {
+  float* W;          // update target (or O output in orthogonalise-only mode)
+  const void* G;     // gradient (or M input in orthogonalise-only mode)
+  float* B;          // momentum buffer (unused in orthogonalise-only mode)
+  __bf16* xhi[2];    // iterate high parts, m_pad x n_pad, ping-pong
+  __bf16* xlo[2];    // iterate residual parts
+  __bf16* gram;      // A, m_pad x m_pad
+  __bf16* poly;      // P, m_pad x m_pad
+  float* partials;   // per-block sums of squares of M
+  float* sigma;      // 1 / (||M||_F + eps)
+  int64_t rows, cols;
+  int32_t m, n, m_pad, n_pad;
+  int32_t flags;
+  int32_t mom_blocks;  // work-groups of the momentum kernel for this matrix
+  float lr_scale;      // lr * scale, formed in float32 on the host
+  float pad_;
+};
+
+// Exclusive prefix sums of work-groups per matrix for each grouped launch;
+// entry [n] is the launch's total.  Stored after the descriptors.
+struct LaunchTables {
+  const int32_t* mom;   // momentum/norm chunks
+  const int32_t* prep;  // 64x64 tiles of the padded iterate
+  const int32_t* sym;   // upper-triangle 128x128 tiles of the Gram side
+  const int32_t* bx;    // 128x128 tiles of the padded iterate
+  const int32_t* upd;   // 64x64 tiles of rows x cols
+};
+
+struct StepScalars {
+  float mu;
+  float eps;
+  int32_t nmats;
+  int32_t pad_;
+};
+
+// Host-side launchers (defined in the kernel translation units).
+hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, int total,
+                           float mu, hipStream_t s);
+hipError_t launch_norm(const MatDesc* d, int nmats, float eps, hipStream_t s);
+hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
+                       hipStream_t s);
+hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
+                         hipStream_t s);
+hipError_t launch_gram(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
+                       hipStream_t s);
+hipError_t launch_poly(const MatDesc* d, const int32_t* prefix, int nmats, int total,
+                       hipStream_t s);
+hipError_t launch_bx(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
+                     hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,244 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Tolerances (per matrix, relative Frobenius):
+  * orthogonalised direction O (bf16 matrix-core path)      <= 2e-2
+  * momentum buffer B (float32)                             <= 1e-5
+  * update W' against W - lr*scale*O_gpu, relative to the
+    size of the step (float32 epilogue)                     <= 1e-5
+Index logic (shape, transpose, padding, grouping) is checked bit for bit in
+tests/test_bitexact_gpu.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import muon_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+NS_TOL = 2e-2
+FP32_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def mm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import matrix_muon_step_amd as m
+
+    m.lib()
+    return m
+
+
+def relfro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def g_tensor(g, g_dtype):
+    if g_dtype == "bf16":
+        return torch.from_numpy(g.view(np.int16)).cuda().view(torch.bfloat16)
+    return dev(g)
+
+
+def log_case(name):
+    print(f"[case] {name}", flush=True)
+
+
+# ------------------------------------------------------------------ orthogonalisation alone
+ORTHO_SHAPES = [(1, 1), (1, 300), (300, 1), (17, 33), (33, 17), (128, 128), (129, 257),
+                (257, 129), (256, 256), (300, 520), (520, 300), (640, 130), (768, 3072)]
+
+
+@pytest.mark.parametrize("shape", ORTHO_SHAPES)
+def test_orthogonalize_matches_oracle(mm, shape):
+    log_case(f"ortho {shape}")
+    r, c = shape
+    M = synth.numpy_gradient(r, c, min(16, r, c), 0.1, "f32", [50, r, c, 0])
+    O = mm.muon_orthogonalize([dev(M)], ns_steps=5)[0]
+    torch.cuda.synchronize()
+    ref = orc.newton_schulz(M.astype(np.float64), 5)
+    err = relfro(O.cpu().numpy(), ref)
+    print(f"  relFro {err:.3e}")
+    assert err <= NS_TOL
+
+
+@pytest.mark.parametrize("steps", [0, 1, 2, 3, 6])
+def test_orthogonalize_step_counts(mm, steps):
+    log_case(f"ortho steps={steps}")
+    shapes = [(200, 330), (330, 200), (64, 64)]
+    Ms = [synth.numpy_gradient(r, c, 8, 0.1, "f32", [51, r, c, steps]) for r, c in shapes]
+    Os = mm.muon_orthogonalize([dev(M) for M in Ms], ns_steps=steps)
+    torch.cuda.synchronize()
+    for M, O in zip(Ms, Os):
+        ref = orc.newton_schulz(M.astype(np.float64), steps)
+        tol = 1e-2 if steps == 0 else NS_TOL
+        assert relfro(O.cpu().numpy(), ref) <= tol
+
+
+def test_orthogonalize_grouped_mixed_shapes(mm):
+    log_case("ortho grouped mixed")
+    shapes = [(1, 1), (5, 3), (3, 5), (128, 384), (384, 128), (250, 250), (96, 700)]
+    Ms = [synth.numpy_gradient(r, c, min(4, r, c), 0.1, "f32", [52, i, 0, 0]) for i, (r, c) in enumerate(shapes)]
+    Os = mm.muon_orthogonalize([dev(M) for M in Ms], ns_steps=5)
+    torch.cuda.synchronize()
+    for M, O in zip(Ms, Os):
+        assert relfro(O.cpu().numpy(), orc.newton_schulz(M.astype(np.float64), 5)) <= NS_TOL
+
+
+# ------------------------------------------------------------------ full step helpers
+def run_workload(mm, w, steps=None, nesterov=False, indices=None):
+    """Runs `steps` Muon steps of workload w on the GPU and the oracle."""
+    steps = w.steps if steps is None else steps
+    idx = list(range(len(w.matrices))) if indices is None else list(indices)
+    host = [synth.numpy_matrix(w, i, 0) for i in idx]
+    W = [dev(h["W0"]) for h in host]
+    B = [dev(h["B0"]) for h in host]
+    Wref = [h["W0"].astype(np.float64) for h in host]
+    Bref = [h["B0"].astype(np.float64) for h in host]
+    for t in range(steps):
+        gs = [synth.numpy_gradient(w.matrices[i].rows, w.matrices[i].cols, w.rank, w.noise, w.g_dtype,
+                                   [w.wid, i, t, 0]) for i in idx]
+        G = [g_tensor(g, w.g_dtype) for g in gs]
+        mm.muon_step([(W[k], G[k], B[k], w.scale) for k in range(len(idx))], mu=w.mu, lr=w.lr,
+                     ns_steps=5, nesterov=nesterov)
+        for k, g in enumerate(gs):
+            g64 = synth.gradient_as_f64(g, w.g_dtype)
+            Wref[k], Bref[k], _ = orc.muon_step(Wref[k], g64, Bref[k], w.mu, w.lr, w.scale, 5, nesterov)
+    torch.cuda.synchronize()
+    return host, W, B, Wref, Bref
+
+
+def check_step_results(host, W, B, Wref, Bref, lr_scale):
+    worst = 0.0
+    for h, Wg, Bg, Wr, Br in zip(host, W, B, Wref, Bref):
+        b_err = relfro(Bg.cpu().numpy(), Br)
+        assert b_err <= FP32_TOL, f"momentum relFro {b_err:.3e}"
+        dW = Wg.cpu().numpy().astype(np.float64) - h["W0"]
+        dref = Wr - h["W0"]
+        err = relfro(dW, dref)
+        worst = max(worst, err)
+        assert err <= NS_TOL, f"direction relFro {err:.3e}"
+    print(f"  worst direction relFro {worst:.3e}")
+
+
+def test_single256(mm):
+    log_case("single256")
+    w = synth.WORKLOADS["single256"]
+    check_step_results(*run_workload(mm, w), w.lr * w.scale)
+
+
+def test_single256_update_epilogue_fp32(mm):
+    """W' against W - lr*scale*O computed from the GPU's own O (float32 bar)."""
+    log_case("single256 update epilogue")
+    w = synth.WORKLOADS["single256"]
+    h = synth.numpy_matrix(w, 0, 0)
+    Wd, Gd, Bd = dev(h["W0"]), dev(h["G"]), dev(h["B0"])
+    mm.muon_step([(Wd, Gd, Bd, 0.75)], mu=w.mu, lr=w.lr, ns_steps=5)
+    O = mm.muon_orthogonalize([Bd.clone()], ns_steps=5)[0]
+    torch.cuda.synchronize()
+    O64 = O.cpu().numpy().astype(np.float64)
+    expect = h["W0"].astype(np.float64) - np.float64(np.float32(w.lr * 0.75)) * O64
+    step = expect - h["W0"]
+    err = np.linalg.norm(Wd.cpu().numpy() - expect) / np.linalg.norm(step)
+    assert err <= FP32_TOL, err
+    assert relfro(Bd.cpu().numpy(), h["G"]) == 0.0  # first step from B = 0: B = G exactly
+
+
+def test_gpt2s_fc_ten_steps(mm):
+    log_case("gpt2s_fc_10step")
+    w = synth.WORKLOADS["gpt2s_fc_10step"]
+    check_step_results(*run_workload(mm, w), w.lr)
+
+
+def test_gpt2_small_grouped(mm):
+    log_case("gpt2_small (72 matrices, one grouped launch per stage)")
+    w = synth.WORKLOADS["gpt2_small"]
+    check_step_results(*run_workload(mm, w), w.lr)
+
+
+def test_nesterov_reading(mm):
+    log_case("nesterov")
+    w = synth.WORKLOADS["gpt2s_fc_10step"]
+    check_step_results(*run_workload(mm, w, steps=3, nesterov=True), w.lr)
+
+
+def test_bf16_gradients_small(mm):
+    log_case("bf16 gradients (moe-like aspect ratios, reduced sizes)")
+    w = synth.Workload(40, "moe_small", (synth.MatrixSpec(256, 896, "up"), synth.MatrixSpec(896, 256, "down"),
+                                         synth.MatrixSpec(512, 1792, "dense")), 8, 0.05, "bf16", 2)
+    check_step_results(*run_workload(mm, w), w.lr)
+
+
+def test_zero_gradient_leaves_weights(mm):
+    log_case("zero gradient")
+    Wd = dev(np.arange(12 * 20, dtype=np.float32).reshape(12, 20) * 1e-3)
+    W0 = Wd.clone()
+    Gd = torch.zeros_like(Wd)
+    Bd = torch.zeros_like(Wd)
+    mm.muon_step([(Wd, Gd, Bd, 1.0)], ns_steps=5)
+    torch.cuda.synchronize()
+    assert torch.equal(Wd, W0) and torch.count_nonzero(Bd) == 0
+
+
+def test_poisoned_workspace_gives_finite_results(mm):
+    """Workspace pre-filled with NaN bytes: every byte the path reads is written first."""
+    log_case("poisoned workspace")
+    shapes = [(130, 260), (260, 130), (17, 33), (256, 256)]
+    mats, host = [], []
+    for i, (r, c) in enumerate(shapes):
+        g = synth.numpy_gradient(r, c, 4, 0.1, "f32", [53, i, 0, 0])
+        W0 = np.zeros((r, c), np.float32)
+        host.append((W0, g))
+        mats.append((dev(W0), dev(g), torch.zeros(r, c, device="cuda"), 1.0))
+    nbytes = mm.muon_workspace_bytes(mats)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    mm.muon_step(mats, workspace=ws)
+    torch.cuda.synchronize()
+    for (W0, g), (Wd, _, _, _) in zip(host, mats):
+        Wn = Wd.cpu().numpy()
+        assert np.isfinite(Wn).all()
+        ref, _, _ = orc.muon_step(W0, g, np.zeros_like(g), 0.95, 0.02)
+        assert relfro(Wn, ref) <= NS_TOL
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled)
+def _full_size(mm, name, sample):
+    w = synth.WORKLOADS[name]
+    log_case(f"{name} full size, sampled matrices {sample}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234 + w.wid)
+    mats, keep = [], {}
+    for i in range(len(w.matrices)):
+        t = synth.torch_matrix(w, i, 0, "cuda", generator=gen)
+        if i in sample:
+            keep[i] = (t["W0"].cpu().numpy().copy(), t["G"].float().cpu().numpy().astype(np.float64))
+        mats.append((t["W0"], t["G"], t["B0"], w.scale))
+    mm.muon_step(mats, mu=w.mu, lr=w.lr, ns_steps=5)
+    torch.cuda.synchronize()
+    for i in sample:
+        W0, g64 = keep[i]
+        Wr, Br, _ = orc.muon_step(W0, g64, np.zeros_like(g64), w.mu, w.lr, w.scale, 5)
+        Wg = mats[i][0].cpu().numpy().astype(np.float64)
+        Bg = mats[i][2].cpu().numpy()
+        assert relfro(Bg, Br) <= FP32_TOL
+        err = relfro(Wg - W0, Wr - W0)
+        print(f"  matrix {i} {w.matrices[i].rows}x{w.matrices[i].cols}: direction relFro {err:.3e}", flush=True)
+        assert err <= NS_TOL
+    del mats
+    torch.cuda.empty_cache()
+
+
+def test_gpt2_xl_full_size_sampled(mm):
+    _full_size(mm, "gpt2_xl_1p5b", [0, 4, 5, 287])
+
+
+def test_moe_share_full_size_sampled(mm):
+    _full_size(mm, "moe_share", [0, 64, 128])
