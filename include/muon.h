@@ -18,10 +18,13 @@
  *   W  <- W - lr * scale * O                parameter update
  *
  * Precision: G is float32 or bfloat16; W and B are float32 and updated in
- * place in float32.  Every matrix product of the iteration runs on bf16
- * matrix cores with float32 accumulation; A and P are stored as bf16; the
- * iterate X is carried as a pair of bf16 values (high part and rounding
- * residual) so that the linear term a*X keeps ~16 significant bits.
+ * place in float32.  For a Gram side m > 64 every matrix product of the
+ * iteration runs on bf16 matrix cores with float32 accumulation; A and P are
+ * stored as bf16; the iterate X is carried as a pair of bf16 values (high
+ * part and rounding residual) so that the linear term a*X keeps ~16
+ * significant bits.  For m <= 64 (few singular values, where bf16 operand
+ * rounding does not average out and the work is small) the iteration runs
+ * in float32 throughout.
  *
  * Memory: every pointer passed to the step calls is a DEVICE pointer on the
  * current HIP device, except the descriptor arrays themselves (mats, hp and
@@ -146,9 +149,9 @@ typedef struct muon_matrix_plan {
   int32_t transposed; /* 1 when rows > cols: the iteration runs on M^T       */
   int32_t m;          /* Gram side min(rows, cols)                           */
   int32_t n;          /* long side max(rows, cols)                           */
-  int32_t m_pad;      /* m rounded up to the tile edge (zero padded)         */
-  int32_t n_pad;      /* n rounded up to the tile edge (zero padded)         */
-  int32_t reserved;
+  int32_t m_pad;      /* padded Gram side of the iterate buffers (zeros)     */
+  int32_t n_pad;      /* padded long side of the iterate buffers (zeros)     */
+  int32_t fp32_path;  /* 1 when m <= 64: float32 iteration (see below)       */
   int64_t x_offset;   /* byte offset of the iterate buffers in the workspace */
 } muon_matrix_plan_t;
 

@@ -186,6 +186,22 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
     for (int c4 = 0; c4 < 4; ++c4) tile[rl][tx * 4 + c4] = v[c4];
   }
   __syncthreads();
+  if (flags & kSmall) {
+    // Float32 iterate for the small-Gram path.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int il = ty + 16 * k;
+      float v[4];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int jl = tx * 4 + c4;
+        v[c4] = sigma * (tr ? tile[jl][il] : tile[il][jl]);
+      }
+      const int64_t off = static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4;
+      *reinterpret_cast<float4*>(d.xf[0] + off) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    return;
+  }
   __bf16* __restrict__ xh = d.xhi[0];
   __bf16* __restrict__ xl = d.xlo[0];
 #pragma unroll
@@ -233,10 +249,19 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
   const int tx = threadIdx.x & 15;
   const int ty = threadIdx.x >> 4;
   // The padded iterate always covers the whole 64x64 tile: no masking here.
+  const bool small = d.flags & kSmall;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int il = ty + 16 * k;
     const int64_t off = (i0 + il) * d.n_pad + j0 + tx * 4;
+    if (small) {
+      const float4 v = *reinterpret_cast<const float4*>(d.xf[buf] + off);
+      tile[il][tx * 4 + 0] = v.x;
+      tile[il][tx * 4 + 1] = v.y;
+      tile[il][tx * 4 + 2] = v.z;
+      tile[il][tx * 4 + 3] = v.w;
+      continue;
+    }
     uint2 hv = *reinterpret_cast<const uint2*>(xh + off);
     uint2 lv = *reinterpret_cast<const uint2*>(xl + off);
     const float o0 = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);

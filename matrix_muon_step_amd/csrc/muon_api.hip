@@ -39,8 +39,11 @@ struct Item {
 
 struct Plan {
   std::vector<MatDesc> descs;
-  std::vector<int32_t> pre_mom, pre_prep, pre_sym, pre_bx, pre_upd;
-  int64_t tot_mom = 0, tot_prep = 0, tot_sym = 0, tot_bx = 0, tot_upd = 0;
+  // Prefix tables, in upload order: momentum, prep, sym (Gram/poly), bx,
+  // update, small Gram chunks, small poly (one per small matrix).
+  static constexpr int kTables = 7;
+  std::vector<int32_t> pre[kTables];
+  int64_t tot[kTables] = {0, 0, 0, 0, 0, 0, 0};
   size_t table_bytes = 0;   // descriptors + prefix tables
   size_t total_bytes = 0;
   std::vector<int64_t> x_offset;
@@ -88,15 +91,11 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
   plan.ns_steps = ns_steps;
   plan.descs.resize(n);
   plan.x_offset.resize(n);
-  plan.pre_mom.resize(n + 1);
-  plan.pre_prep.resize(n + 1);
-  plan.pre_sym.resize(n + 1);
-  plan.pre_bx.resize(n + 1);
-  plan.pre_upd.resize(n + 1);
+  for (auto& v : plan.pre) v.resize(n + 1);
 
   size_t off = 0;
   off += align_up(sizeof(MatDesc) * n);
-  off += align_up(sizeof(int32_t) * 5 * (n + 1));
+  off += align_up(sizeof(int32_t) * Plan::kTables * (n + 1));
   plan.table_bytes = off;
 
   int64_t total_partials = 0;
@@ -115,38 +114,38 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
       return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a non-finite lr*scale");
     MatDesc& d = plan.descs[i];
     memset(&d, 0, sizeof(d));
+    const bool small = m <= kSmallGram;
     d.rows = it.rows;
     d.cols = it.cols;
     d.m = static_cast<int32_t>(m);
     d.n = static_cast<int32_t>(nn);
-    d.m_pad = static_cast<int32_t>(round_up(m, kTile));
-    d.n_pad = static_cast<int32_t>(round_up(nn, kTile));
-    d.flags = it.flags | (tr ? kTransposed : 0);
+    d.m_pad = static_cast<int32_t>(small ? kSmallGram : round_up(m, kTile));
+    d.n_pad = static_cast<int32_t>(round_up(nn, small ? kSmallChunk : kTile));
+    d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0);
     d.lr_scale = it.lr_scale;
+    d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
     const int64_t elems = it.rows * it.cols;
     d.mom_blocks = static_cast<int32_t>((elems + kMomChunk - 1) / kMomChunk);
     total_partials += d.mom_blocks;
 
     const int64_t tm = d.m_pad / kTile, tn = d.n_pad / kTile;
-    plan.pre_mom[i] = static_cast<int32_t>(plan.tot_mom);
-    plan.pre_prep[i] = static_cast<int32_t>(plan.tot_prep);
-    plan.pre_sym[i] = static_cast<int32_t>(plan.tot_sym);
-    plan.pre_bx[i] = static_cast<int32_t>(plan.tot_bx);
-    plan.pre_upd[i] = static_cast<int32_t>(plan.tot_upd);
-    plan.tot_mom += d.mom_blocks;
-    plan.tot_prep += (d.m_pad / kEwTile) * (d.n_pad / kEwTile);
-    plan.tot_sym += tm * (tm + 1) / 2;
-    plan.tot_bx += tm * tn;
-    plan.tot_upd += ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
+    const int64_t work[Plan::kTables] = {
+        d.mom_blocks,
+        (d.m_pad / kEwTile) * (d.n_pad / kEwTile),
+        small ? 0 : tm * (tm + 1) / 2,
+        small ? 0 : tm * tn,
+        ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile),
+        small ? d.s_chunks : 0,
+        small ? 1 : 0,
+    };
     const int64_t lim = (int64_t{1} << 31) - 1;
-    if (plan.tot_mom > lim || plan.tot_prep > lim || plan.tot_bx > lim || plan.tot_upd > lim)
-      return fail(MUON_ERR_UNSUPPORTED, "muon: too many work-groups for one launch");
+    for (int k = 0; k < Plan::kTables; ++k) {
+      plan.pre[k][i] = static_cast<int32_t>(plan.tot[k]);
+      plan.tot[k] += work[k];
+      if (plan.tot[k] > lim) return fail(MUON_ERR_UNSUPPORTED, "muon: too many work-groups for one launch");
+    }
   }
-  plan.pre_mom[n] = static_cast<int32_t>(plan.tot_mom);
-  plan.pre_prep[n] = static_cast<int32_t>(plan.tot_prep);
-  plan.pre_sym[n] = static_cast<int32_t>(plan.tot_sym);
-  plan.pre_bx[n] = static_cast<int32_t>(plan.tot_bx);
-  plan.pre_upd[n] = static_cast<int32_t>(plan.tot_upd);
+  for (int k = 0; k < Plan::kTables; ++k) plan.pre[k][n] = static_cast<int32_t>(plan.tot[k]);
 
   // Partials and sigma.
   const size_t partial_off = off;
@@ -164,6 +163,18 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
   for (int64_t i = 0; i < n; ++i) {
     MatDesc& d = plan.descs[i];
     plan.x_offset[i] = static_cast<int64_t>(off);
+    if (d.flags & kSmall) {
+      const size_t xb = align_up(sizeof(float) * static_cast<size_t>(d.m_pad) * d.n_pad);
+      d.xf[0] = reinterpret_cast<float*>(off); off += xb;
+      if (ns_steps > 0) {
+        d.xf[1] = reinterpret_cast<float*>(off); off += xb;
+        d.sgram = reinterpret_cast<float*>(off);
+        off += align_up(sizeof(float) * static_cast<size_t>(d.s_chunks) * kSmallGram * kSmallGram);
+        d.spoly = reinterpret_cast<float*>(off);
+        off += align_up(sizeof(float) * kSmallGram * kSmallGram);
+      }
+      continue;
+    }
     const size_t xb = align_up(sizeof(__bf16) * static_cast<size_t>(d.m_pad) * d.n_pad);
     const size_t gb = align_up(sizeof(__bf16) * static_cast<size_t>(d.m_pad) * d.m_pad);
     d.xhi[0] = reinterpret_cast<__bf16*>(off); off += xb;
@@ -194,6 +205,10 @@ void bind_workspace(Plan& plan, uintptr_t base) {
     }
     d.gram = rebase(d.gram, base);
     d.poly = rebase(d.poly, base);
+    d.xf[0] = rebase(d.xf[0], base);
+    d.xf[1] = rebase(d.xf[1], base);
+    d.sgram = rebase(d.sgram, base);
+    d.spoly = rebase(d.spoly, base);
   }
 }
 
@@ -318,9 +333,8 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   memcpy(table.data(), plan.descs.data(), sizeof(MatDesc) * n);
   const size_t pre_off = align_up(sizeof(MatDesc) * n);
   int32_t* pre = reinterpret_cast<int32_t*>(table.data() + pre_off);
-  const std::vector<int32_t>* lists[5] = {&plan.pre_mom, &plan.pre_prep, &plan.pre_sym,
-                                          &plan.pre_bx, &plan.pre_upd};
-  for (int k = 0; k < 5; ++k) memcpy(pre + k * (n + 1), lists[k]->data(), sizeof(int32_t) * (n + 1));
+  for (int k = 0; k < Plan::kTables; ++k)
+    memcpy(pre + k * (n + 1), plan.pre[k].data(), sizeof(int32_t) * (n + 1));
 
   const MatDesc* d_desc = reinterpret_cast<const MatDesc*>(base);
   const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pre_off);
@@ -329,38 +343,48 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   const int32_t* p_sym = d_pre + 2 * (n + 1);
   const int32_t* p_bx = d_pre + 3 * (n + 1);
   const int32_t* p_upd = d_pre + 4 * (n + 1);
+  const int32_t* p_sg = d_pre + 5 * (n + 1);
+  const int32_t* p_sp = d_pre + 6 * (n + 1);
+  const int tot_mom = static_cast<int>(plan.tot[0]), tot_prep = static_cast<int>(plan.tot[1]);
+  const int tot_sym = static_cast<int>(plan.tot[2]), tot_bx = static_cast<int>(plan.tot[3]);
+  const int tot_upd = static_cast<int>(plan.tot[4]), tot_sg = static_cast<int>(plan.tot[5]);
+  const int tot_sp = static_cast<int>(plan.tot[6]);
 
   hipError_t e;
   e = run_stage(MUON_STAGE_UPLOAD, s, [&] { return upload_table(table.data(), table.size(), workspace, s); });
   if (e != hipSuccess) return hip_fail(e, "descriptor upload");
   e = run_stage(MUON_STAGE_MOMENTUM, s, [&] {
-    return launch_momentum(d_desc, p_mom, n, static_cast<int>(plan.tot_mom), mu, s);
+    return launch_momentum(d_desc, p_mom, n, tot_mom, mu, s);
   });
   if (e != hipSuccess) return hip_fail(e, "momentum launch");
   e = run_stage(MUON_STAGE_NORM, s, [&] { return launch_norm(d_desc, n, eps, s); });
   if (e != hipSuccess) return hip_fail(e, "norm launch");
   e = run_stage(MUON_STAGE_PREP, s, [&] {
-    return launch_prep(d_desc, p_prep, n, static_cast<int>(plan.tot_prep), mu, s);
+    return launch_prep(d_desc, p_prep, n, tot_prep, mu, s);
   });
   if (e != hipSuccess) return hip_fail(e, "prep launch");
   int buf = 0;
   for (int it = 0; it < plan.ns_steps; ++it) {
-    e = run_stage(MUON_STAGE_GRAM, s, [&] {
-      return launch_gram(d_desc, p_sym, n, static_cast<int>(plan.tot_sym), buf, s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "gram launch");
-    e = run_stage(MUON_STAGE_POLY, s, [&] {
-      return launch_poly(d_desc, p_sym, n, static_cast<int>(plan.tot_sym), s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "poly launch");
-    e = run_stage(MUON_STAGE_BX, s, [&] {
-      return launch_bx(d_desc, p_bx, n, static_cast<int>(plan.tot_bx), buf, s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "bx launch");
+    if (tot_sym > 0) {
+      e = run_stage(MUON_STAGE_GRAM, s, [&] { return launch_gram(d_desc, p_sym, n, tot_sym, buf, s); });
+      if (e != hipSuccess) return hip_fail(e, "gram launch");
+      e = run_stage(MUON_STAGE_POLY, s, [&] { return launch_poly(d_desc, p_sym, n, tot_sym, s); });
+      if (e != hipSuccess) return hip_fail(e, "poly launch");
+      e = run_stage(MUON_STAGE_BX, s, [&] { return launch_bx(d_desc, p_bx, n, tot_bx, buf, s); });
+      if (e != hipSuccess) return hip_fail(e, "bx launch");
+    }
+    if (tot_sg > 0) {
+      e = run_stage(MUON_STAGE_GRAM, s, [&] { return launch_small_gram(d_desc, p_sg, n, tot_sg, buf, s); });
+      if (e != hipSuccess) return hip_fail(e, "small gram launch");
+      e = run_stage(MUON_STAGE_POLY, s, [&] { return launch_small_poly(d_desc, p_sp, n, tot_sp, s); });
+      if (e != hipSuccess) return hip_fail(e, "small poly launch");
+      e = run_stage(MUON_STAGE_BX, s, [&] { return launch_small_bx(d_desc, p_sg, n, tot_sg, buf, s); });
+      if (e != hipSuccess) return hip_fail(e, "small bx launch");
+    }
     buf ^= 1;
   }
   e = run_stage(MUON_STAGE_UPDATE, s, [&] {
-    return launch_update(d_desc, p_upd, n, static_cast<int>(plan.tot_upd), buf, s);
+    return launch_update(d_desc, p_upd, n, tot_upd, buf, s);
   });
   if (e != hipSuccess) return hip_fail(e, "update launch");
   return MUON_OK;
@@ -549,11 +573,12 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
   st = make_plan(items, hp->ns_steps, plan);
   if (st != MUON_OK) return st;
   info->workspace_bytes = static_cast<int64_t>(plan.total_bytes);
-  info->launches = 4 + 3 * static_cast<int64_t>(hp->ns_steps);  // kernels; the table copy is extra
-  info->gram_tiles = plan.tot_sym;
-  info->poly_tiles = plan.tot_sym;
-  info->bx_tiles = plan.tot_bx;
-  info->ew_blocks = plan.tot_mom;
+  const int64_t groups = (plan.tot[2] > 0 ? 1 : 0) + (plan.tot[5] > 0 ? 1 : 0);
+  info->launches = 4 + 3 * groups * static_cast<int64_t>(hp->ns_steps);  // kernels; the table copy is extra
+  info->gram_tiles = plan.tot[2];
+  info->poly_tiles = plan.tot[2];
+  info->bx_tiles = plan.tot[3];
+  info->ew_blocks = plan.tot[0];
   if (per_matrix) {
     for (int64_t i = 0; i < n; ++i) {
       const MatDesc& d = plan.descs[i];
@@ -563,7 +588,7 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
       p.n = d.n;
       p.m_pad = d.m_pad;
       p.n_pad = d.n_pad;
-      p.reserved = 0;
+      p.fp32_path = (d.flags & kSmall) ? 1 : 0;
       p.x_offset = plan.x_offset[i];
     }
   }

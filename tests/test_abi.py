@@ -150,9 +150,25 @@ def test_plan_transpose_rule_and_padding():
     assert [m["transposed"] for m in mats] == [0, 0, 1, 1, 0, 0]
     for m, (r, c) in zip(mats, [(1600, 1600), (1600, 6400), (6400, 1600), (33, 17), (17, 33), (1, 1)]):
         assert m["m"] == min(r, c) and m["n"] == max(r, c)
-        assert m["m_pad"] % t == 0 and m["m"] <= m["m_pad"] < m["m"] + t
-        assert m["n_pad"] % t == 0 and m["n"] <= m["n_pad"] < m["n"] + t
         assert m["x_offset"] % 256 == 0
+        if m["m"] <= 64:
+            # float32 small-Gram path: 64 x (n rounded up to 256)
+            assert m["fp32_path"] == 1 and m["m_pad"] == 64
+            assert m["n_pad"] % 256 == 0 and m["n"] <= m["n_pad"] < m["n"] + 256
+        else:
+            assert m["fp32_path"] == 0
+            assert m["m_pad"] % t == 0 and m["m"] <= m["m_pad"] < m["m"] + t
+            assert m["n_pad"] % t == 0 and m["n"] <= m["n_pad"] < m["n"] + t
+
+
+def test_plan_small_path_threshold():
+    info, mats = mm.muon_plan_query([(64, 1000), (1000, 64), (65, 1000), (1000, 65)])
+    assert [m["fp32_path"] for m in mats] == [1, 1, 0, 0]
+    # Small matrices add no matrix-core tiles; mixing both paths adds launches.
+    assert info["launches"] == 4 + 2 * 3 * 5
+    info_big, _ = mm.muon_plan_query([(65, 1000), (1000, 65)])
+    assert info_big["gram_tiles"] == info["gram_tiles"] and info_big["bx_tiles"] == info["bx_tiles"]
+    assert info_big["launches"] == 4 + 3 * 5
 
 
 def test_plan_tile_counts_and_workspace():

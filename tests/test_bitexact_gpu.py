@@ -57,7 +57,8 @@ def test_fingerprint_grouped_bit_exact(mm):
 
 def test_partial_permutation_five_steps(mm):
     """Support and signs exact; every nonzero magnitude bit-identical to the
-    others; the common value within 1e-2 of p^5(2^-j)."""
+    others; the common value within 2e-2 of p^5(2^-j) and equal to the
+    precision scheme's scalar value."""
     print("[case] partial permutation", flush=True)
     cases = [(300, 200, 3), (200, 300, 3), (1100, 1030, 5)]
     Ms = [synth.signed_partial_permutation(r, c, 4 ** j, [61, r, c]) for r, c, j in cases]
@@ -70,7 +71,32 @@ def test_partial_permutation_five_steps(mm):
         mags = np.abs(On[M != 0])
         assert np.all(mags.view(np.uint32) == mags.view(np.uint32)[0])
         expect = np.abs(ref[M != 0][0])
-        assert abs(mags[0] - expect) <= 1e-2 * expect
+        assert abs(mags[0] - expect) <= 2e-2 * expect
+        assert mags[0] == scheme_scalar(2.0 ** -j, 5)
+
+
+def _bf16(x):
+    return np.float32(torch.tensor(float(x), dtype=torch.float32).to(torch.bfloat16).float().item())
+
+
+def scheme_scalar(x0, steps):
+    """The iteration on one singular value in the library's stated precision
+    scheme: iterate carried as a bf16 pair, A and P rounded to bf16, float32
+    accumulation and epilogues (each a*b+c rounded once).  On an isolated
+    singular value every product is exact, so the GPU must match this bit
+    for bit."""
+    f = np.float32
+    a, b, c = f(3.4445), f(-4.7750), f(2.0315)
+    x = f(x0)
+    xh = _bf16(x)
+    xl = _bf16(f(x - xh))
+    for _ in range(steps):
+        A = _bf16(f(xh * xh))
+        P = _bf16(f(np.float64(c) * np.float64(f(A * A)) + np.float64(f(b * A))))
+        xn = f(np.float64(a) * np.float64(f(xh + xl)) + np.float64(f(P * xh)))
+        xh = _bf16(xn)
+        xl = _bf16(f(xn - xh))
+    return f(xh + xl)
 
 
 def test_grouped_equals_one_by_one(mm):

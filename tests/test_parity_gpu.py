@@ -70,6 +70,35 @@ def test_orthogonalize_matches_oracle(mm, shape):
     assert err <= NS_TOL
 
 
+@pytest.mark.parametrize("shape", [(1, 300), (2, 5), (3, 5), (5, 3), (1, 1), (40, 40), (64, 700), (700, 64),
+                                   (64, 64), (7, 9000)])
+def test_small_gram_path_is_float32(mm, shape):
+    """m <= 64 runs the float32 iteration: far inside the bf16 tolerance even
+    for flat (Gaussian) spectra, where bf16 operands would not be."""
+    log_case(f"small path {shape}")
+    rng = np.random.default_rng(list(shape))
+    M = rng.standard_normal(shape).astype(np.float32)
+    O = mm.muon_orthogonalize([dev(M)], ns_steps=5)[0]
+    torch.cuda.synchronize()
+    err = relfro(O.cpu().numpy(), orc.newton_schulz(M.astype(np.float64), 5))
+    print(f"  relFro {err:.3e}")
+    assert err <= 1e-4
+
+
+@pytest.mark.parametrize("shape", [(65, 300), (300, 65), (96, 96), (128, 256), (200, 200)])
+def test_flat_spectrum_bf16_path(mm, shape):
+    """Gaussian matrices just above the float32 threshold: the hardest case for
+    the bf16 path (singular values spread over the whole band)."""
+    log_case(f"flat spectrum {shape}")
+    rng = np.random.default_rng([7] + list(shape))
+    M = rng.standard_normal(shape).astype(np.float32)
+    O = mm.muon_orthogonalize([dev(M)], ns_steps=5)[0]
+    torch.cuda.synchronize()
+    err = relfro(O.cpu().numpy(), orc.newton_schulz(M.astype(np.float64), 5))
+    print(f"  relFro {err:.3e}")
+    assert err <= NS_TOL
+
+
 @pytest.mark.parametrize("steps", [0, 1, 2, 3, 6])
 def test_orthogonalize_step_counts(mm, steps):
     log_case(f"ortho steps={steps}")
