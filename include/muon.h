@@ -141,18 +141,20 @@ typedef struct muon_plan_info {
   int64_t poly_tiles;        /* work-groups of one polynomial launch        */
   int64_t bx_tiles;          /* work-groups of one BX + aX launch           */
   int64_t ew_blocks;         /* work-groups of the momentum/norm launch     */
-  int32_t tile;              /* output tile edge of the matrix-core kernels */
+  int32_t tile;              /* symmetric tile edge of the first group      */
   int32_t reserved;
 } muon_plan_info_t;
 
 typedef struct muon_matrix_plan {
-  int32_t transposed; /* 1 when rows > cols: the iteration runs on M^T       */
-  int32_t m;          /* Gram side min(rows, cols)                           */
-  int32_t n;          /* long side max(rows, cols)                           */
-  int32_t m_pad;      /* padded Gram side of the iterate buffers (zeros)     */
-  int32_t n_pad;      /* padded long side of the iterate buffers (zeros)     */
-  int32_t fp32_path;  /* 1 when m <= 64: float32 iteration (see below)       */
-  int64_t x_offset;   /* byte offset of the iterate buffers in the workspace */
+  int32_t transposed;   /* 1 when rows > cols: the iteration runs on M^T          */
+  int32_t m;            /* Gram side min(rows, cols)                              */
+  int32_t n;            /* long side max(rows, cols)                              */
+  int32_t m_pad;        /* padded Gram side of the iterate buffers (zeros)        */
+  int32_t n_pad;        /* padded long side of the iterate buffers (zeros)        */
+  int32_t tile;         /* tile edge of the symmetric products; 0 = float32 path  */
+  int32_t bx_tile_cols; /* long-side tile width of the BX product (0 on float32)  */
+  int32_t reserved;
+  int64_t x_offset;     /* byte offset of the iterate buffers in the workspace    */
 } muon_matrix_plan_t;
 
 muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,

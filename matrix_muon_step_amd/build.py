@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuon.so")
-SOURCES = ["muon_api.hip", "ew_kernels.hip", "gemm_kernels.hip", "small_kernels.hip"]
+SOURCES = ["muon_api.hip", "ew_kernels.hip", "gemm_kernels.hip", "gemm32_kernels.hip", "small_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -139,9 +139,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
   const int mi = find_mat(prefix, nmats, blk);
   const MatDesc& d = descs[mi];
   const int local = blk - prefix[mi];
-  const int tpr = d.n_pad / kEwTile;
+  // The padded extents are multiples of 32 but not always of 64: the last
+  // tile row / column is partial and every write below is masked to them
+  // (4-element groups never straddle a padded edge).
+  const int tpr = (d.n_pad + kEwTile - 1) / kEwTile;
   const int i0 = (local / tpr) * kEwTile;  // X rows (short side)
   const int j0 = (local % tpr) * kEwTile;  // X cols (long side)
+  const int m_pad = d.m_pad, n_pad = d.n_pad;
   const int flags = d.flags;
   const bool tr = flags & kTransposed;
   const bool ortho = flags & kOrthoOnly;
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int il = ty + 16 * k;
+      if (i0 + il >= m_pad || j0 + tx * 4 >= n_pad) continue;
       float v[4];
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
@@ -202,26 +207,42 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
     }
     return;
   }
-  __bf16* __restrict__ xh = d.xhi[0];
-  __bf16* __restrict__ xl = d.xlo[0];
+  // Row-major X_hi (Gram operand) when the iteration runs at all.
+  if (d.x_hi) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int il = ty + 16 * k;
+      if (i0 + il >= m_pad || j0 + tx * 4 >= n_pad) continue;
+      __bf16 h[4];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int jl = tx * 4 + c4;
+        h[c4] = static_cast<__bf16>(sigma * (tr ? tile[jl][il] : tile[il][jl]));
+      }
+      uint2 hv;
+      __builtin_memcpy(&hv, h, 8);
+      *reinterpret_cast<uint2*>(d.x_hi + static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4) = hv;
+    }
+  }
+  // X^T as the bf16 pair: row j of X^T holds column j of X.
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int il = ty + 16 * k;
+    const int jl = ty + 16 * k;
+    if (j0 + jl >= n_pad || i0 + tx * 4 >= m_pad) continue;
     __bf16 h[4], l[4];
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
-      const int jl = tx * 4 + c4;
-      const float m = tr ? tile[jl][il] : tile[il][jl];
-      const float x = sigma * m;
+      const int il = tx * 4 + c4;
+      const float x = sigma * (tr ? tile[jl][il] : tile[il][jl]);
       h[c4] = static_cast<__bf16>(x);
       l[c4] = static_cast<__bf16>(x - static_cast<float>(h[c4]));
     }
-    const int64_t off = static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4;
+    const int64_t off = static_cast<int64_t>(j0 + jl) * d.m_pad + i0 + tx * 4;
     uint2 hv, lv;
     __builtin_memcpy(&hv, h, 8);
     __builtin_memcpy(&lv, l, 8);
-    *reinterpret_cast<uint2*>(xh + off) = hv;
-    *reinterpret_cast<uint2*>(xl + off) = lv;
+    *reinterpret_cast<uint2*>(d.xt_hi[0] + off) = hv;
+    *reinterpret_cast<uint2*>(d.xt_lo[0] + off) = lv;
   }
 }
 
@@ -241,37 +262,40 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
   const int64_t c0 = static_cast<int64_t>(local % tpr) * kEwTile;
   const bool tr = d.flags & kTransposed;
   const bool ortho = d.flags & kOrthoOnly;
-  const int64_t i0 = tr ? c0 : r0;
-  const int64_t j0 = tr ? r0 : c0;
-  const __bf16* __restrict__ xh = d.xhi[buf];
-  const __bf16* __restrict__ xl = d.xlo[buf];
+  const bool small = d.flags & kSmall;
+  // Source orientation: the big path keeps X^T (n_pad x m_pad), the small
+  // path X (kSmallGram x n_pad).  O[r][c] is source[r][c] ("direct") when
+  // the source already has W's orientation, else source[c][r].
+  const bool direct = small ? !tr : tr;
+  const int64_t s0 = direct ? r0 : c0;  // first source row of this tile
+  const int64_t s1 = direct ? c0 : r0;  // first source column
   __shared__ float tile[kEwTile][kEwTile + 1];
   const int tx = threadIdx.x & 15;
   const int ty = threadIdx.x >> 4;
-  // The padded iterate always covers the whole 64x64 tile: no masking here.
-  const bool small = d.flags & kSmall;
+  // Source extents (padded); a 64x64 tile may reach past them when the pad
+  // is not a multiple of 64, and those cells are never used for W.
+  const int64_t src_rows = small ? d.m_pad : d.n_pad;
+  const int64_t src_cols = small ? d.n_pad : d.m_pad;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int il = ty + 16 * k;
-    const int64_t off = (i0 + il) * d.n_pad + j0 + tx * 4;
+    const int sl = ty + 16 * k;
+    if (s0 + sl >= src_rows || s1 + tx * 4 >= src_cols) continue;
     if (small) {
+      const int64_t off = (s0 + sl) * d.n_pad + s1 + tx * 4;
       const float4 v = *reinterpret_cast<const float4*>(d.xf[buf] + off);
-      tile[il][tx * 4 + 0] = v.x;
-      tile[il][tx * 4 + 1] = v.y;
-      tile[il][tx * 4 + 2] = v.z;
-      tile[il][tx * 4 + 3] = v.w;
+      tile[sl][tx * 4 + 0] = v.x;
+      tile[sl][tx * 4 + 1] = v.y;
+      tile[sl][tx * 4 + 2] = v.z;
+      tile[sl][tx * 4 + 3] = v.w;
       continue;
     }
-    uint2 hv = *reinterpret_cast<const uint2*>(xh + off);
-    uint2 lv = *reinterpret_cast<const uint2*>(xl + off);
-    const float o0 = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
-    const float o1 = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
-    const float o2 = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
-    const float o3 = __uint_as_float(hv.y & 0xffff0000u) + __uint_as_float(lv.y & 0xffff0000u);
-    tile[il][tx * 4 + 0] = o0;
-    tile[il][tx * 4 + 1] = o1;
-    tile[il][tx * 4 + 2] = o2;
-    tile[il][tx * 4 + 3] = o3;
+    const int64_t off = (s0 + sl) * d.m_pad + s1 + tx * 4;
+    const uint2 hv = *reinterpret_cast<const uint2*>(d.xt_hi[buf] + off);
+    const uint2 lv = *reinterpret_cast<const uint2*>(d.xt_lo[buf] + off);
+    tile[sl][tx * 4 + 0] = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
+    tile[sl][tx * 4 + 1] = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
+    tile[sl][tx * 4 + 2] = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
+    tile[sl][tx * 4 + 3] = __uint_as_float(hv.y & 0xffff0000u) + __uint_as_float(lv.y & 0xffff0000u);
   }
   __syncthreads();
   const float ls = d.lr_scale;
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
       const int cl = tx * 4 + c4;
       const int64_t c = c0 + cl;
       if (c >= cols) continue;
-      const float o = tr ? tile[cl][rl] : tile[rl][cl];
+      const float o = direct ? tile[rl][cl] : tile[cl][rl];
       const int64_t e = r * cols + c;
       if (ortho) W[e] = o;
       else W[e] = fmaf(-ls, o, W[e]);

@@ -1,0 +1,397 @@
+// Wide-tile matrix-core kernels of the Newton-Schulz iteration on gfx950
+// (v_mfma_f32_32x32x16_bf16, two waves per SIMD).
+//
+// The quintic step of the Muon synthesis note (papers.chlience.com,
+// section 4) is evaluated as A = X_hi X_hi^T, P = b A + c A A^T and
+// X' = a (X_hi + X_lo) + P X_hi, exactly as in gemm_kernels.hip (same
+// layouts, same epilogue arithmetic, so the two kernel families are
+// interchangeable per matrix); this file holds the bigger tiles:
+//
+//   G256 : 256 x 256 output tile, 8 waves as 2 x 4, wave tile 128 x 64.
+//          Gram, polynomial (upper tiles) and BX.
+//   W160 : 160 x 256 output tile (160 rows on the Gram side m, 256 columns on
+//          the long side n), 4 waves as 1 x 4, wave tile 160 x 64.  BX only,
+//          for Gram sides that are multiples of 160 but not of 256.
+//
+// A 32x32x16 MFMA does twice the work of a 16x16x32 one per instruction
+// and keeps the matrix pipe full from two waves per SIMD; wave tiles of
+// 128 x 64 / 160 x 64 read 12 / 14 KB of LDS fragments per 32-deep k-step
+// for 16 / 20 MFMAs.
+//
+// Main loop: a ring of three LDS stages (32 k each) is filled by
+// direct-to-LDS 16-byte loads issued two steps ahead.  Fragment reads are
+// ordinary LDS loads inside a step function whose stage pointers are
+// __restrict__ (the stage being filled and the stage being read are always
+// different ring slots), which lets the compiler order the reads against
+// the in-flight direct-to-LDS loads without a blanket wait.  Each wave
+// waits for its own loads (vmcnt) and a barrier publishes a stage.
+// Operand rows are 64 bytes in LDS with the four 16-byte k-chunks
+// XOR-swizzled by row ((r >> 1) ^ (r >> 3)), conflict-free for the 32-row
+// fragment reads; rows 32 apart share the swizzle, so one base address per
+// k16 half serves every fragment of a wave (+2048 bytes per 32 rows).
+//
+// Epilogue: a 32x32 accumulator holds, per lane, column (lane & 31) and
+// rows 8g + 4 (lane >> 5) + r (g, r = 0..3): four runs of four consecutive
+// rows, stored transposed straight from registers as 8-byte writes; the
+// row-major copy goes through a private 32-row LDS slice per wave.
+#include "muon_internal.h"
+
+namespace muon {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+#define GAS __attribute__((address_space(1)))
+#define LAS __attribute__((address_space(3)))
+#define MUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
+constexpr float kCoefA = 3.4445f;
+constexpr float kCoefB = -4.7750f;
+constexpr float kCoefC = 2.0315f;
+
+enum Mode { GRAM = 0, POLY = 1, BXM = 2 };
+
+template <int BM_, int BN_, int NWM_, int NWN_>
+struct G32 {
+  static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+  static constexpr int NW = NWM * NWN;
+  static constexpr int kThreads = NW * 64;
+  static constexpr int WM = BM / NWM, WN = BN / NWN;
+  static constexpr int BMB = WM / 32, BNB = WN / 32;
+  static constexpr int QA = BM / 16, QB = BN / 16;        // 1 KB load instructions per step
+  static constexpr int QAMAX = (QA + NW - 1) / NW;
+  static constexpr int QBMAX = (QB + NW - 1) / NW;
+  static constexpr int OPA = BM * 64, OPB = BN * 64;      // bytes per stage
+  static constexpr int STAGEB = OPA + OPB;
+  static constexpr int NSTAGE = 3;
+  static constexpr int SLICE_LD = WN + 8;                 // epilogue slice row stride (elements)
+  static constexpr int SLICEB = 32 * SLICE_LD * 2;        // bytes per wave
+  static constexpr int LDSB = (NSTAGE * STAGEB > SLICEB * NW) ? NSTAGE * STAGEB : SLICEB * NW;
+  static constexpr int MINB = (NW == 4) ? 2 : 1;          // two waves per SIMD
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(NW == 4 || NW == 8, "swizzle invariance of the load slots assumes 4 or 8 waves");
+};
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+
+__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
+  int lo = 0, hi = nmats - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
+  uint16_t ux, uy;
+  __builtin_memcpy(&ux, &x, 2);
+  __builtin_memcpy(&uy, &y, 2);
+  return static_cast<uint32_t>(ux) | (static_cast<uint32_t>(uy) << 16);
+}
+
+// Waits until at most `newer` later steps of this wave's loads are in flight
+// (`per` loads per step, a compile-time count for each wave class).
+template <int PER>
+__device__ __forceinline__ void wait_newer(int newer) {
+  if (newer <= 0) MUON_WAIT_VM(0);
+  else MUON_WAIT_VM(PER);
+}
+
+template <class C>
+struct Slots {
+  int a0, b0;       // element offset of this lane's first A / B load slot
+  int astr, bstr;   // element stride between its successive slots
+  int na, nb;       // slots per step (A, B)
+};
+
+template <class C>
+__device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                            const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
+                                            int wave) {
+#pragma unroll
+  for (int i = 0; i < C::QAMAX; ++i) {
+    const int q = wave + i * C::NW;
+    if (i < C::QAMAX - 1 || q < C::QA)
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.a0 + i * sl.astr + k0),
+                                       (LAS void*)(dst + q * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < C::QBMAX; ++i) {
+    const int q = wave + i * C::NW;
+    if (i < C::QBMAX - 1 || q < C::QB)
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.b0 + i * sl.bstr + k0),
+                                       (LAS void*)(dst + C::OPA + q * 1024), 16, 0, 0);
+  }
+}
+
+// One 32-deep k-step: optionally queue a future step's loads into `dst`,
+// then multiply the fragments of the stage at `src`.
+template <class C>
+__device__ __forceinline__ void kstep(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                      const Slots<C>& sl, int kfut, bool queue,
+                                      LAS unsigned char* __restrict__ dst,
+                                      const LAS unsigned char* __restrict__ src,
+                                      f32x16_t (&acc)[C::BMB][C::BNB], int wave,
+                                      const int (&abase)[2], const int (&bbase)[2]) {
+  if (queue) issue_loads<C>(Aop, Bop, sl, kfut, dst, wave);
+  bf16x8_t a[2][C::BMB], b[2][C::BNB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j) b[h][j] = *(const LAS bf16x8_t*)(src + bbase[h] + j * 2048);
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) a[h][i] = *(const LAS bf16x8_t*)(src + abase[h] + i * 2048);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+}
+
+template <class C, int MODE>
+__global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
+    const MatDesc* __restrict__ descs, const int32_t* __restrict__ prefix, int nmats, XcdSplit split, int buf) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDSB];
+
+  // XCD-aware work: XCD (block id % 8) walks its own cost-balanced
+  // contiguous range of (matrix, tile) work.
+  const int work = split.start[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
+  if (work >= split.start[(blockIdx.x & 7) + 1]) return;
+  const int mi = find_mat(prefix, nmats, work);
+  const MatDesc& d = descs[mi];
+  int local = work - prefix[mi];
+  const int m_pad = d.m_pad, n_pad = d.n_pad;
+
+  int ti, tj;
+  if (MODE == BXM) {
+    const int tpc = m_pad / C::BM;   // Gram-side index fastest: running tiles share X^T panels
+    tj = local / tpc;
+    ti = local - tj * tpc;
+  } else {
+    const int nt = m_pad / C::BM;
+    ti = 0;
+    while (local >= nt - ti) {
+      local -= nt - ti;
+      ++ti;
+    }
+    tj = ti + local;
+  }
+
+  const __bf16* __restrict__ Aop;
+  const __bf16* __restrict__ Bop;
+  int ld, K;
+  if (MODE == GRAM) {
+    Aop = d.x_hi + static_cast<int64_t>(ti) * C::BM * n_pad;
+    Bop = d.x_hi + static_cast<int64_t>(tj) * C::BN * n_pad;
+    ld = n_pad;
+    K = d.k_gram;
+  } else if (MODE == POLY) {
+    Aop = d.gram + static_cast<int64_t>(ti) * C::BM * m_pad;
+    Bop = d.gram + static_cast<int64_t>(tj) * C::BN * m_pad;
+    ld = K = m_pad;
+  } else {
+    Aop = d.poly + static_cast<int64_t>(ti) * C::BM * m_pad;
+    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * C::BN * m_pad;
+    ld = K = m_pad;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / C::NWN, wc = wave - wr * C::NWN;
+
+  // Load slots: instruction q covers operand rows 16q..16q+15, lane l fills
+  // LDS position l%4 of row 16q + l/4 with the k-chunk the swizzle maps
+  // there.  Rows of one wave's successive slots are NW*16 apart, which
+  // leaves the swizzle unchanged, so slot i is slot 0 plus i*NW*16 rows.
+  Slots<C> sl;
+  {
+    const int r0 = wave * 16 + (lane >> 2);
+    const int c0 = swz(r0, lane & 3);
+    sl.a0 = r0 * ld + c0 * 8;
+    sl.b0 = sl.a0;
+    sl.astr = sl.bstr = C::NW * 16 * ld;
+  }
+  const int na = (C::QA - wave + C::NW - 1) / C::NW;
+  const int nb = (C::QB - wave + C::NW - 1) / C::NW;
+  const int per = na + nb;
+
+  const int a_row0 = wr * C::WM + (lane & 31), b_row0 = wc * C::WN + (lane & 31);
+  int abase[2], bbase[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 2 + (lane >> 5);
+    abase[h] = a_row0 * 64 + swz(a_row0, c) * 16;
+    bbase[h] = C::OPA + b_row0 * 64 + swz(b_row0, c) * 16;
+  }
+
+  f32x16_t acc[C::BMB][C::BNB];
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = K / 32;
+  LAS unsigned char* lds = (LAS unsigned char*)smem;
+  issue_loads<C>(Aop, Bop, sl, 0, lds, wave);
+  if (nk > 1) issue_loads<C>(Aop, Bop, sl, 32, lds + C::STAGEB, wave);
+
+  constexpr int PER_FULL = C::QAMAX + C::QBMAX;
+  for (int kt = 0; kt < nk; ++kt) {
+    // Outstanding: steps kt and (if it exists) kt+1; wait for the older.
+    const int newer = (kt + 1 < nk) ? 1 : 0;
+    if (per == PER_FULL) wait_newer<PER_FULL>(newer);
+    else if (per == PER_FULL - 1) wait_newer<PER_FULL - 1>(newer);
+    else wait_newer<PER_FULL - 2>(newer);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // keep LDS reads and refills of this step below the barrier
+    const int fut = kt + 2;
+    kstep<C>(Aop, Bop, sl, fut * 32, fut < nk, lds + (fut % 3) * C::STAGEB, lds + (kt % 3) * C::STAGEB,
+             acc, wave, abase, bbase);
+  }
+  __syncthreads();
+
+  // ---- epilogue (wave-local).
+  const bool diag = (MODE != BXM) && (ti == tj);
+  const int wi0 = ti * C::BM + wr * C::WM;   // first global row of the wave's sub-tile
+  const int wj0 = tj * C::BN + wc * C::WN;   // first global column
+  __bf16* slice = reinterpret_cast<__bf16*>(smem) + wave * (C::SLICEB / 2);
+  __bf16* rdst;
+  int64_t rld;
+  if (MODE == BXM) { rdst = d.x_hi; rld = n_pad; }
+  else { rdst = (MODE == POLY) ? d.poly : d.gram; rld = m_pad; }
+  const int col = lane & 31;
+  const int rq = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i) {
+    // Global reads of this block row first (independent, mostly from HBM).
+    uint2 in_a[C::BNB][4], in_b[C::BNB][4];
+    if (MODE != GRAM) {
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int gi = wi0 + i * 32 + 8 * g + rq;
+          const int gj = wj0 + j * 32 + col;
+          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+          if (MODE == BXM) {
+            in_a[j][g] = *reinterpret_cast<const uint2*>(d.xt_hi[buf] + off);
+            in_b[j][g] = *reinterpret_cast<const uint2*>(d.xt_lo[buf] + off);
+          } else {
+            in_a[j][g] = *reinterpret_cast<const uint2*>(d.gram + off);  // A symmetric
+          }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gi = wi0 + i * 32 + 8 * g + rq;
+        const int gj = wj0 + j * 32 + col;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
+        uint32_t w0, w1;
+        if (MODE == BXM) {
+          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+          const uint2 hx = in_a[j][g], lx = in_b[j][g];
+          v[0] = fmaf(kCoefA, bf_lo(hx.x) + bf_lo(lx.x), v[0]);
+          v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), v[1]);
+          v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), v[2]);
+          v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), v[3]);
+          w0 = pack_bf16(v[0], v[1]);
+          w1 = pack_bf16(v[2], v[3]);
+          const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
+          const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
+          *reinterpret_cast<uint2*>(d.xt_hi[buf ^ 1] + off) = make_uint2(w0, w1);
+          *reinterpret_cast<uint2*>(d.xt_lo[buf ^ 1] + off) = make_uint2(l0, l1);
+        } else {
+          if (MODE == POLY) {
+            const uint2 a = in_a[j][g];
+            v[0] = fmaf(kCoefC, v[0], kCoefB * bf_lo(a.x));
+            v[1] = fmaf(kCoefC, v[1], kCoefB * bf_hi(a.x));
+            v[2] = fmaf(kCoefC, v[2], kCoefB * bf_lo(a.y));
+            v[3] = fmaf(kCoefC, v[3], kCoefB * bf_hi(a.y));
+          }
+          w0 = pack_bf16(v[0], v[1]);
+          w1 = pack_bf16(v[2], v[3]);
+          __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;  // mirror position
+          if (!diag || gi + 3 <= gj) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+          } else {
+            const uint32_t wv[2] = {w0, w1};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (gi + r <= gj) {
+                const uint16_t bits = static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16));
+                __builtin_memcpy(p + r, &bits, 2);
+              }
+            }
+          }
+        }
+        // row-major copy of the high parts into the wave's 32-row slice
+        const int rl = 8 * g + rq;
+        const int cl = j * 32 + col;
+        const uint16_t hb[4] = {static_cast<uint16_t>(w0), static_cast<uint16_t>(w0 >> 16),
+                                static_cast<uint16_t>(w1), static_cast<uint16_t>(w1 >> 16)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::SLICE_LD + cl, &hb[r], 2);
+      }
+    }
+    // Slice (32 rows x WN) -> global rows, 16 bytes at a time.  The wave's
+    // own LDS writes are ordered before its reads by the compiler.
+    constexpr int CPR = C::WN / 8;
+#pragma unroll
+    for (int c = lane; c < 32 * CPR; c += 64) {
+      const int rl = c / CPR;
+      const int cc = c - rl * CPR;
+      const int gi = wi0 + i * 32 + rl;
+      const int gj = wj0 + cc * 8;
+      const uint4 val = *reinterpret_cast<const uint4*>(slice + rl * C::SLICE_LD + cc * 8);
+      __bf16* p = rdst + static_cast<int64_t>(gi) * rld + gj;
+      if (!diag || gi <= gj) {
+        *reinterpret_cast<uint4*>(p) = val;
+      } else if (gi < gj + 8) {
+        uint16_t hv[8];
+        __builtin_memcpy(hv, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gi <= gj + e) __builtin_memcpy(p + e, &hv[e], 2);
+      }
+    }
+  }
+}
+
+using G256 = G32<256, 256, 2, 4>;
+using W160 = G32<160, 256, 1, 4>;
+
+template <class C, int MODE>
+hipError_t launch(const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp, int buf, hipStream_t s) {
+  if (sp.max_len <= 0) return hipSuccess;
+  hipLaunchKernelGGL((ns_gemm32_kernel<C, MODE>), dim3(8 * sp.max_len), dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
+                            const XcdSplit& split, int buf, hipStream_t s) {
+  if (cfg == kCfgG256) {
+    if (mode == GRAM) return launch<G256, GRAM>(d, prefix, nmats, split, buf, s);
+    if (mode == POLY) return launch<G256, POLY>(d, prefix, nmats, split, buf, s);
+    return launch<G256, BXM>(d, prefix, nmats, split, buf, s);
+  }
+  if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace muon

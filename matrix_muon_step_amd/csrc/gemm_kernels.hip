@@ -2,25 +2,47 @@
 //
 // The quintic step of the Muon synthesis note (papers.chlience.com,
 // section 4), X <- aX + b(XX^T)X + c(XX^T)^2 X with (a,b,c) =
-// (3.4445, -4.7750, 2.0315), is computed as three grouped GEMM launches:
+// (3.4445, -4.7750, 2.0315), is computed as three grouped GEMM launches per
+// iteration:
 //
-//   GRAM : A = X_hi X_hi^T          symmetric: upper 128x128 tiles, mirrored
-//   POLY : P = b A + c A A          symmetric (A A = A A^T): upper tiles,
-//                                   axpy epilogue, mirrored
-//   BX   : X' = a (X_hi + X_lo) + P X_hi   epilogue re-splits X' into the
-//                                   bf16 pair (ping-pong buffers)
+//   GRAM : A  = X_hi X_hi^T             symmetric: upper tiles only
+//   POLY : P  = b A + c A A^T           symmetric (A = A^T): upper tiles,
+//                                       axpy epilogue
+//   BX   : X' = a (X_hi + X_lo) + P X_hi    float32 epilogue, re-split into
+//                                       the bf16 pair
 //
-// All operands are bf16 and go through v_mfma_f32_32x32x16_bf16 with float32
-// accumulation.  One work-group (4 waves, 256 threads) owns a 128x128 output
-// tile; each wave owns a 64x64 quarter as 2x2 MFMA blocks.  K advances 64 at
-// a time through double-buffered LDS with the next slab prefetched into
-// registers while the current one is multiplied.  Every buffer is zero padded
-// to multiples of 128 in both dimensions, so no load or store is masked.
+// Layout.  The iterate is kept twice so every product reads K-contiguous
+// rows of both operands ("NT" form), which is what an MFMA lane consumes:
+//   xt_hi / xt_lo : X^T as n_pad x m_pad bf16 (high part, rounding residual),
+//                   ping-pong between iterations; B operand of BX and the
+//                   source of the aX term;
+//   x_hi          : X_hi as m_pad x n_pad bf16; both operands of GRAM.
+//   gram, poly    : m_pad x m_pad bf16, stored in full (both triangles, bit
+//                   identical), so rows can be read as operands.
+// Every buffer is zero padded to multiples of the tile edge, so the main
+// loop never bounds-checks and padding stays exactly zero.
 //
-// Both operands reach LDS as [row][k] with 8 consecutive k per 16 bytes,
-// which is what an MFMA lane consumes.  GRAM and POLY read K-contiguous rows
-// directly; BX's right operand (X, K x N with N contiguous) is transposed in
-// registers (8 k-rows x 4 columns per thread) on its way into LDS.
+// Kernel.  One work-group owns a T x T output tile; its waves form an
+// NWM x NWN grid, each wave a (T/NWM) x (T/NWN) block of
+// v_mfma_f32_16x16x32_bf16 tiles with float32 accumulators.  K advances 32
+// per step through a ring of three LDS stages filled by direct-to-LDS
+// 16-byte loads (global_load_lds_dwordx4) issued two steps ahead, so no
+// registers stage the operands and two steps of matrix work cover the load
+// latency.  Each wave waits for its own loads (vmcnt) and a barrier makes a
+// stage visible to all.  An LDS row holds the 32 k-values of one operand row
+// as four 16-byte chunks whose positions are XOR-swizzled by the row index,
+// which keeps the 16-lane fragment reads free of bank conflicts.
+//
+// Tile order.  Work-groups are dealt to the 8 XCDs round-robin; the block id
+// is remapped so each XCD walks a contiguous range of (matrix, tile) work,
+// which keeps the operand panels of neighbouring tiles in that XCD's L2.
+//
+// Epilogue.  An MFMA accumulator holds four consecutive rows of one column,
+// so outputs stored transposed (xt_*, and the mirror half of a symmetric
+// tile) go straight from registers as 8-byte stores; row-major outputs
+// (x_hi, the direct half of a symmetric tile) are staged through LDS one
+// band of rows at a time and written as 16-byte rows.  On diagonal tiles
+// each symmetric pair is written from the element with i <= j only.
 #include "muon_internal.h"
 
 namespace muon {
@@ -28,18 +50,125 @@ namespace muon {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kCoefA = 3.4445f;
 constexpr float kCoefB = -4.7750f;
 constexpr float kCoefC = 2.0315f;
 
-constexpr int BM = kTile;   // 128
-constexpr int BK = 64;
-constexpr int LDK = BK + 8; // LDS row stride in bf16 elements (144 bytes)
-constexpr int kThreads = 256;
-
 enum Mode { GRAM = 0, POLY = 1, BXM = 2 };
+
+template <int T_, int NWM_, int NWN_, int NSTAGE_>
+struct Cfg {
+  static constexpr int T = T_;
+  static constexpr int NWM = NWM_;
+  static constexpr int NWN = NWN_;
+  static constexpr int NW = NWM * NWN;
+  static constexpr int kThreads = NW * 64;
+  // Work-groups that must fit on one CU: two waves per SIMD either way.
+  static constexpr int MINB = (NW == 4) ? 2 : 1;
+  static constexpr int WM = T / NWM;
+  static constexpr int WN = T / NWN;
+  static constexpr int BMB = WM / 16;
+  static constexpr int BNB = WN / 16;
+  static constexpr int BK = 32;                      // k per step: 4 chunks of 16 bytes
+  static constexpr int ROWB = BK * 2;                // bytes per LDS row
+  static constexpr int QN = T / 16;                  // 1 KB load instructions per operand per step
+  static constexpr int QMAX = (QN + NW - 1) / NW;    // per wave (some waves one fewer)
+  static constexpr int OPB = T * ROWB;               // bytes of one operand in one stage
+  static constexpr int STAGEB = 2 * OPB;             // A + B
+  static constexpr int NSTAGE = NSTAGE_;            // LDS ring depth; loads run NSTAGE-1 steps ahead
+  // Epilogue: each wave stages its own sub-tile (EPI_ROWS rows at a time)
+  // in a private LDS slice, so no block-wide barrier is needed.
+  static constexpr int EPI_LD = WN + 8;              // staged row stride (elements)
+  static constexpr int EPI_ROWS = (WM * EPI_LD * 2 * NW <= NSTAGE * STAGEB) ? WM : WM / 2;
+  static constexpr int EPIB = EPI_ROWS * EPI_LD * 2; // bytes per wave
+  static constexpr int LDSB = (NSTAGE * STAGEB > EPIB * NW) ? NSTAGE * STAGEB : EPIB * NW;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be a multiple of 16");
+  static_assert(T % 16 == 0, "tile edge must be a multiple of 16");
+};
+
+// Chunk position of k-chunk c (0..3) in LDS row r.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+
+// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
+#define MUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
+#define GAS __attribute__((address_space(1)))
+#define LAS __attribute__((address_space(3)))
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS fragment reads of one k-step.  They are written as one asm block that
+// ends with its own lgkmcnt wait: the compiler cannot see that the stage was
+// filled by direct-to-LDS loads, so it would otherwise guard every LDS read
+// with a wait on all outstanding loads, and no read leaves the block in
+// flight.  A fragment of rows r0 + 16 i sits at byte base + 1024 i, where
+// the base depends only on the parity of i (the chunk swizzle repeats every
+// 32 rows): ae/ao are the even/odd bases of the A operand, be/bo of B.
+#define MUON_DSR(n, b, off) "ds_read_b128 %" #n ", %[" #b "] offset:" #off "\n\t"
+template <int NA, int NB>
+struct FragLoad;
+
+template <>
+struct FragLoad<8, 4> {
+  static __device__ __forceinline__ void run(i32x4_t (&a)[8], i32x4_t (&b)[4], int ae, int ao, int be, int bo) {
+    asm volatile(MUON_DSR(0, ae, 0) MUON_DSR(1, ao, 1024) MUON_DSR(2, ae, 2048) MUON_DSR(3, ao, 3072)
+                 MUON_DSR(4, ae, 4096) MUON_DSR(5, ao, 5120) MUON_DSR(6, ae, 6144) MUON_DSR(7, ao, 7168)
+                 MUON_DSR(8, be, 0) MUON_DSR(9, bo, 1024) MUON_DSR(10, be, 2048) MUON_DSR(11, bo, 3072)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+                   "=&v"(a[6]), "=&v"(a[7]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+                 : [ae] "v"(ae), [ao] "v"(ao), [be] "v"(be), [bo] "v"(bo)
+                 : "memory");
+  }
+};
+
+template <>
+struct FragLoad<5, 5> {
+  static __device__ __forceinline__ void run(i32x4_t (&a)[5], i32x4_t (&b)[5], int ae, int ao, int be, int bo) {
+    asm volatile(MUON_DSR(0, ae, 0) MUON_DSR(1, ao, 1024) MUON_DSR(2, ae, 2048) MUON_DSR(3, ao, 3072)
+                 MUON_DSR(4, ae, 4096)
+                 MUON_DSR(5, be, 0) MUON_DSR(6, bo, 1024) MUON_DSR(7, be, 2048) MUON_DSR(8, bo, 3072)
+                 MUON_DSR(9, be, 4096)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]),
+                   "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4])
+                 : [ae] "v"(ae), [ao] "v"(ao), [be] "v"(be), [bo] "v"(bo)
+                 : "memory");
+  }
+};
+
+template <>
+struct FragLoad<4, 4> {
+  static __device__ __forceinline__ void run(i32x4_t (&a)[4], i32x4_t (&b)[4], int ae, int ao, int be, int bo) {
+    asm volatile(MUON_DSR(0, ae, 0) MUON_DSR(1, ao, 1024) MUON_DSR(2, ae, 2048) MUON_DSR(3, ao, 3072)
+                 MUON_DSR(4, be, 0) MUON_DSR(5, bo, 1024) MUON_DSR(6, be, 2048) MUON_DSR(7, bo, 3072)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
+                   "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+                 : [ae] "v"(ae), [ao] "v"(ao), [be] "v"(be), [bo] "v"(bo)
+                 : "memory");
+  }
+};
+
+// Waits until at most `newer` steps of this wave's direct-to-LDS loads are
+// outstanding (each step issues 2*QMAX or 2*(QMAX-1) loads per wave).
+template <class C>
+__device__ __forceinline__ void wait_steps(int newer, bool full) {
+  if (full) {
+    if (newer <= 0) MUON_WAIT_VM(0);
+    else if (newer == 1) MUON_WAIT_VM(2 * C::QMAX);
+    else if (newer == 2) MUON_WAIT_VM(4 * C::QMAX);
+    else MUON_WAIT_VM(6 * C::QMAX);
+  } else {
+    if (newer <= 0) MUON_WAIT_VM(0);
+    else if (newer == 1) MUON_WAIT_VM(2 * (C::QMAX - 1));
+    else if (newer == 2) MUON_WAIT_VM(4 * (C::QMAX - 1));
+    else MUON_WAIT_VM(6 * (C::QMAX - 1));
+  }
+}
 
 __device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
   int lo = 0, hi = nmats - 1;
@@ -50,31 +179,48 @@ __device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int 
   return lo;
 }
 
-__device__ __forceinline__ float bf2f(__bf16 h) { return static_cast<float>(h); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
-                                                           const int32_t* __restrict__ prefix,
-                                                           int nmats, int buf) {
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][BM * LDK];
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const __bf16 x = static_cast<__bf16>(a);
+  const __bf16 y = static_cast<__bf16>(b);
+  uint16_t ux, uy;
+  __builtin_memcpy(&ux, &x, 2);
+  __builtin_memcpy(&uy, &y, 2);
+  return static_cast<uint32_t>(ux) | (static_cast<uint32_t>(uy) << 16);
+}
 
-  const int blk = blockIdx.x;
-  const int mi = find_mat(prefix, nmats, blk);
+template <class C, int MODE>
+__global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
+                                                              const int32_t* __restrict__ prefix,
+                                                              int nmats, XcdSplit split, int buf) {
+  constexpr int T = C::T;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[C::LDSB];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+
+  // ---- XCD-aware work: XCD (block id % 8) walks its own cost-balanced
+  // contiguous range of (matrix, tile) work.
+  const int work = split.start[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
+  if (work >= split.start[(blockIdx.x & 7) + 1]) return;
+  const int mi = find_mat(prefix, nmats, work);
   const MatDesc& d = descs[mi];
-  int local = blk - prefix[mi];
+  int local = work - prefix[mi];
   const int m_pad = d.m_pad;
   const int n_pad = d.n_pad;
 
   int ti, tj;
   if (MODE == BXM) {
-    const int tpr = n_pad / BM;
-    ti = local / tpr;
-    tj = local - ti * tpr;
+    // Gram-side index fastest: tiles running together share the X^T panels
+    // (read once from HBM) and cycle through the small P.
+    const int tpc = m_pad / T;
+    tj = local / tpc;
+    ti = local - tj * tpc;
   } else {
-    const int T = m_pad / BM;
+    const int nt = m_pad / T;
     ti = 0;
-    while (local >= T - ti) {
-      local -= T - ti;
+    while (local >= nt - ti) {
+      local -= nt - ti;
       ++ti;
     }
     tj = ti + local;
@@ -82,193 +228,252 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDesc* __rest
 
   const __bf16* __restrict__ Aop;
   const __bf16* __restrict__ Bop;
-  int lda, ldb, K;
+  int ld, K;
   if (MODE == GRAM) {
-    Aop = d.xhi[buf] + static_cast<int64_t>(ti) * BM * n_pad;
-    Bop = d.xhi[buf] + static_cast<int64_t>(tj) * BM * n_pad;
-    lda = ldb = K = n_pad;
+    Aop = d.x_hi + static_cast<int64_t>(ti) * T * n_pad;
+    Bop = d.x_hi + static_cast<int64_t>(tj) * T * n_pad;
+    ld = n_pad;
+    K = d.k_gram;
   } else if (MODE == POLY) {
-    Aop = d.gram + static_cast<int64_t>(ti) * BM * m_pad;
-    Bop = d.gram + static_cast<int64_t>(tj) * BM * m_pad;
-    lda = ldb = K = m_pad;
+    Aop = d.gram + static_cast<int64_t>(ti) * T * m_pad;
+    Bop = d.gram + static_cast<int64_t>(tj) * T * m_pad;
+    ld = K = m_pad;
   } else {
-    Aop = d.poly + static_cast<int64_t>(ti) * BM * m_pad;
-    Bop = d.xhi[buf] + static_cast<int64_t>(tj) * BM;  // column offset; rows are k
-    lda = K = m_pad;
-    ldb = n_pad;
+    Aop = d.poly + static_cast<int64_t>(ti) * T * m_pad;
+    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * T * m_pad;
+    ld = K = m_pad;
   }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 1;
-  const int wc = wave & 1;
+  const int wr = wave / C::NWN;
+  const int wc = wave - wr * C::NWN;
+  const int l16 = lane & 15;
+  const int lq = lane >> 4;
 
-  // ---- global -> register prefetch
-  uint4 ra[4];
-  uint4 rb[4];   // NT right operand
-  uint2 rn[8];   // NN right operand (BX)
+  // Direct-to-LDS load slots of this wave: instruction q covers operand rows
+  // 16q..16q+15; lane l fills LDS chunk slot (row 16q + l/4, position l%4)
+  // with the global k-chunk that the swizzle maps there.
+  int g_off[C::QMAX];
+#pragma unroll
+  for (int i = 0; i < C::QMAX; ++i) {
+    const int q = wave + i * C::NW;
+    const int r = q * 16 + (lane >> 2);
+    const int c = swz(r, lane & 3);   // swz is an involution on the chunk index
+    g_off[i] = r * ld + c * 8;
+  }
+  // Loads this wave issues per step (both operands).
+  const int nq = (C::QN - wave + C::NW - 1) / C::NW;
 
-  auto load_tiles = [&](int k0) {
+  auto issue = [&](int k0, int stage) __attribute__((always_inline)) {
+    unsigned char* sb = smem_raw + stage * C::STAGEB;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c >> 3;
-      const int kc = c & 7;
-      ra[r] = *reinterpret_cast<const uint4*>(Aop + static_cast<int64_t>(row) * lda + k0 + kc * 8);
-    }
-    if (MODE == BXM) {
-      const int jb = tid & 31;
-      const int kb = tid >> 5;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int64_t k = k0 + kb * 8 + r;
-        rn[r] = *reinterpret_cast<const uint2*>(Bop + k * ldb + jb * 4);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = tid + kThreads * r;
-        const int row = c >> 3;
-        const int kc = c & 7;
-        rb[r] = *reinterpret_cast<const uint4*>(Bop + static_cast<int64_t>(row) * ldb + k0 + kc * 8);
+    for (int i = 0; i < C::QMAX; ++i) {
+      const int q = wave + i * C::NW;
+      if (i < C::QMAX - 1 || q < C::QN) {
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + k0),
+                                         (LAS void*)(sb + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + k0),
+                                         (LAS void*)(sb + C::OPB + q * 1024), 16, 0, 0);
       }
     }
   };
 
-  auto store_tiles = [&](int sb) {
-    __bf16* As = smem[sb][0];
-    __bf16* Bs = smem[sb][1];
+  f32x4_t acc[C::BMB][C::BNB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c >> 3;
-      const int kc = c & 7;
-      *reinterpret_cast<uint4*>(As + row * LDK + kc * 8) = ra[r];
-    }
-    if (MODE == BXM) {
-      const int jb = tid & 31;
-      const int kb = tid >> 5;
-      // rn[r] holds row k = kb*8 + r, columns jb*4 .. jb*4+3 (two per dword).
+  for (int i = 0; i < C::BMB; ++i)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t lo = (x < 2) ? rn[2 * p].x : rn[2 * p].y;
-          const uint32_t hi = (x < 2) ? rn[2 * p + 1].x : rn[2 * p + 1].y;
-          w[p] = (x & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        *reinterpret_cast<uint4*>(Bs + (jb * 4 + x) * LDK + kb * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = tid + kThreads * r;
-        const int row = c >> 3;
-        const int kc = c & 7;
-        *reinterpret_cast<uint4*>(Bs + row * LDK + kc * 8) = rb[r];
-      }
-    }
-  };
+    for (int j = 0; j < C::BNB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  f32x16_t acc[2][2];
+  const int nk = K / C::BK;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  for (int st = 0; st < C::NSTAGE - 1; ++st)
+    if (st < nk) issue(st * C::BK, st);
 
-  const int nk = K / BK;
-  load_tiles(0);
-  store_tiles(0);
+  // Fragment bases (LDS byte addresses within stage 0) for even / odd row
+  // blocks of this wave; a stage adds stage * STAGEB.
+  const int a_row0 = wr * C::WM + l16;
+  const int b_row0 = wc * C::WN + l16;
+  const int lds0 = static_cast<int>(reinterpret_cast<uintptr_t>((LAS void*)smem_raw));
+  const int a_even = lds0 + a_row0 * C::ROWB + swz(a_row0, lq) * 16;
+  const int a_odd = lds0 + (a_row0 + 16) * C::ROWB + swz(a_row0 + 16, lq) * 16 - 1024;
+  const int b_even = lds0 + C::OPB + b_row0 * C::ROWB + swz(b_row0, lq) * 16;
+  const int b_odd = lds0 + C::OPB + (b_row0 + 16) * C::ROWB + swz(b_row0 + 16, lq) * 16 - 1024;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // Steps kt .. kt+NSTAGE-2 may be outstanding; wait for the oldest.
+    {
+      const int newer = (nk - 1 - kt < C::NSTAGE - 2) ? nk - 1 - kt : C::NSTAGE - 2;
+      wait_steps<C>(newer, nq == C::QMAX);
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // keep LDS reads and refills of this step below the barrier
+    if (kt + C::NSTAGE - 1 < nk) issue((kt + C::NSTAGE - 1) * C::BK, (kt + C::NSTAGE - 1) % C::NSTAGE);
+    const int so = (kt % C::NSTAGE) * C::STAGEB;
+    i32x4_t af[C::BMB], bfr[C::BNB];
+    FragLoad<C::BMB, C::BNB>::run(af, bfr, a_even + so, a_odd + so, b_even + so, b_odd + so);
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[i]);
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                            acc[i][j], 0, 0, 0);
+    }
+  }
   __syncthreads();
 
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int sb = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-    const __bf16* As = smem[sb][0];
-    const __bf16* Bs = smem[sb][1];
+  // ---- epilogue.  16x16 accumulator layout: lane holds column (lane & 15),
+  // register r holds row 4 * (lane >> 4) + r.  Each wave works alone on its
+  // sub-tile: transposed outputs from registers, the row-major copy through
+  // its private LDS slice, EPI_ROWS rows at a time.
+  const bool diag = (MODE != BXM) && (ti == tj);
+  const int wi0 = ti * T + wr * C::WM;      // first global row of the wave's sub-tile
+  const int wj0 = tj * T + wc * C::WN;      // first global column
+  __bf16* slice = smem + wave * (C::EPIB / 2);
+  __bf16* rdst;
+  int64_t rld;
+  if (MODE == BXM) { rdst = d.x_hi; rld = n_pad; }
+  else { rdst = (MODE == POLY) ? d.poly : d.gram; rld = m_pad; }
+  constexpr int HALVES = C::WM / C::EPI_ROWS;
+  constexpr int HB = C::EPI_ROWS / 16;      // row blocks per half
+  // Global reads are issued a batch of PRE block rows at a time (they are
+  // independent and mostly come from HBM), then combined.
+  constexpr int PRE = (16 / C::BNB) > 0 ? (16 / C::BNB) : 1;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ko = ks * 16 + fk;
-      bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(As + (wr * 64 + frow) * LDK + ko);
-      bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(As + (wr * 64 + 32 + frow) * LDK + ko);
-      bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(Bs + (wc * 64 + frow) * LDK + ko);
-      bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(Bs + (wc * 64 + 32 + frow) * LDK + ko);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tiles(sb ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31),
-  // register v holds row 8*(v/4) + 4*(lane/32) + (v%4).
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  for (int h = 0; h < HALVES; ++h) {
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi) {
+  for (int b0 = 0; b0 < HB; b0 += PRE) {
+    constexpr int NPRE = PRE;
+    uint2 in_a[NPRE][C::BNB], in_b[NPRE][C::BNB];
+    if (MODE != GRAM) {
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
+      for (int ib = b0; ib < b0 + NPRE && ib < HB; ++ib) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int il = wr * 64 + bi * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-        const int jl = wc * 64 + bj * 32 + col;
-        const float val = acc[bi][bj][v];
-        const int gi = ti * BM + il;
-        const int gj = tj * BM + jl;
-        if (MODE == BXM) {
-          const int64_t idx = static_cast<int64_t>(gi) * n_pad + gj;
-          const float x = bf2f(d.xhi[buf][idx]) + bf2f(d.xlo[buf][idx]);
-          const float o = fmaf(kCoefA, x, val);
-          const __bf16 h = static_cast<__bf16>(o);
-          const __bf16 l = static_cast<__bf16>(o - bf2f(h));
-          d.xhi[buf ^ 1][idx] = h;
-          d.xlo[buf ^ 1][idx] = l;
-        } else {
-          // Diagonal tiles write each symmetric pair once, from (i <= j).
-          if (ti == tj && gi > gj) continue;
-          float out = val;
-          __bf16* dst;
-          if (MODE == POLY) {
-            out = fmaf(kCoefC, val, kCoefB * bf2f(d.gram[static_cast<int64_t>(gi) * m_pad + gj]));
-            dst = d.poly;
+        for (int j = 0; j < C::BNB; ++j) {
+          const int gi = wi0 + (h * HB + ib) * 16 + lq * 4;
+          const int gj = wj0 + j * 16 + l16;
+          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+          if (MODE == BXM) {
+            in_a[ib - b0][j] = *reinterpret_cast<const uint2*>(d.xt_hi[buf] + off);
+            in_b[ib - b0][j] = *reinterpret_cast<const uint2*>(d.xt_lo[buf] + off);
           } else {
-            dst = d.gram;
+            in_a[ib - b0][j] = *reinterpret_cast<const uint2*>(d.gram + off);
           }
-          const __bf16 h = static_cast<__bf16>(out);
-          dst[static_cast<int64_t>(gi) * m_pad + gj] = h;
-          dst[static_cast<int64_t>(gj) * m_pad + gi] = h;
         }
       }
     }
+#pragma unroll
+    for (int ib = b0; ib < b0 + NPRE && ib < HB; ++ib) {
+      const int i = h * HB + ib;
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j) {
+        const int gi = wi0 + i * 16 + lq * 4;
+        const int gj = wj0 + j * 16 + l16;
+        float v[4];
+        uint32_t w0, w1;
+        if (MODE == BXM) {
+          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+          const uint2 hx = in_a[ib - b0][j];
+          const uint2 lx = in_b[ib - b0][j];
+          v[0] = fmaf(kCoefA, bf_lo(hx.x) + bf_lo(lx.x), acc[i][j][0]);
+          v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), acc[i][j][1]);
+          v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), acc[i][j][2]);
+          v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), acc[i][j][3]);
+          w0 = pack_bf16(v[0], v[1]);
+          w1 = pack_bf16(v[2], v[3]);
+          const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
+          const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
+          *reinterpret_cast<uint2*>(d.xt_hi[buf ^ 1] + off) = make_uint2(w0, w1);
+          *reinterpret_cast<uint2*>(d.xt_lo[buf ^ 1] + off) = make_uint2(l0, l1);
+        } else {
+          if (MODE == POLY) {
+            // A is stored symmetric: A[gi..gi+3][gj] == A[gj][gi..gi+3].
+            const uint2 a = in_a[ib - b0][j];
+            v[0] = fmaf(kCoefC, acc[i][j][0], kCoefB * bf_lo(a.x));
+            v[1] = fmaf(kCoefC, acc[i][j][1], kCoefB * bf_hi(a.x));
+            v[2] = fmaf(kCoefC, acc[i][j][2], kCoefB * bf_lo(a.y));
+            v[3] = fmaf(kCoefC, acc[i][j][3], kCoefB * bf_hi(a.y));
+          } else {
+            v[0] = acc[i][j][0]; v[1] = acc[i][j][1]; v[2] = acc[i][j][2]; v[3] = acc[i][j][3];
+          }
+          w0 = pack_bf16(v[0], v[1]);
+          w1 = pack_bf16(v[2], v[3]);
+          __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;  // mirror position
+          if (!diag || gi + 3 <= gj) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+          } else {
+            const uint32_t wv[2] = {w0, w1};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (gi + r <= gj) {
+                const uint16_t bits = static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16));
+                __builtin_memcpy(p + r, &bits, 2);
+              }
+            }
+          }
+        }
+        // row-major copy of the high parts into the wave's slice
+        const int rl = ib * 16 + lq * 4;
+        const int cl = j * 16 + l16;
+        const uint16_t hb[4] = {static_cast<uint16_t>(w0), static_cast<uint16_t>(w0 >> 16),
+                                static_cast<uint16_t>(w1), static_cast<uint16_t>(w1 >> 16)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::EPI_LD + cl, &hb[r], 2);
+      }
+    }
   }
+    // Slice rows -> global rows, 16 bytes at a time (wave-local; the
+    // compiler orders this wave's LDS writes before its reads).
+    constexpr int CPR = C::WN / 8;
+    for (int c = lane; c < C::EPI_ROWS * CPR; c += 64) {
+      const int rl = c / CPR;
+      const int cc = c - rl * CPR;
+      const int gi = wi0 + h * C::EPI_ROWS + rl;
+      const int gj = wj0 + cc * 8;
+      const uint4 val = *reinterpret_cast<const uint4*>(slice + rl * C::EPI_LD + cc * 8);
+      __bf16* p = rdst + static_cast<int64_t>(gi) * rld + gj;
+      if (!diag || gi <= gj) {
+        *reinterpret_cast<uint4*>(p) = val;
+      } else if (gi < gj + 8) {
+        uint16_t hv[8];
+        __builtin_memcpy(hv, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gi <= gj + e) __builtin_memcpy(p + e, &hv[e], 2);
+      }
+    }
+  }
+}
+
+// Tile configurations: edge T and wave grid.
+using C160 = Cfg<160, 2, 2, 4>;
+using C128 = Cfg<128, 2, 2, 4>;
+
+template <class C>
+hipError_t launch_mode(int mode, const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp,
+                       int buf, hipStream_t s) {
+  if (sp.max_len <= 0) return hipSuccess;
+  const dim3 grid(8 * sp.max_len);
+  if (mode == GRAM)
+    hipLaunchKernelGGL((ns_gemm_kernel<C, GRAM>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+  else if (mode == POLY)
+    hipLaunchKernelGGL((ns_gemm_kernel<C, POLY>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+  else
+    hipLaunchKernelGGL((ns_gemm_kernel<C, BXM>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gram(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(ns_gemm_kernel<GRAM>, dim3(total), dim3(kThreads), 0, s, d, prefix, nmats, buf);
-  return hipGetLastError();
-}
 
-hipError_t launch_poly(const MatDesc* d, const int32_t* prefix, int nmats, int total,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(ns_gemm_kernel<POLY>, dim3(total), dim3(kThreads), 0, s, d, prefix, nmats, 0);
-  return hipGetLastError();
-}
 
-hipError_t launch_bx(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
-                     hipStream_t s) {
-  hipLaunchKernelGGL(ns_gemm_kernel<BXM>, dim3(total), dim3(kThreads), 0, s, d, prefix, nmats, buf);
-  return hipGetLastError();
+hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
+                          const XcdSplit& split, int buf, hipStream_t s) {
+  if (cfg == kCfgT160) return launch_mode<C160>(mode, d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgT128) return launch_mode<C128>(mode, d, prefix, nmats, split, buf, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace muon

@@ -2,6 +2,7 @@
 // descriptor upload and the grouped launch sequence of one Muon step
 // (Muon synthesis note on papers.chlience.com, section 4).
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -37,13 +38,18 @@ struct Item {
   int32_t flags;
 };
 
+// Prefix tables uploaded after the descriptors.  Fixed ones first, then one
+// table per kernel configuration for the symmetric stages (Gram and
+// polynomial share it) and one per configuration for the BX stage.
+enum Table { kTabMom = 0, kTabPrep, kTabUpd, kTabSmallGram, kTabSmallPoly, kTabFixed };
+constexpr int kNumTables = kTabFixed + 2 * kNumCfg;
+int tab_sym(int cfg) { return kTabFixed + cfg; }
+int tab_bx(int cfg) { return kTabFixed + kNumCfg + cfg; }
+
 struct Plan {
   std::vector<MatDesc> descs;
-  // Prefix tables, in upload order: momentum, prep, sym (Gram/poly), bx,
-  // update, small Gram chunks, small poly (one per small matrix).
-  static constexpr int kTables = 7;
-  std::vector<int32_t> pre[kTables];
-  int64_t tot[kTables] = {0, 0, 0, 0, 0, 0, 0};
+  std::vector<int32_t> pre[kNumTables];
+  int64_t tot[kNumTables] = {};
   size_t table_bytes = 0;   // descriptors + prefix tables
   size_t total_bytes = 0;
   std::vector<int64_t> x_offset;
@@ -82,6 +88,57 @@ muon_status_t check_aliasing(std::vector<Range>& rs) {
 
 bool finite(float x) { return isfinite(x); }
 
+// Kernel configurations of one matrix: (symmetric stages, BX stage).
+struct MatCfg {
+  int sym, bx;
+  int64_t m_pad, n_pad;
+};
+
+int64_t upper_tiles(int64_t mp, int t) {
+  const int64_t nt = mp / t;
+  return nt * (nt + 1) / 2;
+}
+
+// Choice of kernel configurations for a Gram side m and long side n: the
+// combination with the least estimated time, i.e. padded matrix-core work
+// (upper tiles for the symmetric products) divided by each configuration's
+// sustained rate on gfx950 (measured: 32x32 wide tiles ~1.1 PF/s, 16x16
+// 160-tiles ~0.85, 128-tiles ~0.7).  MUON_GEMM_CFG=g256|w160|t160|t128
+// forces one combination (tuning).
+MatCfg choose_cfg(int64_t m, int64_t n) {
+  struct Cand { const char* name; int sym, bx; };
+  static const Cand cands[] = {
+      {"g256", kCfgG256, kCfgG256}, {"w160", kCfgT160, kCfgW160},
+      {"t160", kCfgT160, kCfgT160}, {"t128", kCfgT128, kCfgT128}};
+  static const double rate[kNumCfg] = {1.10, 1.00, 0.85, 0.70};
+  static const int forced = [] {
+    const char* e = getenv("MUON_GEMM_CFG");
+    if (!e) return -1;
+    for (int i = 0; i < 4; ++i)
+      if (strcmp(e, cands[i].name) == 0) return i;
+    return -1;
+  }();
+  MatCfg best{};
+  double best_cost = 0.0;
+  for (int i = 0; i < 4; ++i) {
+    if (forced >= 0 && i != forced) continue;
+    const Cand& c = cands[i];
+    const int64_t mp = round_up(m, kCfgRows[c.sym]);
+    if (mp % kCfgRows[c.bx] != 0) continue;
+    const int64_t np = round_up(n, kCfgCols[c.bx]);
+    const int64_t kg = round_up(n, 32);
+    const int t = kCfgRows[c.sym];
+    const double sym_work = static_cast<double>(upper_tiles(mp, t)) * 2.0 * t * t * (kg + mp);
+    const double bx_work = 2.0 * static_cast<double>(mp) * np * mp;
+    const double cost = sym_work / rate[c.sym] + bx_work / rate[c.bx];
+    if (best_cost == 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = MatCfg{c.sym, c.bx, mp, np};
+    }
+  }
+  return best;
+}
+
 // Validates shapes and scalars of every item and fills the plan (offsets
 // relative to a workspace base of 0).  Pointer checks happen separately.
 muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan) {
@@ -95,7 +152,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
 
   size_t off = 0;
   off += align_up(sizeof(MatDesc) * n);
-  off += align_up(sizeof(int32_t) * Plan::kTables * (n + 1));
+  off += align_up(sizeof(int32_t) * kNumTables * (n + 1));
   plan.table_bytes = off;
 
   int64_t total_partials = 0;
@@ -115,12 +172,16 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     MatDesc& d = plan.descs[i];
     memset(&d, 0, sizeof(d));
     const bool small = m <= kSmallGram;
+    const MatCfg cfg = small ? MatCfg{-1, -1, kSmallGram, round_up(nn, kSmallChunk)} : choose_cfg(m, nn);
     d.rows = it.rows;
     d.cols = it.cols;
     d.m = static_cast<int32_t>(m);
     d.n = static_cast<int32_t>(nn);
-    d.m_pad = static_cast<int32_t>(small ? kSmallGram : round_up(m, kTile));
-    d.n_pad = static_cast<int32_t>(round_up(nn, small ? kSmallChunk : kTile));
+    d.sym_cfg = cfg.sym;
+    d.bx_cfg = cfg.bx;
+    d.m_pad = static_cast<int32_t>(cfg.m_pad);
+    d.n_pad = static_cast<int32_t>(cfg.n_pad);
+    d.k_gram = static_cast<int32_t>(round_up(nn, 32));
     d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0);
     d.lr_scale = it.lr_scale;
     d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
@@ -128,24 +189,25 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.mom_blocks = static_cast<int32_t>((elems + kMomChunk - 1) / kMomChunk);
     total_partials += d.mom_blocks;
 
-    const int64_t tm = d.m_pad / kTile, tn = d.n_pad / kTile;
-    const int64_t work[Plan::kTables] = {
-        d.mom_blocks,
-        (d.m_pad / kEwTile) * (d.n_pad / kEwTile),
-        small ? 0 : tm * (tm + 1) / 2,
-        small ? 0 : tm * tn,
-        ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile),
-        small ? d.s_chunks : 0,
-        small ? 1 : 0,
-    };
+    int64_t work[kNumTables] = {};
+    work[kTabMom] = d.mom_blocks;
+    work[kTabPrep] = ((d.m_pad + kEwTile - 1) / kEwTile) * ((d.n_pad + kEwTile - 1) / kEwTile);
+    work[kTabUpd] = ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
+    if (small) {
+      work[kTabSmallGram] = d.s_chunks;
+      work[kTabSmallPoly] = 1;
+    } else {
+      work[tab_sym(cfg.sym)] = upper_tiles(d.m_pad, kCfgRows[cfg.sym]);
+      work[tab_bx(cfg.bx)] = (d.m_pad / kCfgRows[cfg.bx]) * (d.n_pad / kCfgCols[cfg.bx]);
+    }
     const int64_t lim = (int64_t{1} << 31) - 1;
-    for (int k = 0; k < Plan::kTables; ++k) {
+    for (int k = 0; k < kNumTables; ++k) {
       plan.pre[k][i] = static_cast<int32_t>(plan.tot[k]);
       plan.tot[k] += work[k];
       if (plan.tot[k] > lim) return fail(MUON_ERR_UNSUPPORTED, "muon: too many work-groups for one launch");
     }
   }
-  for (int k = 0; k < Plan::kTables; ++k) plan.pre[k][n] = static_cast<int32_t>(plan.tot[k]);
+  for (int k = 0; k < kNumTables; ++k) plan.pre[k][n] = static_cast<int32_t>(plan.tot[k]);
 
   // Partials and sigma.
   const size_t partial_off = off;
@@ -177,11 +239,12 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     }
     const size_t xb = align_up(sizeof(__bf16) * static_cast<size_t>(d.m_pad) * d.n_pad);
     const size_t gb = align_up(sizeof(__bf16) * static_cast<size_t>(d.m_pad) * d.m_pad);
-    d.xhi[0] = reinterpret_cast<__bf16*>(off); off += xb;
-    d.xlo[0] = reinterpret_cast<__bf16*>(off); off += xb;
+    d.xt_hi[0] = reinterpret_cast<__bf16*>(off); off += xb;
+    d.xt_lo[0] = reinterpret_cast<__bf16*>(off); off += xb;
     if (ns_steps > 0) {
-      d.xhi[1] = reinterpret_cast<__bf16*>(off); off += xb;
-      d.xlo[1] = reinterpret_cast<__bf16*>(off); off += xb;
+      d.x_hi = reinterpret_cast<__bf16*>(off); off += xb;
+      d.xt_hi[1] = reinterpret_cast<__bf16*>(off); off += xb;
+      d.xt_lo[1] = reinterpret_cast<__bf16*>(off); off += xb;
       d.gram = reinterpret_cast<__bf16*>(off); off += gb;
       d.poly = reinterpret_cast<__bf16*>(off); off += gb;
     }
@@ -199,14 +262,14 @@ void bind_workspace(Plan& plan, uintptr_t base) {
   for (MatDesc& d : plan.descs) {
     d.partials = rebase(d.partials, base);
     d.sigma = rebase(d.sigma, base);
+    d.x_hi = rebase(d.x_hi, base);
     for (int b = 0; b < 2; ++b) {
-      d.xhi[b] = rebase(d.xhi[b], base);
-      d.xlo[b] = rebase(d.xlo[b], base);
+      d.xt_hi[b] = rebase(d.xt_hi[b], base);
+      d.xt_lo[b] = rebase(d.xt_lo[b], base);
+      d.xf[b] = rebase(d.xf[b], base);
     }
     d.gram = rebase(d.gram, base);
     d.poly = rebase(d.poly, base);
-    d.xf[0] = rebase(d.xf[0], base);
-    d.xf[1] = rebase(d.xf[1], base);
     d.sgram = rebase(d.sgram, base);
     d.spoly = rebase(d.spoly, base);
   }
@@ -318,6 +381,45 @@ hipError_t run_stage(int stage, hipStream_t s, F&& f) {
   return e;
 }
 
+// Cost-balanced split of one grouped GEMM launch over the 8 XCDs.  A tile's
+// cost is taken as its reduction length (tiles of one launch share their
+// shape): k_gram for the Gram stage, m_pad for the polynomial and BX stages.
+XcdSplit make_split(const Plan& plan, int tab, int mode) {
+  const std::vector<int32_t>& pre = plan.pre[tab];
+  const int n = static_cast<int>(plan.descs.size());
+  double total = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double c = (mode == 0) ? plan.descs[i].k_gram : plan.descs[i].m_pad;
+    total += static_cast<double>(pre[i + 1] - pre[i]) * c;
+  }
+  XcdSplit sp;
+  sp.start[0] = 0;
+  sp.start[8] = pre[n];
+  int i = 0;
+  double before = 0.0;  // cost of matrices 0..i-1
+  for (int x = 1; x < 8; ++x) {
+    const double target = total * x / 8.0;
+    while (i < n) {
+      const double c = (mode == 0) ? plan.descs[i].k_gram : plan.descs[i].m_pad;
+      const double mc = static_cast<double>(pre[i + 1] - pre[i]) * c;
+      if (before + mc >= target) break;
+      before += mc;
+      ++i;
+    }
+    int w = pre[n];
+    if (i < n) {
+      const double c = (mode == 0) ? plan.descs[i].k_gram : plan.descs[i].m_pad;
+      const int64_t k = static_cast<int64_t>((target - before) / c + 0.5);
+      const int64_t lo = pre[i], hi = pre[i + 1];
+      w = static_cast<int>(std::min(hi, std::max(lo, lo + k)));
+    }
+    sp.start[x] = std::max(w, sp.start[x - 1]);
+  }
+  sp.max_len = 0;
+  for (int x = 0; x < 8; ++x) sp.max_len = std::max(sp.max_len, sp.start[x + 1] - sp.start[x]);
+  return sp;
+}
+
 muon_status_t hip_fail(hipError_t e, const char* where) {
   return fail(MUON_ERR_HIP, std::string("muon: ") + where + ": " + hipGetErrorString(e));
 }
@@ -333,59 +435,56 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   memcpy(table.data(), plan.descs.data(), sizeof(MatDesc) * n);
   const size_t pre_off = align_up(sizeof(MatDesc) * n);
   int32_t* pre = reinterpret_cast<int32_t*>(table.data() + pre_off);
-  for (int k = 0; k < Plan::kTables; ++k)
+  for (int k = 0; k < kNumTables; ++k)
     memcpy(pre + k * (n + 1), plan.pre[k].data(), sizeof(int32_t) * (n + 1));
 
   const MatDesc* d_desc = reinterpret_cast<const MatDesc*>(base);
   const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pre_off);
-  const int32_t* p_mom = d_pre;
-  const int32_t* p_prep = d_pre + (n + 1);
-  const int32_t* p_sym = d_pre + 2 * (n + 1);
-  const int32_t* p_bx = d_pre + 3 * (n + 1);
-  const int32_t* p_upd = d_pre + 4 * (n + 1);
-  const int32_t* p_sg = d_pre + 5 * (n + 1);
-  const int32_t* p_sp = d_pre + 6 * (n + 1);
-  const int tot_mom = static_cast<int>(plan.tot[0]), tot_prep = static_cast<int>(plan.tot[1]);
-  const int tot_sym = static_cast<int>(plan.tot[2]), tot_bx = static_cast<int>(plan.tot[3]);
-  const int tot_upd = static_cast<int>(plan.tot[4]), tot_sg = static_cast<int>(plan.tot[5]);
-  const int tot_sp = static_cast<int>(plan.tot[6]);
+  auto ptab = [&](int k) { return d_pre + k * (n + 1); };
+  auto ttot = [&](int k) { return static_cast<int>(plan.tot[k]); };
 
   hipError_t e;
   e = run_stage(MUON_STAGE_UPLOAD, s, [&] { return upload_table(table.data(), table.size(), workspace, s); });
   if (e != hipSuccess) return hip_fail(e, "descriptor upload");
-  e = run_stage(MUON_STAGE_MOMENTUM, s, [&] {
-    return launch_momentum(d_desc, p_mom, n, tot_mom, mu, s);
-  });
+  e = run_stage(MUON_STAGE_MOMENTUM, s, [&] { return launch_momentum(d_desc, ptab(kTabMom), n, ttot(kTabMom), mu, s); });
   if (e != hipSuccess) return hip_fail(e, "momentum launch");
   e = run_stage(MUON_STAGE_NORM, s, [&] { return launch_norm(d_desc, n, eps, s); });
   if (e != hipSuccess) return hip_fail(e, "norm launch");
-  e = run_stage(MUON_STAGE_PREP, s, [&] {
-    return launch_prep(d_desc, p_prep, n, tot_prep, mu, s);
-  });
+  e = run_stage(MUON_STAGE_PREP, s, [&] { return launch_prep(d_desc, ptab(kTabPrep), n, ttot(kTabPrep), mu, s); });
   if (e != hipSuccess) return hip_fail(e, "prep launch");
   int buf = 0;
+  static const int stage_of_mode[3] = {MUON_STAGE_GRAM, MUON_STAGE_POLY, MUON_STAGE_BX};
   for (int it = 0; it < plan.ns_steps; ++it) {
-    if (tot_sym > 0) {
-      e = run_stage(MUON_STAGE_GRAM, s, [&] { return launch_gram(d_desc, p_sym, n, tot_sym, buf, s); });
-      if (e != hipSuccess) return hip_fail(e, "gram launch");
-      e = run_stage(MUON_STAGE_POLY, s, [&] { return launch_poly(d_desc, p_sym, n, tot_sym, s); });
-      if (e != hipSuccess) return hip_fail(e, "poly launch");
-      e = run_stage(MUON_STAGE_BX, s, [&] { return launch_bx(d_desc, p_bx, n, tot_bx, buf, s); });
-      if (e != hipSuccess) return hip_fail(e, "bx launch");
+    for (int mode = 0; mode < 3; ++mode) {
+      for (int c = 0; c < kNumCfg; ++c) {
+        const int tab = mode == 2 ? tab_bx(c) : tab_sym(c);
+        if (plan.tot[tab] == 0) continue;
+        const XcdSplit sp = make_split(plan, tab, mode);
+        e = run_stage(stage_of_mode[mode], s, [&] {
+          return (c == kCfgG256 || c == kCfgW160)
+                     ? launch_ns_gemm32(mode, c, d_desc, ptab(tab), n, sp, buf, s)
+                     : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
+      }
     }
-    if (tot_sg > 0) {
-      e = run_stage(MUON_STAGE_GRAM, s, [&] { return launch_small_gram(d_desc, p_sg, n, tot_sg, buf, s); });
+    if (plan.tot[kTabSmallGram] > 0) {
+      e = run_stage(MUON_STAGE_GRAM, s, [&] {
+        return launch_small_gram(d_desc, ptab(kTabSmallGram), n, ttot(kTabSmallGram), buf, s);
+      });
       if (e != hipSuccess) return hip_fail(e, "small gram launch");
-      e = run_stage(MUON_STAGE_POLY, s, [&] { return launch_small_poly(d_desc, p_sp, n, tot_sp, s); });
+      e = run_stage(MUON_STAGE_POLY, s, [&] {
+        return launch_small_poly(d_desc, ptab(kTabSmallPoly), n, ttot(kTabSmallPoly), s);
+      });
       if (e != hipSuccess) return hip_fail(e, "small poly launch");
-      e = run_stage(MUON_STAGE_BX, s, [&] { return launch_small_bx(d_desc, p_sg, n, tot_sg, buf, s); });
+      e = run_stage(MUON_STAGE_BX, s, [&] {
+        return launch_small_bx(d_desc, ptab(kTabSmallGram), n, ttot(kTabSmallGram), buf, s);
+      });
       if (e != hipSuccess) return hip_fail(e, "small bx launch");
     }
     buf ^= 1;
   }
-  e = run_stage(MUON_STAGE_UPDATE, s, [&] {
-    return launch_update(d_desc, p_upd, n, tot_upd, buf, s);
-  });
+  e = run_stage(MUON_STAGE_UPDATE, s, [&] { return launch_update(d_desc, ptab(kTabUpd), n, ttot(kTabUpd), buf, s); });
   if (e != hipSuccess) return hip_fail(e, "update launch");
   return MUON_OK;
 }
@@ -567,18 +666,26 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
   muon_status_t st = items_from_step(mats, n, hp, false, items);
   if (st != MUON_OK) return st;
   memset(info, 0, sizeof(*info));
-  info->tile = kTile;
   if (n == 0) return MUON_OK;
   Plan plan;
   st = make_plan(items, hp->ns_steps, plan);
   if (st != MUON_OK) return st;
   info->workspace_bytes = static_cast<int64_t>(plan.total_bytes);
-  const int64_t groups = (plan.tot[2] > 0 ? 1 : 0) + (plan.tot[5] > 0 ? 1 : 0);
-  info->launches = 4 + 3 * groups * static_cast<int64_t>(hp->ns_steps);  // kernels; the table copy is extra
-  info->gram_tiles = plan.tot[2];
-  info->poly_tiles = plan.tot[2];
-  info->bx_tiles = plan.tot[3];
-  info->ew_blocks = plan.tot[0];
+  int64_t launches_per_iter = plan.tot[kTabSmallGram] > 0 ? 3 : 0;
+  for (int c = 0; c < kNumCfg; ++c) {
+    if (plan.tot[tab_sym(c)] > 0) {
+      launches_per_iter += 2;
+      info->gram_tiles += plan.tot[tab_sym(c)];
+      if (info->tile == 0) info->tile = kCfgRows[c];
+    }
+    if (plan.tot[tab_bx(c)] > 0) {
+      launches_per_iter += 1;
+      info->bx_tiles += plan.tot[tab_bx(c)];
+    }
+  }
+  info->poly_tiles = info->gram_tiles;
+  info->launches = 4 + launches_per_iter * static_cast<int64_t>(hp->ns_steps);  // kernels; the table copy is extra
+  info->ew_blocks = plan.tot[kTabMom];
   if (per_matrix) {
     for (int64_t i = 0; i < n; ++i) {
       const MatDesc& d = plan.descs[i];
@@ -588,7 +695,8 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
       p.n = d.n;
       p.m_pad = d.m_pad;
       p.n_pad = d.n_pad;
-      p.fp32_path = (d.flags & kSmall) ? 1 : 0;
+      p.tile = (d.flags & kSmall) ? 0 : kCfgRows[d.sym_cfg];
+      p.bx_tile_cols = (d.flags & kSmall) ? 0 : kCfgCols[d.bx_cfg];
       p.x_offset = plan.x_offset[i];
     }
   }

@@ -6,9 +6,16 @@
 
 namespace muon {
 
-// Output tile edge of the matrix-core kernels; every iterate / Gram buffer is
-// zero padded to a multiple of it, so the GEMM kernels never bounds-check.
-constexpr int kTile = 128;
+// Matrix-core kernel configurations (tile rows x tile columns, MFMA shape):
+//   G256: 256 x 256, 32x32x16   (Gram, polynomial, BX)
+//   W160: 160 x 256, 32x32x16   (BX only; Gram side a multiple of 160)
+//   T160: 160 x 160, 16x16x32   (Gram, polynomial, BX)
+//   T128: 128 x 128, 16x16x32   (Gram, polynomial, BX)
+// Every iterate / Gram buffer is zero padded to multiples of its matrix's
+// tile edges, so the GEMM kernels never bounds-check.
+enum GemmCfg : int32_t { kCfgG256 = 0, kCfgW160 = 1, kCfgT160 = 2, kCfgT128 = 3, kNumCfg = 4 };
+constexpr int kCfgRows[kNumCfg] = {256, 160, 160, 128};   // tile rows (Gram side)
+constexpr int kCfgCols[kNumCfg] = {256, 256, 160, 128};   // tile columns (long side for BX)
 // Tile edge of the layout kernels (normalise/transpose, update).
 constexpr int kEwTile = 64;
 // Elements per work-group of the momentum/norm kernel.
@@ -33,10 +40,11 @@ struct MatDesc {
   float* W;          // update target (or O output in orthogonalise-only mode)
   const void* G;     // gradient (or M input in orthogonalise-only mode)
   float* B;          // momentum buffer (unused in orthogonalise-only mode)
-  __bf16* xhi[2];    // iterate high parts, m_pad x n_pad, ping-pong
-  __bf16* xlo[2];    // iterate residual parts
-  __bf16* gram;      // A, m_pad x m_pad
-  __bf16* poly;      // P, m_pad x m_pad
+  __bf16* x_hi;      // X high part, m_pad x n_pad (row-major, Gram operand)
+  __bf16* xt_hi[2];  // X^T high part, n_pad x m_pad, ping-pong
+  __bf16* xt_lo[2];  // X^T rounding residual, n_pad x m_pad, ping-pong
+  __bf16* gram;      // A, m_pad x m_pad (both triangles)
+  __bf16* poly;      // P, m_pad x m_pad (both triangles)
   float* xf[2];      // float32 iterate (small path), kSmallGram x n_pad
   float* sgram;      // small path: per-chunk partial Gram matrices
   float* spoly;      // small path: P, kSmallGram x kSmallGram float32
@@ -48,6 +56,19 @@ struct MatDesc {
   int32_t mom_blocks;  // work-groups of the momentum kernel for this matrix
   float lr_scale;      // lr * scale, formed in float32 on the host
   int32_t s_chunks;    // small path: column chunks (n_pad / kSmallChunk)
+  int32_t sym_cfg;     // kernel configuration of the Gram / polynomial stages
+  int32_t bx_cfg;      // kernel configuration of the BX stage
+  int32_t k_gram;      // reduction length of the Gram product: n rounded up to 32
+};
+
+// Split of one grouped GEMM launch over the 8 XCDs: work-groups are dealt
+// to XCDs round-robin (block id % 8), and XCD x runs the contiguous work
+// range [start[x], start[x+1]), chosen on the host so every XCD gets the
+// same estimated cost (tiles differ in reduction length).  Blocks beyond
+// their XCD's range exit at once; the grid is 8 * max range length.
+struct XcdSplit {
+  int32_t start[9];
+  int32_t max_len;
 };
 
 // Host-side launchers (defined in the kernel translation units).  `prefix`
@@ -61,12 +82,13 @@ hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int t
                        hipStream_t s);
 hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
                          hipStream_t s);
-hipError_t launch_gram(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
-                       hipStream_t s);
-hipError_t launch_poly(const MatDesc* d, const int32_t* prefix, int nmats, int total,
-                       hipStream_t s);
-hipError_t launch_bx(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
-                     hipStream_t s);
+// Matrix-core GEMM stage (mode 0 = Gram, 1 = polynomial, 2 = BX) for the
+// matrices whose configuration for that stage is `cfg` (16x16 kernels:
+// T160, T128; 32x32 kernels: G256, W160).
+hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
+                          const XcdSplit& split, int buf, hipStream_t s);
+hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
+                            const XcdSplit& split, int buf, hipStream_t s);
 hipError_t launch_small_gram(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
                              hipStream_t s);
 hipError_t launch_small_poly(const MatDesc* d, const int32_t* prefix, int nmats, int total,

@@ -145,20 +145,24 @@ def test_orthogonalize_errors():
 
 # ------------------------------------------------------------------ plan
 def test_plan_transpose_rule_and_padding():
-    info, mats = mm.muon_plan_query([(1600, 1600), (1600, 6400), (6400, 1600), (33, 17), (17, 33), (1, 1)])
-    t = info["tile"]
-    assert [m["transposed"] for m in mats] == [0, 0, 1, 1, 0, 0]
-    for m, (r, c) in zip(mats, [(1600, 1600), (1600, 6400), (6400, 1600), (33, 17), (17, 33), (1, 1)]):
+    shapes = [(1600, 1600), (1600, 6400), (6400, 1600), (33, 17), (17, 33), (1, 1), (2048, 7168),
+              (768, 3072), (100, 300)]
+    info, mats = mm.muon_plan_query(shapes)
+    assert [m["transposed"] for m in mats] == [0, 0, 1, 1, 0, 0, 0, 0, 0]
+    for m, (r, c) in zip(mats, shapes):
         assert m["m"] == min(r, c) and m["n"] == max(r, c)
         assert m["x_offset"] % 256 == 0
         if m["m"] <= 64:
             # float32 small-Gram path: 64 x (n rounded up to 256)
-            assert m["fp32_path"] == 1 and m["m_pad"] == 64
+            assert m["tile"] == 0 and m["fp32_path"] == 1 and m["m_pad"] == 64
             assert m["n_pad"] % 256 == 0 and m["n"] <= m["n_pad"] < m["n"] + 256
         else:
-            assert m["fp32_path"] == 0
+            t, tc = m["tile"], m["bx_tile_cols"]
+            assert t in (128, 160, 256) and tc in (128, 160, 256) and m["fp32_path"] == 0
             assert m["m_pad"] % t == 0 and m["m"] <= m["m_pad"] < m["m"] + t
-            assert m["n_pad"] % t == 0 and m["n"] <= m["n_pad"] < m["n"] + t
+            assert m["n_pad"] % tc == 0 and m["n"] <= m["n_pad"] < m["n"] + tc
+    # Tile choice: exact fits are preferred (1600 = 10 x 160, 2048 = 8 x 256).
+    assert [m["tile"] for m in mats] == [160, 160, 160, 0, 0, 0, 256, 256, 128]
 
 
 def test_plan_small_path_threshold():
@@ -174,17 +178,23 @@ def test_plan_small_path_threshold():
 def test_plan_tile_counts_and_workspace():
     shapes = [(1600, 1600)] * 4 + [(1600, 6400), (6400, 1600)]
     info, mats = mm.muon_plan_query(shapes, ns_steps=5)
-    t = info["tile"]
-    sym = sum((m["m_pad"] // t) * (m["m_pad"] // t + 1) // 2 for m in mats)
-    bx = sum((m["m_pad"] // t) * (m["n_pad"] // t) for m in mats)
+    sym = sum((m["m_pad"] // m["tile"]) * (m["m_pad"] // m["tile"] + 1) // 2 for m in mats)
+    bx = sum((m["m_pad"] // m["tile"]) * (m["n_pad"] // m["bx_tile_cols"]) for m in mats)
     assert info["gram_tiles"] == sym == info["poly_tiles"]
     assert info["bx_tiles"] == bx
     assert info["launches"] == 4 + 3 * 5
-    floor = sum(4 * 2 * m["m_pad"] * m["n_pad"] + 2 * 2 * m["m_pad"] ** 2 for m in mats)
+    # five bf16 copies of the iterate (x_hi, two hi/lo pairs of X^T) + A + P
+    floor = sum(5 * 2 * m["m_pad"] * m["n_pad"] + 2 * 2 * m["m_pad"] ** 2 for m in mats)
     assert floor <= info["workspace_bytes"] <= floor + (1 << 20)
     info0, _ = mm.muon_plan_query(shapes, ns_steps=0)
     assert info0["workspace_bytes"] < info["workspace_bytes"]
     assert info0["launches"] == 4
+
+
+def test_plan_mixed_tiles_launch_groups():
+    info, mats = mm.muon_plan_query([(1600, 1600), (2048, 2048), (100, 300)], ns_steps=5)
+    assert sorted(m["tile"] for m in mats) == [128, 160, 256]
+    assert info["launches"] == 4 + 3 * 3 * 5
 
 
 def test_plan_limits():
