@@ -49,7 +49,7 @@ def ns_flops(shapes, kind):
     return tot
 
 
-def source_hash(*names):
+def source_hash(names):
     h = hashlib.sha256()
     for nm in names:
         with open(os.path.join(ROOT, "matrix_muon_step_amd", "csrc", nm), "rb") as f:
@@ -57,7 +57,7 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_file, workload):
+def load_traffic(kernel_files, workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
@@ -65,7 +65,7 @@ def load_traffic(kernel_file, workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash(kernel_file):
+    if rec.get("source_hash") != source_hash(kernel_files):
         return None
     return rec.get("bytes_per_launch")
 
@@ -146,7 +146,7 @@ def main():
         src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads nb bytes, writes nb bytes
+        torch.sqrt(src, out=dst)  # one elementwise kernel: reads nb bytes, writes nb bytes
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {nb} bytes read, {nb} bytes written")
         del src, dst
@@ -183,16 +183,24 @@ def main():
     stage_ms = {k: v[0] / args.steps for k, v in prof.items()}
     launches = {k: v[1] / args.steps for k, v in prof.items()}
     fl = {k: ns_flops(big, k) * args.ns_steps for k in ("gram", "poly", "bx")}
-    ns_ms = stage_ms["gram"] + stage_ms["poly"] + stage_ms["bx"]
+    ns_ms = stage_ms["gram"] + stage_ms["poly"] + stage_ms["bx"] + stage_ms["bx_update"]
     ns_alg = fl["gram"] + fl["poly"] + fl["bx"]
     ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
     dense_eq = sum(4.0 * min(s) ** 2 * max(s) + 2.0 * min(s) ** 3 for s in big) * args.ns_steps
-    # dominant kernel: the BX + aX GEMM
+    # Dominant kernel: the BX + aX product of the first ns_steps - 1
+    # iterations (the last one also applies the update and is timed apart).
+    # One launch per iteration covers every matrix when they share a tile
+    # configuration (all workloads here do); the figure is per iteration.
+    bx_iters = (args.ns_steps - 1) * args.steps
     bx_launches = prof["bx"][1]
-    bx_avg_ms = prof["bx"][0] / bx_launches if bx_launches else None
+    bx_avg_ms = prof["bx"][0] / bx_iters if bx_iters and bx_launches else None
     bx_flops_per_launch = ns_flops(big, "bx")
     bx_tflops = bx_flops_per_launch / (bx_avg_ms * 1e-3) / 1e12 if bx_avg_ms else None
-    traffic = load_traffic("gemm_kernels.hip", w.name)
+    bx_cfgs = sorted({(p["tile"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
+    bx_kernel = {(160, 256): "W160", (256, 256): "G256"}
+    kname = "+".join(f"ns_gemm32_kernel<{bx_kernel[c]}, BX>" if c in bx_kernel else f"ns_gemm_kernel<T{c[0]}, BX>"
+                     for c in bx_cfgs)
+    traffic = load_traffic(("gemm32_kernels.hip", "muon_internal.h"), w.name)
     n_el = w.n_params
     g_bytes = 2 if w.g_dtype == "bf16" else 4
     mom_bytes = n_el * (g_bytes + 8)          # read G, B; write B
@@ -219,7 +227,7 @@ def main():
                    "shapes": sorted({f"{r}x{c}" for r, c in shapes}), "ns_steps": args.ns_steps,
                    "mu": w.mu, "lr": w.lr, "g_dtype": w.g_dtype},
         "roofline": {
-            "kernel": "ns_gemm_kernel<BX> (X' = aX + P X)",
+            "kernel": f"{kname} (X' = a X + P X)",
             "bound": "mfma",
             "achieved": round(bx_tflops, 2) if bx_tflops else None,
             "peak": PEAK_BF16_TFLOPS,
@@ -227,6 +235,7 @@ def main():
             "frac": round(bx_tflops / PEAK_BF16_TFLOPS, 4) if bx_tflops else None,
             "traffic": traffic,
             "avg_launch_ms": round(bx_avg_ms, 4) if bx_avg_ms else None,
+            "launches_per_step": bx_launches / args.steps,
             "alg_flops_per_launch": bx_flops_per_launch,
         },
         "ns5": {

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -153,7 +153,9 @@ typedef struct muon_matrix_plan {
   int32_t n_pad;        /* padded long side of the iterate buffers (zeros)        */
   int32_t tile;         /* tile edge of the symmetric products; 0 = float32 path  */
   int32_t bx_tile_cols; /* long-side tile width of the BX product (0 on float32)  */
-  int32_t reserved;
+  int32_t fused_update; /* 1: the last BX launch writes W (or O) itself, from the  */
+                        /* float32 accumulator; 0: a separate update pass reads   */
+                        /* the final iterate pair (hi + lo)                       */
   int64_t x_offset;     /* byte offset of the iterate buffers in the workspace    */
 } muon_matrix_plan_t;
 
@@ -174,7 +176,9 @@ typedef enum muon_stage {
   MUON_STAGE_BX = 5,       /* X = a X + P X                            */
   MUON_STAGE_UPDATE = 6,   /* W -= lr * scale * O (or O store)         */
   MUON_STAGE_UPLOAD = 7,   /* descriptor table copy                    */
-  MUON_STAGE_COUNT = 8
+  MUON_STAGE_BX_UPDATE = 8, /* last X = a X + P X with W -= lr*scale*O  */
+                            /* applied in the same launch (wide tiles)  */
+  MUON_STAGE_COUNT = 9
 } muon_stage_t;
 
 muon_status_t muon_profile_enable(int32_t on);

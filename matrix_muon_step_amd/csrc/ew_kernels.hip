@@ -56,26 +56,26 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
     const int cnt = (end - e >= 4) ? 4 : static_cast<int>(end - e);
     if (cnt == 4) {
       if (gbf) {
-        const uint2 gv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.G) + e);
+        const uint2 gv = gld<uint2>(static_cast<const uint16_t*>(d.G) + e);
         g[0] = __uint_as_float(gv.x << 16);
         g[1] = __uint_as_float(gv.x & 0xffff0000u);
         g[2] = __uint_as_float(gv.y << 16);
         g[3] = __uint_as_float(gv.y & 0xffff0000u);
       } else {
-        const float4 gv = *reinterpret_cast<const float4*>(static_cast<const float*>(d.G) + e);
+        const float4 gv = gld<float4>(static_cast<const float*>(d.G) + e);
         g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
       }
       if (!ortho) {
-        const float4 bv = *reinterpret_cast<const float4*>(B + e);
+        const float4 bv = gld<float4>(B + e);
         b[0] = bv.x; b[1] = bv.y; b[2] = bv.z; b[3] = bv.w;
       }
     } else {
       for (int k = 0; k < 4; ++k) {
         g[k] = 0.f; b[k] = 0.f;
         if (k < cnt) {
-          g[k] = gbf ? bf16_bits_to_float(static_cast<const uint16_t*>(d.G)[e + k])
-                     : static_cast<const float*>(d.G)[e + k];
-          if (!ortho) b[k] = B[e + k];
+          g[k] = gbf ? bf16_bits_to_float(gld<uint16_t>(static_cast<const uint16_t*>(d.G) + e + k))
+                     : gld<float>(static_cast<const float*>(d.G) + e + k);
+          if (!ortho) b[k] = gld<float>(B + e + k);
         }
       }
     }
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
     }
     if (!ortho) {
       if (cnt == 4) {
-        *reinterpret_cast<float4*>(B + e) = make_float4(b[0], b[1], b[2], b[3]);
+        gst(B + e, make_float4(b[0], b[1], b[2], b[3]));
       } else {
-        for (int k = 0; k < cnt; ++k) B[e + k] = b[k];
+        for (int k = 0; k < cnt; ++k) gst(B + e + k, b[k]);
       }
     }
 #pragma unroll
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) d.partials[local] = ((red[0] + red[1]) + red[2]) + red[3];
+  if (threadIdx.x == 0) gst(d.partials + local, ((red[0] + red[1]) + red[2]) + red[3]);
 }
 
 // ---------------------------------------------------------------- norm
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
   const MatDesc& d = descs[blockIdx.x];
   const int nb = d.mom_blocks;
   double s = 0.0;
-  for (int i = threadIdx.x; i < nb; i += 256) s += static_cast<double>(d.partials[i]);
+  for (int i = threadIdx.x; i < nb; i += 256) s += static_cast<double>(gld<float>(d.partials + i));
   __shared__ double red[256];
   red[threadIdx.x] = s;
   __syncthreads();
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
   }
   if (threadIdx.x == 0) {
     const double nrm = sqrt(red[0]);
-    d.sigma[0] = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
+    gst(d.sigma, static_cast<float>(1.0 / (nrm + static_cast<double>(eps))));
   }
 }
 
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
   // Region of M (original orientation) that feeds this X tile.
   const int64_t r0 = tr ? j0 : i0;
   const int64_t c0 = tr ? i0 : j0;
-  const float sigma = d.sigma[0];
+  const float sigma = gld<float>(d.sigma);
   __shared__ float tile[kEwTile][kEwTile + 1];
   const int tx = threadIdx.x & 15;   // column group of 4
   const int ty = threadIdx.x >> 4;   // 0..15
@@ -171,12 +171,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
           const int64_t e = r * cols + c;
           float mval;
           if (ortho) {
-            mval = static_cast<const float*>(d.G)[e];
+            mval = gld<float>(static_cast<const float*>(d.G) + e);
           } else {
-            const float bval = d.B[e];
+            const float bval = gld<float>(d.B + e);
             if (nest) {
-              const float g = gbf ? bf16_bits_to_float(static_cast<const uint16_t*>(d.G)[e])
-                                  : static_cast<const float*>(d.G)[e];
+              const float g = gbf ? bf16_bits_to_float(gld<uint16_t>(static_cast<const uint16_t*>(d.G) + e))
+                                  : gld<float>(static_cast<const float*>(d.G) + e);
               mval = fmaf(mu, bval, g);
             } else {
               mval = bval;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
         v[c4] = sigma * (tr ? tile[jl][il] : tile[il][jl]);
       }
       const int64_t off = static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4;
-      *reinterpret_cast<float4*>(d.xf[0] + off) = make_float4(v[0], v[1], v[2], v[3]);
+      gst(d.xf[0] + off, make_float4(v[0], v[1], v[2], v[3]));
     }
     return;
   }
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
       }
       uint2 hv;
       __builtin_memcpy(&hv, h, 8);
-      *reinterpret_cast<uint2*>(d.x_hi + static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4) = hv;
+      gst(d.x_hi + static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4, hv);
     }
   }
   // X^T as the bf16 pair: row j of X^T holds column j of X.
@@ -241,8 +241,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
     uint2 hv, lv;
     __builtin_memcpy(&hv, h, 8);
     __builtin_memcpy(&lv, l, 8);
-    *reinterpret_cast<uint2*>(d.xt_hi[0] + off) = hv;
-    *reinterpret_cast<uint2*>(d.xt_lo[0] + off) = lv;
+    gst(d.xt_hi[0] + off, hv);
+    gst(d.xt_lo[0] + off, lv);
   }
 }
 
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
     if (s0 + sl >= src_rows || s1 + tx * 4 >= src_cols) continue;
     if (small) {
       const int64_t off = (s0 + sl) * d.n_pad + s1 + tx * 4;
-      const float4 v = *reinterpret_cast<const float4*>(d.xf[buf] + off);
+      const float4 v = gld<float4>(d.xf[buf] + off);
       tile[sl][tx * 4 + 0] = v.x;
       tile[sl][tx * 4 + 1] = v.y;
       tile[sl][tx * 4 + 2] = v.z;
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
       continue;
     }
     const int64_t off = (s0 + sl) * d.m_pad + s1 + tx * 4;
-    const uint2 hv = *reinterpret_cast<const uint2*>(d.xt_hi[buf] + off);
-    const uint2 lv = *reinterpret_cast<const uint2*>(d.xt_lo[buf] + off);
+    const uint2 hv = gld<uint2>(d.xt_hi[buf] + off);
+    const uint2 lv = gld<uint2>(d.xt_lo[buf] + off);
     tile[sl][tx * 4 + 0] = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
     tile[sl][tx * 4 + 1] = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
     tile[sl][tx * 4 + 2] = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
@@ -311,8 +311,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
       if (c >= cols) continue;
       const float o = direct ? tile[rl][cl] : tile[cl][rl];
       const int64_t e = r * cols + c;
-      if (ortho) W[e] = o;
-      else W[e] = fmaf(-ls, o, W[e]);
+      gst(W + e, ortho ? o : fmaf(-ls, o, gld<float>(W + e)));
     }
   }
 }

@@ -33,7 +33,12 @@
 // Epilogue: a 32x32 accumulator holds, per lane, column (lane & 31) and
 // rows 8g + 4 (lane >> 5) + r (g, r = 0..3): four runs of four consecutive
 // rows, stored transposed straight from registers as 8-byte writes; the
-// row-major copy goes through a private 32-row LDS slice per wave.
+// row-major copy goes through a private 32-row LDS slice per wave.  The
+// last BX of a step (mode BXL) applies the parameter update of the
+// synthesis note's section 4, W <- W - lr * scale * O, directly: O^T rows
+// are W rows for a transposed matrix (16-byte stores from registers), and
+// otherwise the float32 values pass through the slice.  The iterate itself
+// is not stored on the last iteration.
 #include "muon_internal.h"
 
 namespace muon {
@@ -51,7 +56,10 @@ constexpr float kCoefA = 3.4445f;
 constexpr float kCoefB = -4.7750f;
 constexpr float kCoefC = 2.0315f;
 
-enum Mode { GRAM = 0, POLY = 1, BXM = 2 };
+// BXL: the last BX of a step; instead of storing the iterate it applies the
+// parameter update W -= lr * scale * O (or stores O in orthogonalise-only
+// mode) straight from the epilogue.
+enum Mode { GRAM = 0, POLY = 1, BXM = 2, BXL = 3 };
 
 template <int BM_, int BN_, int NWM_, int NWN_>
 struct G32 {
@@ -66,8 +74,9 @@ struct G32 {
   static constexpr int OPA = BM * 64, OPB = BN * 64;      // bytes per stage
   static constexpr int STAGEB = OPA + OPB;
   static constexpr int NSTAGE = 3;
-  static constexpr int SLICE_LD = WN + 8;                 // epilogue slice row stride (elements)
-  static constexpr int SLICEB = 32 * SLICE_LD * 2;        // bytes per wave
+  static constexpr int SLICE_LD = WN + 8;                 // epilogue slice row stride (bf16 elements)
+  static constexpr int SLICEF_LD = WN + 4;                // same, float32 slice of the fused update
+  static constexpr int SLICEB = 32 * SLICEF_LD * 4;       // bytes per wave (covers both uses)
   static constexpr int LDSB = (NSTAGE * STAGEB > SLICEB * NW) ? NSTAGE * STAGEB : SLICEB * NW;
   static constexpr int MINB = (NW == 4) ? 2 : 1;          // two waves per SIMD
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int m_pad = d.m_pad, n_pad = d.n_pad;
 
   int ti, tj;
-  if (MODE == BXM) {
+  if (MODE >= BXM) {
     const int tpc = m_pad / C::BM;   // Gram-side index fastest: running tiles share X^T panels
     tj = local / tpc;
     ti = local - tj * tpc;
@@ -261,36 +270,47 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   __syncthreads();
 
   // ---- epilogue (wave-local).
-  const bool diag = (MODE != BXM) && (ti == tj);
+  const bool diag = (MODE == GRAM || MODE == POLY) && (ti == tj);
   const int wi0 = ti * C::BM + wr * C::WM;   // first global row of the wave's sub-tile
   const int wj0 = tj * C::BN + wc * C::WN;   // first global column
   __bf16* slice = reinterpret_cast<__bf16*>(smem) + wave * (C::SLICEB / 2);
+  float* slicef = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
   __bf16* rdst;
   int64_t rld;
-  if (MODE == BXM) { rdst = d.x_hi; rld = n_pad; }
+  if (MODE >= BXM) { rdst = d.x_hi; rld = n_pad; }
   else { rdst = (MODE == POLY) ? d.poly : d.gram; rld = m_pad; }
   const int col = lane & 31;
   const int rq = 4 * (lane >> 5);
+  const bool tr = d.flags & kTransposed;
+  const bool ortho = d.flags & kOrthoOnly;
+  const float ls = d.lr_scale;
+  // W is 16-byte aligned (checked at the API); rows are when cols % 4 == 0.
+  const bool w16 = (d.cols & 3) == 0;
+
+  // Epilogue inputs of one block row (X^T pair, or A), double buffered so
+  // the reads of row i+1 are in flight while row i is finished.
+  uint2 in_a[2][C::BNB][4], in_b[2][C::BNB][4];
+  auto load_row = [&](int i, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int gi = wi0 + i * 32 + 8 * g + rq;
+        const int gj = wj0 + j * 32 + col;
+        const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+        if (MODE >= BXM) {
+          in_a[slot][j][g] = gld<uint2>(d.xt_hi[buf] + off);
+          in_b[slot][j][g] = gld<uint2>(d.xt_lo[buf] + off);
+        } else if (MODE == POLY) {
+          in_a[slot][j][g] = gld<uint2>(d.gram + off);  // A symmetric
+        }
+      }
+  };
+  if (MODE != GRAM) load_row(0, 0);
 #pragma unroll
   for (int i = 0; i < C::BMB; ++i) {
-    // Global reads of this block row first (independent, mostly from HBM).
-    uint2 in_a[C::BNB][4], in_b[C::BNB][4];
-    if (MODE != GRAM) {
-#pragma unroll
-      for (int j = 0; j < C::BNB; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int gi = wi0 + i * 32 + 8 * g + rq;
-          const int gj = wj0 + j * 32 + col;
-          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-          if (MODE == BXM) {
-            in_a[j][g] = *reinterpret_cast<const uint2*>(d.xt_hi[buf] + off);
-            in_b[j][g] = *reinterpret_cast<const uint2*>(d.xt_lo[buf] + off);
-          } else {
-            in_a[j][g] = *reinterpret_cast<const uint2*>(d.gram + off);  // A symmetric
-          }
-        }
-    }
+    const int slot = i & 1;
+    if (MODE != GRAM && i + 1 < C::BMB) load_row(i + 1, slot ^ 1);
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j) {
 #pragma unroll
@@ -300,23 +320,51 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
-        uint32_t w0, w1;
-        if (MODE == BXM) {
-          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-          const uint2 hx = in_a[j][g], lx = in_b[j][g];
+        uint32_t w0 = 0, w1 = 0;
+        if (MODE >= BXM) {
+          const uint2 hx = in_a[slot][j][g], lx = in_b[slot][j][g];
           v[0] = fmaf(kCoefA, bf_lo(hx.x) + bf_lo(lx.x), v[0]);
           v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), v[1]);
           v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), v[2]);
           v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), v[3]);
+        }
+        if (MODE == BXM) {
+          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
           w0 = pack_bf16(v[0], v[1]);
           w1 = pack_bf16(v[2], v[3]);
           const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
           const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
-          *reinterpret_cast<uint2*>(d.xt_hi[buf ^ 1] + off) = make_uint2(w0, w1);
-          *reinterpret_cast<uint2*>(d.xt_lo[buf ^ 1] + off) = make_uint2(l0, l1);
+          gst(d.xt_hi[buf ^ 1] + off, make_uint2(w0, w1));
+          gst(d.xt_lo[buf ^ 1] + off, make_uint2(l0, l1));
+        } else if (MODE == BXL) {
+          // O = X' (fp32).  Transposed matrix: O^T = X'^T is W's orientation,
+          // so rows gj of W take four consecutive columns gi..gi+3.
+          if (tr) {
+            if (gj < d.n) {
+              float* wp = d.W + static_cast<int64_t>(gj) * d.cols + gi;
+              if (gi + 3 < d.m && w16) {
+                float4 o = make_float4(v[0], v[1], v[2], v[3]);
+                if (!ortho) {
+                  const float4 w = gld<float4>(wp);
+                  o = make_float4(fmaf(-ls, v[0], w.x), fmaf(-ls, v[1], w.y), fmaf(-ls, v[2], w.z), fmaf(-ls, v[3], w.w));
+                }
+                gst(wp, o);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (gi + r < d.m) gst(wp + r, ortho ? v[r] : fmaf(-ls, v[r], gld<float>(wp + r)));
+              }
+            }
+          } else {
+            const int rl = 8 * g + rq;
+            const int cl = j * 32 + col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) slicef[(rl + r) * C::SLICEF_LD + cl] = v[r];
+          }
+          continue;
         } else {
           if (MODE == POLY) {
-            const uint2 a = in_a[j][g];
+            const uint2 a = in_a[slot][j][g];
             v[0] = fmaf(kCoefC, v[0], kCoefB * bf_lo(a.x));
             v[1] = fmaf(kCoefC, v[1], kCoefB * bf_hi(a.x));
             v[2] = fmaf(kCoefC, v[2], kCoefB * bf_lo(a.y));
@@ -326,15 +374,12 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
           w1 = pack_bf16(v[2], v[3]);
           __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;  // mirror position
           if (!diag || gi + 3 <= gj) {
-            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+            gst(p, make_uint2(w0, w1));
           } else {
             const uint32_t wv[2] = {w0, w1};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              if (gi + r <= gj) {
-                const uint16_t bits = static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16));
-                __builtin_memcpy(p + r, &bits, 2);
-              }
+              if (gi + r <= gj) gst(p + r, static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16)));
             }
           }
         }
@@ -346,6 +391,36 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::SLICE_LD + cl, &hb[r], 2);
       }
+    }
+    if (MODE == BXL) {
+      // Non-transposed matrix: W[gi][gj..gj+3] from the float32 slice.
+      if (!tr) {
+        constexpr int CPR = C::WN / 4;
+#pragma unroll
+        for (int c = lane; c < 32 * CPR; c += 64) {
+          const int rl = c / CPR;
+          const int cc = c - rl * CPR;
+          const int gi = wi0 + i * 32 + rl;
+          const int gj = wj0 + cc * 4;
+          if (gi >= d.m || gj >= d.n) continue;
+          const float4 o = *reinterpret_cast<const float4*>(slicef + rl * C::SLICEF_LD + cc * 4);
+          float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
+          if (gj + 3 < d.n && w16) {
+            if (ortho) {
+              gst(wp, o);
+            } else {
+              const float4 w = gld<float4>(wp);
+              gst(wp, make_float4(fmaf(-ls, o.x, w.x), fmaf(-ls, o.y, w.y), fmaf(-ls, o.z, w.z), fmaf(-ls, o.w, w.w)));
+            }
+          } else {
+            const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gj + e < d.n) gst(wp + e, ortho ? ov[e] : fmaf(-ls, ov[e], gld<float>(wp + e)));
+          }
+        }
+      }
+      continue;
     }
     // Slice (32 rows x WN) -> global rows, 16 bytes at a time.  The wave's
     // own LDS writes are ordered before its reads by the compiler.
@@ -359,13 +434,13 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       const uint4 val = *reinterpret_cast<const uint4*>(slice + rl * C::SLICE_LD + cc * 8);
       __bf16* p = rdst + static_cast<int64_t>(gi) * rld + gj;
       if (!diag || gi <= gj) {
-        *reinterpret_cast<uint4*>(p) = val;
+        gst(p, val);
       } else if (gi < gj + 8) {
         uint16_t hv[8];
         __builtin_memcpy(hv, &val, 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gi <= gj + e) __builtin_memcpy(p + e, &hv[e], 2);
+          if (gi <= gj + e) gst(p + e, hv[e]);
       }
     }
   }
@@ -388,9 +463,11 @@ hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* 
   if (cfg == kCfgG256) {
     if (mode == GRAM) return launch<G256, GRAM>(d, prefix, nmats, split, buf, s);
     if (mode == POLY) return launch<G256, POLY>(d, prefix, nmats, split, buf, s);
-    return launch<G256, BXM>(d, prefix, nmats, split, buf, s);
+    if (mode == BXM) return launch<G256, BXM>(d, prefix, nmats, split, buf, s);
+    return launch<G256, BXL>(d, prefix, nmats, split, buf, s);
   }
   if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgW160 && mode == BXL) return launch<W160, BXL>(d, prefix, nmats, split, buf, s);
   return hipErrorInvalidValue;
 }
 

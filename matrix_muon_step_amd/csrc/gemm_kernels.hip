@@ -356,10 +356,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
           const int gj = wj0 + j * 16 + l16;
           const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
           if (MODE == BXM) {
-            in_a[ib - b0][j] = *reinterpret_cast<const uint2*>(d.xt_hi[buf] + off);
-            in_b[ib - b0][j] = *reinterpret_cast<const uint2*>(d.xt_lo[buf] + off);
+            in_a[ib - b0][j] = gld<uint2>(d.xt_hi[buf] + off);
+            in_b[ib - b0][j] = gld<uint2>(d.xt_lo[buf] + off);
           } else {
-            in_a[ib - b0][j] = *reinterpret_cast<const uint2*>(d.gram + off);
+            in_a[ib - b0][j] = gld<uint2>(d.gram + off);
           }
         }
       }
@@ -385,8 +385,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
           w1 = pack_bf16(v[2], v[3]);
           const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
           const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
-          *reinterpret_cast<uint2*>(d.xt_hi[buf ^ 1] + off) = make_uint2(w0, w1);
-          *reinterpret_cast<uint2*>(d.xt_lo[buf ^ 1] + off) = make_uint2(l0, l1);
+          gst(d.xt_hi[buf ^ 1] + off, make_uint2(w0, w1));
+          gst(d.xt_lo[buf ^ 1] + off, make_uint2(l0, l1));
         } else {
           if (MODE == POLY) {
             // A is stored symmetric: A[gi..gi+3][gj] == A[gj][gi..gi+3].
@@ -402,14 +402,14 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
           w1 = pack_bf16(v[2], v[3]);
           __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;  // mirror position
           if (!diag || gi + 3 <= gj) {
-            *reinterpret_cast<uint2*>(p) = make_uint2(w0, w1);
+            gst(p, make_uint2(w0, w1));
           } else {
             const uint32_t wv[2] = {w0, w1};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               if (gi + r <= gj) {
                 const uint16_t bits = static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16));
-                __builtin_memcpy(p + r, &bits, 2);
+                gst(p + r, bits);
               }
             }
           }
@@ -435,13 +435,13 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
       const uint4 val = *reinterpret_cast<const uint4*>(slice + rl * C::EPI_LD + cc * 8);
       __bf16* p = rdst + static_cast<int64_t>(gi) * rld + gj;
       if (!diag || gi <= gj) {
-        *reinterpret_cast<uint4*>(p) = val;
+        gst(p, val);
       } else if (gi < gj + 8) {
         uint16_t hv[8];
         __builtin_memcpy(hv, &val, 16);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gi <= gj + e) __builtin_memcpy(p + e, &hv[e], 2);
+          if (gi <= gj + e) gst(p + e, hv[e]);
       }
     }
   }

@@ -182,7 +182,9 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.m_pad = static_cast<int32_t>(cfg.m_pad);
     d.n_pad = static_cast<int32_t>(cfg.n_pad);
     d.k_gram = static_cast<int32_t>(round_up(nn, 32));
-    d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0);
+    // The wide-tile BX kernels apply the update from their last launch.
+    const bool fused = !small && ns_steps > 0 && (cfg.bx == kCfgG256 || cfg.bx == kCfgW160);
+    d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0) | (fused ? kFusedUpd : 0);
     d.lr_scale = it.lr_scale;
     d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
     const int64_t elems = it.rows * it.cols;
@@ -192,7 +194,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     int64_t work[kNumTables] = {};
     work[kTabMom] = d.mom_blocks;
     work[kTabPrep] = ((d.m_pad + kEwTile - 1) / kEwTile) * ((d.n_pad + kEwTile - 1) / kEwTile);
-    work[kTabUpd] = ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
+    work[kTabUpd] = fused ? 0 : ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
     if (small) {
       work[kTabSmallGram] = d.s_chunks;
       work[kTabSmallPoly] = 1;
@@ -455,15 +457,17 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   int buf = 0;
   static const int stage_of_mode[3] = {MUON_STAGE_GRAM, MUON_STAGE_POLY, MUON_STAGE_BX};
   for (int it = 0; it < plan.ns_steps; ++it) {
+    const bool last = it + 1 == plan.ns_steps;
     for (int mode = 0; mode < 3; ++mode) {
       for (int c = 0; c < kNumCfg; ++c) {
         const int tab = mode == 2 ? tab_bx(c) : tab_sym(c);
         if (plan.tot[tab] == 0) continue;
         const XcdSplit sp = make_split(plan, tab, mode);
-        e = run_stage(stage_of_mode[mode], s, [&] {
-          return (c == kCfgG256 || c == kCfgW160)
-                     ? launch_ns_gemm32(mode, c, d_desc, ptab(tab), n, sp, buf, s)
-                     : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
+        const bool wide = c == kCfgG256 || c == kCfgW160;
+        const int kmode = (wide && last && mode == 2) ? 3 : mode;  // 3: BX with the update applied
+        e = run_stage(kmode == 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
+          return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, s)
+                      : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
         });
         if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
       }
@@ -484,8 +488,10 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
     }
     buf ^= 1;
   }
-  e = run_stage(MUON_STAGE_UPDATE, s, [&] { return launch_update(d_desc, ptab(kTabUpd), n, ttot(kTabUpd), buf, s); });
-  if (e != hipSuccess) return hip_fail(e, "update launch");
+  if (plan.tot[kTabUpd] > 0) {
+    e = run_stage(MUON_STAGE_UPDATE, s, [&] { return launch_update(d_desc, ptab(kTabUpd), n, ttot(kTabUpd), buf, s); });
+    if (e != hipSuccess) return hip_fail(e, "update launch");
+  }
   return MUON_OK;
 }
 
@@ -684,7 +690,8 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
     }
   }
   info->poly_tiles = info->gram_tiles;
-  info->launches = 4 + launches_per_iter * static_cast<int64_t>(hp->ns_steps);  // kernels; the table copy is extra
+  // momentum, norm, prep (+ update unless every matrix fuses it); the table copy is extra
+  info->launches = 3 + (plan.tot[kTabUpd] > 0 ? 1 : 0) + launches_per_iter * static_cast<int64_t>(hp->ns_steps);
   info->ew_blocks = plan.tot[kTabMom];
   if (per_matrix) {
     for (int64_t i = 0; i < n; ++i) {
@@ -697,6 +704,7 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
       p.n_pad = d.n_pad;
       p.tile = (d.flags & kSmall) ? 0 : kCfgRows[d.sym_cfg];
       p.bx_tile_cols = (d.flags & kSmall) ? 0 : kCfgCols[d.bx_cfg];
+      p.fused_update = (d.flags & kFusedUpd) ? 1 : 0;
       p.x_offset = plan.x_offset[i];
     }
   }

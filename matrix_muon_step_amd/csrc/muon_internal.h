@@ -6,6 +6,22 @@
 
 namespace muon {
 
+// Device memory accesses through the global address space.  The kernels
+// reach their buffers through generic pointers held in the descriptors;
+// copying through an address_space(1) pointer makes the compiler emit
+// global (not flat) loads and stores, which only the vector-memory counter
+// tracks, so waits on them do not also drain pending LDS traffic.
+template <class T>
+__device__ __forceinline__ T gld(const void* p) {
+  T v;
+  __builtin_memcpy(&v, (const __attribute__((address_space(1))) void*)p, sizeof(T));
+  return v;
+}
+template <class T>
+__device__ __forceinline__ void gst(void* p, T v) {
+  __builtin_memcpy((__attribute__((address_space(1))) void*)p, &v, sizeof(T));
+}
+
 // Matrix-core kernel configurations (tile rows x tile columns, MFMA shape):
 //   G256: 256 x 256, 32x32x16   (Gram, polynomial, BX)
 //   W160: 160 x 256, 32x32x16   (BX only; Gram side a multiple of 160)
@@ -33,6 +49,7 @@ enum GFlags : int32_t {
   kNesterov = 4,    // orthogonalise G + mu * B
   kOrthoOnly = 8,   // muon_orthogonalize: read M, write O, no momentum/update
   kSmall = 16,      // m <= kSmallGram: float32 iterate and Gram path
+  kFusedUpd = 32,   // the last BX launch applies the update (no update_kernel work)
 };
 
 // One matrix of a call, as the kernels see it (lives in the workspace).

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void small_gram_kernel(const MatDesc* __restri
   __shared__ __attribute__((aligned(16))) float xs[SC][XS];  // [k][i]
   const int t = threadIdx.x;
   // Load X[0:64][chunk] transposed into xs.
-  for (int i = 0; i < SM; ++i) xs[t][i] = X[static_cast<int64_t>(i) * n_pad + t];
+  for (int i = 0; i < SM; ++i) xs[t][i] = gld<float>(X + static_cast<int64_t>(i) * n_pad + t);
   __syncthreads();
   const int ib = (t >> 4) * 4;
   const int jb = (t & 15) * 4;
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void small_gram_kernel(const MatDesc* __restri
   float* __restrict__ out = d.sgram + static_cast<int64_t>(chunk) * SM * SM;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
-    *reinterpret_cast<float4*>(out + (ib + r) * SM + jb) =
-        make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+    gst(out + (ib + r) * SM + jb,
+        make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]));
 }
 
 // A = sum of the chunk partials (fixed order), P = b A + c A A.
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void small_poly_kernel(const MatDesc* __restri
   const int nc = d.s_chunks;
   for (int e = t; e < SM * SM; e += 256) {
     float s = 0.f;
-    for (int c = 0; c < nc; ++c) s += d.sgram[static_cast<int64_t>(c) * SM * SM + e];
+    for (int c = 0; c < nc; ++c) s += gld<float>(d.sgram + static_cast<int64_t>(c) * SM * SM + e);
     A[e / SM][e % SM] = s;
   }
   __syncthreads();
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void small_poly_kernel(const MatDesc* __restri
     const int i = e / SM, j = e % SM;
     float s = 0.f;
     for (int k = 0; k < SM; ++k) s = fmaf(A[i][k], A[k][j], s);
-    d.spoly[e] = fmaf(kCoefC, s, kCoefB * A[i][j]);
+    gst(d.spoly + e, fmaf(kCoefC, s, kCoefB * A[i][j]));
   }
 }
 
@@ -104,14 +104,14 @@ __global__ __launch_bounds__(256) void small_bx_kernel(const MatDesc* __restrict
   const int n_pad = d.n_pad;
   __shared__ __attribute__((aligned(16))) float P[SM * SM];
   const int t = threadIdx.x;
-  for (int e = t; e < SM * SM; e += 256) P[e] = d.spoly[e];
+  for (int e = t; e < SM * SM; e += 256) P[e] = gld<float>(d.spoly + e);
   __syncthreads();
   const int64_t col = static_cast<int64_t>(chunk) * SC + t;
   const float* __restrict__ X = d.xf[buf] + col;
   float* __restrict__ Y = d.xf[buf ^ 1] + col;
   float x[SM];
 #pragma unroll
-  for (int k = 0; k < SM; ++k) x[k] = X[static_cast<int64_t>(k) * n_pad];
+  for (int k = 0; k < SM; ++k) x[k] = gld<float>(X + static_cast<int64_t>(k) * n_pad);
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
     float s = 0.f;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void small_bx_kernel(const MatDesc* __restrict
       s = fmaf(p.z, x[k + 2], s);
       s = fmaf(p.w, x[k + 3], s);
     }
-    Y[static_cast<int64_t>(i) * n_pad] = fmaf(kCoefA, x[i], s);
+    gst(Y + static_cast<int64_t>(i) * n_pad, fmaf(kCoefA, x[i], s));
   }
 }
 

@@ -27,8 +27,16 @@ def test_header_symbols_exported():
         assert hasattr(L, name), name
 
 
+def test_stage_names_match_header():
+    src = open(os.path.join(ROOT, "include", "muon.h")).read()
+    enum = {name.lower(): int(v) for name, v in re.findall(r"MUON_STAGE_([A-Z_]+)\s*=\s*(\d+)", src)}
+    count = enum.pop("count")
+    assert count == len(bd.STAGES) == bd.MUON_STAGE_COUNT
+    assert all(bd.STAGES[v] == name for name, v in enum.items())
+
+
 def test_abi_version_and_strings():
-    assert mm.muon_abi_version() == 1
+    assert mm.muon_abi_version() == 2
     assert mm.muon_status_string(0) == "MUON_OK"
     assert mm.muon_status_string(-4) == "MUON_ERR_ALIAS"
 
@@ -170,9 +178,9 @@ def test_plan_small_path_threshold():
     assert [m["fp32_path"] for m in mats] == [1, 1, 0, 0]
     # Small matrices add no matrix-core tiles; mixing both paths adds launches.
     assert info["launches"] == 4 + 2 * 3 * 5
-    info_big, _ = mm.muon_plan_query([(65, 1000), (1000, 65)])
+    info_big, big = mm.muon_plan_query([(65, 1000), (1000, 65)])
     assert info_big["gram_tiles"] == info["gram_tiles"] and info_big["bx_tiles"] == info["bx_tiles"]
-    assert info_big["launches"] == 4 + 3 * 5
+    assert info_big["launches"] == 3 + _update_launch(big) + 3 * 5
 
 
 def test_plan_tile_counts_and_workspace():
@@ -182,7 +190,7 @@ def test_plan_tile_counts_and_workspace():
     bx = sum((m["m_pad"] // m["tile"]) * (m["n_pad"] // m["bx_tile_cols"]) for m in mats)
     assert info["gram_tiles"] == sym == info["poly_tiles"]
     assert info["bx_tiles"] == bx
-    assert info["launches"] == 4 + 3 * 5
+    assert info["launches"] == 3 + _update_launch(mats) + 3 * 5
     # five bf16 copies of the iterate (x_hi, two hi/lo pairs of X^T) + A + P
     floor = sum(5 * 2 * m["m_pad"] * m["n_pad"] + 2 * 2 * m["m_pad"] ** 2 for m in mats)
     assert floor <= info["workspace_bytes"] <= floor + (1 << 20)
@@ -194,7 +202,28 @@ def test_plan_tile_counts_and_workspace():
 def test_plan_mixed_tiles_launch_groups():
     info, mats = mm.muon_plan_query([(1600, 1600), (2048, 2048), (100, 300)], ns_steps=5)
     assert sorted(m["tile"] for m in mats) == [128, 160, 256]
-    assert info["launches"] == 4 + 3 * 3 * 5
+    assert info["launches"] == 3 + _update_launch(mats) + 3 * 3 * 5
+
+
+def _update_launch(mats):
+    """1 when some matrix still needs the separate update pass."""
+    return int(any(m["fused_update"] == 0 for m in mats))
+
+
+def test_plan_fused_update_flags():
+    """The wide-tile BX kernels (256 long-side columns) apply the update in
+    their last launch; the float32 path, the narrow tiles and ns_steps = 0
+    keep the separate update pass."""
+    shapes = [(2048, 7168), (7168, 2048), (1600, 1600), (100, 300), (33, 17)]
+    info, mats = mm.muon_plan_query(shapes, ns_steps=5)
+    for m in mats:
+        assert m["fused_update"] == int(m["bx_tile_cols"] == 256 and m["fp32_path"] == 0)
+    assert [m["fused_update"] for m in mats][:2] == [1, 1]
+    assert [m["fused_update"] for m in mats][3:] == [0, 0]
+    info_w, _ = mm.muon_plan_query(shapes[:2], ns_steps=5)
+    assert info_w["launches"] == 3 + 3 * 5
+    _, mats0 = mm.muon_plan_query(shapes, ns_steps=0)
+    assert all(m["fused_update"] == 0 for m in mats0)
 
 
 def test_plan_limits():

@@ -64,7 +64,8 @@ def test_partial_permutation_five_steps(mm):
     Ms = [synth.signed_partial_permutation(r, c, 4 ** j, [61, r, c]) for r, c, j in cases]
     Os = mm.muon_orthogonalize([dev(M) for M in Ms], ns_steps=5, eps=0.0)
     torch.cuda.synchronize()
-    for (r, c, j), M, O in zip(cases, Ms, Os):
+    _, plans = mm.muon_plan_query([(r, c) for r, c, _ in cases])
+    for (r, c, j), M, O, pl in zip(cases, Ms, Os, plans):
         On = O.cpu().numpy()
         ref = orc.newton_schulz(M.astype(np.float64), 5, eps=0.0)
         assert np.array_equal(np.sign(On), np.sign(ref))
@@ -72,19 +73,20 @@ def test_partial_permutation_five_steps(mm):
         assert np.all(mags.view(np.uint32) == mags.view(np.uint32)[0])
         expect = np.abs(ref[M != 0][0])
         assert abs(mags[0] - expect) <= 2e-2 * expect
-        assert mags[0] == scheme_scalar(2.0 ** -j, 5)
+        assert mags[0] == scheme_scalar(2.0 ** -j, 5, fused=bool(pl["fused_update"]))
 
 
 def _bf16(x):
     return np.float32(torch.tensor(float(x), dtype=torch.float32).to(torch.bfloat16).float().item())
 
 
-def scheme_scalar(x0, steps):
+def scheme_scalar(x0, steps, fused=False):
     """The iteration on one singular value in the library's stated precision
     scheme: iterate carried as a bf16 pair, A and P rounded to bf16, float32
     accumulation and epilogues (each a*b+c rounded once).  On an isolated
     singular value every product is exact, so the GPU must match this bit
-    for bit."""
+    for bit.  The result is the final pair's sum, or with the fused update
+    the last iteration's float32 value itself."""
     f = np.float32
     a, b, c = f(3.4445), f(-4.7750), f(2.0315)
     x = f(x0)
@@ -96,7 +98,7 @@ def scheme_scalar(x0, steps):
         xn = f(np.float64(a) * np.float64(f(xh + xl)) + np.float64(f(P * xh)))
         xh = _bf16(xn)
         xl = _bf16(f(xn - xh))
-    return f(xh + xl)
+    return xn if fused else f(xh + xl)
 
 
 def test_grouped_equals_one_by_one(mm):

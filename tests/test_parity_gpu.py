@@ -169,16 +169,50 @@ def test_single256_update_epilogue_fp32(mm):
     log_case("single256 update epilogue")
     w = synth.WORKLOADS["single256"]
     h = synth.numpy_matrix(w, 0, 0)
-    Wd, Gd, Bd = dev(h["W0"]), dev(h["G"]), dev(h["B0"])
-    mm.muon_step([(Wd, Gd, Bd, 0.75)], mu=w.mu, lr=w.lr, ns_steps=5)
+    _check_update_against_direction(mm, h["W0"], h["G"], w.mu, w.lr, 0.75)
+
+
+# Shapes of both update routes: the wide-tile BX kernels write W from their
+# last launch (fused), the others leave it to the separate update pass.  The
+# list covers both orientations, ragged Gram sides, and rows whose length is
+# not a multiple of 4 (element-wise W accesses).
+UPDATE_SHAPES = [(130, 1000), (1000, 132), (515, 1030), (1030, 515), (2048, 512),
+                 (128, 128), (300, 520), (520, 300), (33, 17)]
+
+
+@pytest.mark.parametrize("shape", UPDATE_SHAPES)
+def test_update_routes_fp32(mm, shape):
+    log_case(f"update route {shape}")
+    r, c = shape
+    rng = np.random.default_rng([71, r, c])
+    W0 = (0.02 * rng.standard_normal((r, c))).astype(np.float32)
+    G = synth.numpy_gradient(r, c, 8, 0.1, "f32", [71, r, c, 1])
+    _check_update_against_direction(mm, W0, G, 0.95, 0.02, 1.5)
+
+
+def _check_update_against_direction(mm, W0, G, mu, lr, scale, offset=4):
+    """W sits inside a larger buffer (16-byte aligned, as the ABI requires)
+    with guard bands on both sides that must stay untouched."""
+    r, c = W0.shape
+    store = torch.zeros(r * c + offset + 64, dtype=torch.float32, device="cuda")
+    Wd = store[offset:offset + r * c].view(r, c)
+    Wd.copy_(dev(W0))
+    Gd, Bd = dev(G), torch.zeros(r, c, dtype=torch.float32, device="cuda")
+    mm.muon_step([(Wd, Gd, Bd, scale)], mu=mu, lr=lr, ns_steps=5)
     O = mm.muon_orthogonalize([Bd.clone()], ns_steps=5)[0]
     torch.cuda.synchronize()
     O64 = O.cpu().numpy().astype(np.float64)
-    expect = h["W0"].astype(np.float64) - np.float64(np.float32(w.lr * 0.75)) * O64
-    step = expect - h["W0"]
+    expect = W0.astype(np.float64) - np.float64(np.float32(lr * scale)) * O64
+    step = expect - W0
     err = np.linalg.norm(Wd.cpu().numpy() - expect) / np.linalg.norm(step)
     assert err <= FP32_TOL, err
-    assert relfro(Bd.cpu().numpy(), h["G"]) == 0.0  # first step from B = 0: B = G exactly
+    assert relfro(Bd.cpu().numpy(), G) == 0.0  # first step from B = 0: B = G exactly
+    # nothing outside W was touched
+    assert torch.count_nonzero(store[:offset]).item() == 0
+    assert torch.count_nonzero(store[offset + r * c:]).item() == 0
+    # and the direction itself is the oracle's, to the Newton-Schulz bar
+    ref = orc.newton_schulz(G.astype(np.float64), 5)
+    assert relfro(O64, ref) <= NS_TOL
 
 
 def test_gpt2s_fc_ten_steps(mm):
