@@ -25,6 +25,8 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+# Sources of the kernel whose counters the traffic record holds.
+TRAFFIC_SOURCES = ("gemm32_kernels.hip", "muon_internal.h")
 METRIC = "Muon optimizer steps/sec on 1.5B-shaped hidden params; NS5 TFLOP/s % of bf16 peak"
 
 
@@ -67,7 +69,64 @@ def load_traffic(kernel_files, workload):
         rec = json.load(f)
     if rec.get("source_hash") != source_hash(kernel_files):
         return None
-    return rec.get("bytes_per_launch")
+    return round(rec.get("bytes_per_launch"))
+
+
+BX_KERNEL_RE = {
+    # (Gram-side tile rows, long-side tile columns) -> rocprofv3 kernel-name pattern of the BX launch
+    (160, 256): r"ns_gemm32_kernel<[^<]*G32<160, 256, 1, 4>, 2>",
+    (256, 256): r"ns_gemm32_kernel<[^<]*G32<256, 256, 2, 4>, 2>",
+}
+CALIB_RE = r"sqrt"
+
+
+def read_counter_csv(path, counter):
+    """{kernel name: [value per dispatch]} of one counter from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            per.setdefault(row["Kernel_Name"], {}).setdefault(row["Dispatch_Id"], 0.0)
+            per[row["Kernel_Name"]][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def record_traffic(workload, fetch_csv, write_csv, calib_bytes):
+    """HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for a plain elementwise kernel that reads and writes
+    calib_bytes.  Writes profiles/traffic_<workload>.json."""
+    import re
+    import statistics
+    import matrix_muon_step_amd as mm
+    w = synth.WORKLOADS[workload]
+    shapes = [(s.rows, s.cols) for s in w.matrices]
+    cfgs = sorted({(p["tile"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
+    assert len(cfgs) == 1 and cfgs[0] in BX_KERNEL_RE, cfgs
+    pat = re.compile(BX_KERNEL_RE[cfgs[0]])
+    rec = {"workload": workload, "kernel_pattern": BX_KERNEL_RE[cfgs[0]],
+           "source_hash": source_hash(TRAFFIC_SOURCES)}
+    for name, path in (("fetch", fetch_csv), ("write", write_csv)):
+        counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
+        per = read_counter_csv(path, counter)
+        cal = [v for k, vs in per.items() if re.search(CALIB_RE, k) for v in vs]
+        bx = [v for k, vs in per.items() if pat.search(k) for v in vs]
+        assert cal and bx, (name, list(per))
+        factor = calib_bytes / (max(cal) * 1024.0)
+        rec[f"{name}_kib_per_launch_raw"] = statistics.mean(bx)
+        rec[f"{name}_calibration_kib"] = max(cal)
+        rec[f"{name}_factor"] = round(factor, 4)
+        rec[f"{name}_bytes_per_launch"] = statistics.mean(bx) * 1024.0 * factor
+        rec[f"{name}_launches"] = len(bx)
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, budget_s=20.0):
@@ -111,7 +170,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--copy-calibration-mib; no GPU needed")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic, args.copy_calibration_mib * 2**20)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -200,7 +267,7 @@ def main():
     bx_kernel = {(160, 256): "W160", (256, 256): "G256"}
     kname = "+".join(f"ns_gemm32_kernel<{bx_kernel[c]}, BX>" if c in bx_kernel else f"ns_gemm_kernel<T{c[0]}, BX>"
                      for c in bx_cfgs)
-    traffic = load_traffic(("gemm32_kernels.hip", "muon_internal.h"), w.name)
+    traffic = load_traffic(TRAFFIC_SOURCES, w.name)
     n_el = w.n_params
     g_bytes = 2 if w.g_dtype == "bf16" else 4
     mom_bytes = n_el * (g_bytes + 8)          # read G, B; write B

@@ -30,15 +30,16 @@
 // fragment reads; rows 32 apart share the swizzle, so one base address per
 // k16 half serves every fragment of a wave (+2048 bytes per 32 rows).
 //
-// Epilogue: a 32x32 accumulator holds, per lane, column (lane & 31) and
+// Epilogues: a 32x32 accumulator holds, per lane, column (lane & 31) and
 // rows 8g + 4 (lane >> 5) + r (g, r = 0..3): four runs of four consecutive
-// rows, stored transposed straight from registers as 8-byte writes; the
-// row-major copy goes through a private 32-row LDS slice per wave.  The
-// last BX of a step (mode BXL) applies the parameter update of the
-// synthesis note's section 4, W <- W - lr * scale * O, directly: O^T rows
-// are W rows for a transposed matrix (16-byte stores from registers), and
-// otherwise the float32 values pass through the slice.  The iterate itself
-// is not stored on the last iteration.
+// rows.  Gram and polynomial tiles are stored transposed straight from
+// registers (8-byte writes, the mirror half) and row-major through a
+// private 32-row LDS slice per wave.  The BX epilogue (bx_epilogue) passes
+// the float32 results through a wave-private LDS tile so that the X^T pair,
+// the row-major X_hi copy and W are all read and written 16 bytes per lane
+// along contiguous rows.  The last BX of a step (mode BXL) applies the
+// parameter update of the synthesis note's section 4, W <- W - lr*scale*O,
+// from the float32 values directly; the iterate itself is not stored then.
 #include "muon_internal.h"
 
 namespace muon {
@@ -74,9 +75,11 @@ struct G32 {
   static constexpr int OPA = BM * 64, OPB = BN * 64;      // bytes per stage
   static constexpr int STAGEB = OPA + OPB;
   static constexpr int NSTAGE = 3;
-  static constexpr int SLICE_LD = WN + 8;                 // epilogue slice row stride (bf16 elements)
-  static constexpr int SLICEF_LD = WN + 4;                // same, float32 slice of the fused update
-  static constexpr int SLICEB = 32 * SLICEF_LD * 4;       // bytes per wave (covers both uses)
+  static constexpr int SLICE_LD = WN + 8;                 // Gram/poly epilogue slice row stride (bf16)
+  static constexpr int TP = 36;                           // BX epilogue tile pitch (floats), see bx_epilogue
+  static constexpr int SLICEB_SYM = 32 * SLICE_LD * 2;
+  static constexpr int SLICEB_BX = WN * TP * 4;
+  static constexpr int SLICEB = SLICEB_SYM > SLICEB_BX ? SLICEB_SYM : SLICEB_BX;  // bytes per wave
   static constexpr int LDSB = (NSTAGE * STAGEB > SLICEB * NW) ? NSTAGE * STAGEB : SLICEB * NW;
   static constexpr int MINB = (NW == 4) ? 2 : 1;          // two waves per SIMD
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
@@ -166,6 +169,150 @@ __device__ __forceinline__ void kstep(const __bf16* __restrict__ Aop, const __bf
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
 }
 
+// Loads of one 32-row block of the BX epilogue inputs (the X^T pair at the
+// positions bx_epilogue's X^T-major pass visits).
+template <class C>
+__device__ __forceinline__ void bx_load_block(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
+                                              uint4 (&hi)[4], uint4 (&lo)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int gj = wj0 + p * 16 + (lane & 15);
+    const int gi = gi0 + (lane >> 4) * 8;
+    const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+    hi[p] = gld<uint4>(d.xt_hi[buf] + off);
+    lo[p] = gld<uint4>(d.xt_lo[buf] + off);
+  }
+}
+
+// BX epilogue of one 32-row block of a wave's sub-tile (32 Gram-side rows
+// gi0.., WN = 64 long-side columns wj0..), X' = a (X_hi + X_lo) + P X_hi.
+//
+// The accumulators (column gj per lane, four runs of four rows) go to a
+// wave-private float32 tile T[gj][gi] in LDS (pitch TP = 36 floats: 16-byte
+// writes of 16 consecutive columns hit all 64 banks once).  Two passes then
+// read T back so that every global access is 16 bytes per lane on
+// contiguous memory:
+//   X^T-major pass: lane (gj, 8 consecutive gi) -> the X^T pair (read and
+//     written 64 contiguous bytes per row), or W's row gj when the matrix
+//     is transposed and this is the last iteration;
+//   X-major pass: lane (gi, 8 consecutive gj) -> the row-major X_hi copy
+//     (128 contiguous bytes per row), or W's row gi on the last iteration.
+// A wave's LDS operations complete in order; the compiler barriers keep the
+// cross-lane exchanges through T in program order.
+template <class C, int MODE>
+__device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int n_pad, int gi0, int wj0,
+                                            int lane, const f32x16_t (&acc)[C::BNB], float* T,
+                                            const uint4 (&hi)[4], const uint4 (&lo)[4]) {
+  const int col = lane & 31;
+  const int rq = 4 * (lane >> 5);
+  const bool tr = d.flags & kTransposed;
+  const bool ortho = d.flags & kOrthoOnly;
+  const float ls = d.lr_scale;
+  const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
+  // accumulators -> T
+#pragma unroll
+  for (int j = 0; j < C::BNB; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float4 v = make_float4(acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+      *reinterpret_cast<float4*>(T + (j * 32 + col) * C::TP + 8 * g + rq) = v;
+    }
+  asm volatile("" ::: "memory");
+  // X^T-major pass
+  const bool need_xmajor = (MODE == BXM) || !tr;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int jl = p * 16 + (lane & 15);
+    const int il = (lane >> 4) * 8;
+    float* tp = T + jl * C::TP + il;
+    const float4 t0 = *reinterpret_cast<const float4*>(tp);
+    const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
+    float v[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    const uint32_t hw[4] = {hi[p].x, hi[p].y, hi[p].z, hi[p].w};
+    const uint32_t lw[4] = {lo[p].x, lo[p].y, lo[p].z, lo[p].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = fmaf(kCoefA, bf_lo(hw[q]) + bf_lo(lw[q]), v[2 * q]);
+      v[2 * q + 1] = fmaf(kCoefA, bf_hi(hw[q]) + bf_hi(lw[q]), v[2 * q + 1]);
+    }
+    const int gj = wj0 + jl;
+    const int gi = gi0 + il;
+    if (MODE == BXM) {
+      uint32_t nh[4], nl[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        nh[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
+        nl[q] = pack_bf16(v[2 * q] - bf_lo(nh[q]), v[2 * q + 1] - bf_hi(nh[q]));
+      }
+      const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+      gst(d.xt_hi[buf ^ 1] + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
+      gst(d.xt_lo[buf ^ 1] + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
+    } else if (tr) {
+      // O^T = X'^T has W's orientation: W[gj][gi .. gi+7].
+      if (gj < d.n) {
+        float* wp = d.W + static_cast<int64_t>(gj) * d.cols + gi;
+        if (gi + 7 < d.m && w16) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+            if (!ortho) {
+              const float4 w = gld<float4>(wp + 4 * h);
+              o = make_float4(fmaf(-ls, o.x, w.x), fmaf(-ls, o.y, w.y), fmaf(-ls, o.z, w.z), fmaf(-ls, o.w, w.w));
+            }
+            gst(wp + 4 * h, o);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gi + e < d.m) gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], gld<float>(wp + e)));
+        }
+      }
+    }
+    if (need_xmajor) {
+      *reinterpret_cast<float4*>(tp) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(tp + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+  if (!need_xmajor) return;
+  asm volatile("" ::: "memory");
+  // X-major pass
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int il = p * 8 + (lane & 7);
+    const int jl = (lane >> 3) * 8;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = T[(jl + e) * C::TP + il];
+    const int gi = gi0 + il;
+    const int gj = wj0 + jl;
+    if (MODE == BXM) {
+      uint32_t nh[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nh[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
+      gst(d.x_hi + static_cast<int64_t>(gi) * n_pad + gj, make_uint4(nh[0], nh[1], nh[2], nh[3]));
+    } else if (gi < d.m) {
+      // non-transposed matrix, last iteration: W[gi][gj .. gj+7]
+      float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
+      if (gj + 7 < d.n && w16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+          if (!ortho) {
+            const float4 w = gld<float4>(wp + 4 * h);
+            o = make_float4(fmaf(-ls, o.x, w.x), fmaf(-ls, o.y, w.y), fmaf(-ls, o.z, w.z), fmaf(-ls, o.w, w.w));
+          }
+          gst(wp + 4 * h, o);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gj + e < d.n) gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], gld<float>(wp + e)));
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     const MatDesc* __restrict__ descs, const int32_t* __restrict__ prefix, int nmats, XcdSplit split, int buf) {
@@ -173,8 +320,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
 
   // XCD-aware work: XCD (block id % 8) walks its own cost-balanced
   // contiguous range of (matrix, tile) work.
-  const int work = split.start[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
-  if (work >= split.start[(blockIdx.x & 7) + 1]) return;
+  const int work = split.begin[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
+  if (work >= split.end[blockIdx.x & 7]) return;
   const int mi = find_mat(prefix, nmats, work);
   const MatDesc& d = descs[mi];
   int local = work - prefix[mi];
@@ -182,9 +329,18 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
 
   int ti, tj;
   if (MODE >= BXM) {
-    const int tpc = m_pad / C::BM;   // Gram-side index fastest: running tiles share X^T panels
-    tj = local / tpc;
-    ti = local - tj * tpc;
+    // Grouped order: groups of bx_group Gram-side tile rows; inside a group
+    // the long-side index is slow and the Gram-side index fast, so tiles
+    // that run together share X^T panels, and the group's rows of P stay
+    // in L2 while the group sweeps the long side.
+    const int tpc = m_pad / C::BM;
+    const int tpr = n_pad / C::BN;
+    const int g = d.bx_group;
+    const int grp = local / (g * tpr);
+    const int rows = min(g, tpc - grp * g);
+    const int rem = local - grp * g * tpr;
+    tj = rem / rows;
+    ti = grp * g + (rem - tj * rows);
   } else {
     const int nt = m_pad / C::BM;
     ti = 0;
@@ -270,26 +426,29 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   __syncthreads();
 
   // ---- epilogue (wave-local).
-  const bool diag = (MODE == GRAM || MODE == POLY) && (ti == tj);
   const int wi0 = ti * C::BM + wr * C::WM;   // first global row of the wave's sub-tile
   const int wj0 = tj * C::BN + wc * C::WN;   // first global column
+  if constexpr (MODE >= BXM) {
+    float* T = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
+    uint4 hi[2][4], lo[2][4];
+    bx_load_block<C>(d, buf, m_pad, wi0, wj0, lane, hi[0], lo[0]);
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) {
+      if (i + 1 < C::BMB) bx_load_block<C>(d, buf, m_pad, wi0 + (i + 1) * 32, wj0, lane, hi[(i + 1) & 1], lo[(i + 1) & 1]);
+      bx_epilogue<C, MODE>(d, buf, m_pad, n_pad, wi0 + i * 32, wj0, lane, acc[i], T, hi[i & 1], lo[i & 1]);
+    }
+    return;
+  }
+  const bool diag = ti == tj;
   __bf16* slice = reinterpret_cast<__bf16*>(smem) + wave * (C::SLICEB / 2);
-  float* slicef = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
-  __bf16* rdst;
-  int64_t rld;
-  if (MODE >= BXM) { rdst = d.x_hi; rld = n_pad; }
-  else { rdst = (MODE == POLY) ? d.poly : d.gram; rld = m_pad; }
+  __bf16* rdst = (MODE == POLY) ? d.poly : d.gram;
+  const int64_t rld = m_pad;
   const int col = lane & 31;
   const int rq = 4 * (lane >> 5);
-  const bool tr = d.flags & kTransposed;
-  const bool ortho = d.flags & kOrthoOnly;
-  const float ls = d.lr_scale;
-  // W is 16-byte aligned (checked at the API); rows are when cols % 4 == 0.
-  const bool w16 = (d.cols & 3) == 0;
 
-  // Epilogue inputs of one block row (X^T pair, or A), double buffered so
-  // the reads of row i+1 are in flight while row i is finished.
-  uint2 in_a[2][C::BNB][4], in_b[2][C::BNB][4];
+  // Epilogue inputs of one block row (A, for the polynomial), double
+  // buffered so the reads of row i+1 are in flight while row i is finished.
+  uint2 in_a[2][C::BNB][4];
   auto load_row = [&](int i, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j)
@@ -298,12 +457,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
         const int gi = wi0 + i * 32 + 8 * g + rq;
         const int gj = wj0 + j * 32 + col;
         const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-        if (MODE >= BXM) {
-          in_a[slot][j][g] = gld<uint2>(d.xt_hi[buf] + off);
-          in_b[slot][j][g] = gld<uint2>(d.xt_lo[buf] + off);
-        } else if (MODE == POLY) {
-          in_a[slot][j][g] = gld<uint2>(d.gram + off);  // A symmetric
-        }
+        if (MODE == POLY) in_a[slot][j][g] = gld<uint2>(d.gram + off);  // A symmetric
       }
   };
   if (MODE != GRAM) load_row(0, 0);
@@ -321,48 +475,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
         uint32_t w0 = 0, w1 = 0;
-        if (MODE >= BXM) {
-          const uint2 hx = in_a[slot][j][g], lx = in_b[slot][j][g];
-          v[0] = fmaf(kCoefA, bf_lo(hx.x) + bf_lo(lx.x), v[0]);
-          v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), v[1]);
-          v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), v[2]);
-          v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), v[3]);
-        }
-        if (MODE == BXM) {
-          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-          w0 = pack_bf16(v[0], v[1]);
-          w1 = pack_bf16(v[2], v[3]);
-          const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
-          const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
-          gst(d.xt_hi[buf ^ 1] + off, make_uint2(w0, w1));
-          gst(d.xt_lo[buf ^ 1] + off, make_uint2(l0, l1));
-        } else if (MODE == BXL) {
-          // O = X' (fp32).  Transposed matrix: O^T = X'^T is W's orientation,
-          // so rows gj of W take four consecutive columns gi..gi+3.
-          if (tr) {
-            if (gj < d.n) {
-              float* wp = d.W + static_cast<int64_t>(gj) * d.cols + gi;
-              if (gi + 3 < d.m && w16) {
-                float4 o = make_float4(v[0], v[1], v[2], v[3]);
-                if (!ortho) {
-                  const float4 w = gld<float4>(wp);
-                  o = make_float4(fmaf(-ls, v[0], w.x), fmaf(-ls, v[1], w.y), fmaf(-ls, v[2], w.z), fmaf(-ls, v[3], w.w));
-                }
-                gst(wp, o);
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (gi + r < d.m) gst(wp + r, ortho ? v[r] : fmaf(-ls, v[r], gld<float>(wp + r)));
-              }
-            }
-          } else {
-            const int rl = 8 * g + rq;
-            const int cl = j * 32 + col;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) slicef[(rl + r) * C::SLICEF_LD + cl] = v[r];
-          }
-          continue;
-        } else {
+        {
           if (MODE == POLY) {
             const uint2 a = in_a[slot][j][g];
             v[0] = fmaf(kCoefC, v[0], kCoefB * bf_lo(a.x));
@@ -392,38 +505,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
         for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::SLICE_LD + cl, &hb[r], 2);
       }
     }
-    if (MODE == BXL) {
-      // Non-transposed matrix: W[gi][gj..gj+3] from the float32 slice.
-      if (!tr) {
-        constexpr int CPR = C::WN / 4;
-#pragma unroll
-        for (int c = lane; c < 32 * CPR; c += 64) {
-          const int rl = c / CPR;
-          const int cc = c - rl * CPR;
-          const int gi = wi0 + i * 32 + rl;
-          const int gj = wj0 + cc * 4;
-          if (gi >= d.m || gj >= d.n) continue;
-          const float4 o = *reinterpret_cast<const float4*>(slicef + rl * C::SLICEF_LD + cc * 4);
-          float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
-          if (gj + 3 < d.n && w16) {
-            if (ortho) {
-              gst(wp, o);
-            } else {
-              const float4 w = gld<float4>(wp);
-              gst(wp, make_float4(fmaf(-ls, o.x, w.x), fmaf(-ls, o.y, w.y), fmaf(-ls, o.z, w.z), fmaf(-ls, o.w, w.w)));
-            }
-          } else {
-            const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gj + e < d.n) gst(wp + e, ortho ? ov[e] : fmaf(-ls, ov[e], gld<float>(wp + e)));
-          }
-        }
-      }
-      continue;
-    }
-    // Slice (32 rows x WN) -> global rows, 16 bytes at a time.  The wave's
-    // own LDS writes are ordered before its reads by the compiler.
+    // Slice (32 rows x WN) -> global rows, 16 bytes at a time.  A wave's
+    // LDS operations complete in order; the compiler barrier keeps the
+    // cross-lane exchange through the slice in program order.
+    asm volatile("" ::: "memory");
     constexpr int CPR = C::WN / 8;
 #pragma unroll
     for (int c = lane; c < 32 * CPR; c += 64) {

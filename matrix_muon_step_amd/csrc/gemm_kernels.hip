@@ -201,8 +201,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
 
   // ---- XCD-aware work: XCD (block id % 8) walks its own cost-balanced
   // contiguous range of (matrix, tile) work.
-  const int work = split.start[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
-  if (work >= split.start[(blockIdx.x & 7) + 1]) return;
+  const int work = split.begin[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
+  if (work >= split.end[blockIdx.x & 7]) return;
   const int mi = find_mat(prefix, nmats, work);
   const MatDesc& d = descs[mi];
   int local = work - prefix[mi];

@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/muon.h"
+#include "muon.h"
 #include "muon_internal.h"
 
 using namespace muon;
@@ -139,6 +139,17 @@ MatCfg choose_cfg(int64_t m, int64_t n) {
   return best;
 }
 
+// Gram-side tile rows per group of the BX tile order (wide-tile kernels).
+int bx_group(const MatCfg& cfg) {
+  const int tpc = static_cast<int>(cfg.m_pad / kCfgRows[cfg.bx]);
+  static const int forced = [] {
+    const char* e = getenv("MUON_BX_GROUP");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced > 0) return forced < tpc ? forced : tpc;
+  return tpc;
+}
+
 // Validates shapes and scalars of every item and fills the plan (offsets
 // relative to a workspace base of 0).  Pointer checks happen separately.
 muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan) {
@@ -182,6 +193,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.m_pad = static_cast<int32_t>(cfg.m_pad);
     d.n_pad = static_cast<int32_t>(cfg.n_pad);
     d.k_gram = static_cast<int32_t>(round_up(nn, 32));
+    d.bx_group = small ? 0 : bx_group(cfg);
     // The wide-tile BX kernels apply the update from their last launch.
     const bool fused = !small && ns_steps > 0 && (cfg.bx == kCfgG256 || cfg.bx == kCfgW160);
     d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0) | (fused ? kFusedUpd : 0);
@@ -394,9 +406,9 @@ XcdSplit make_split(const Plan& plan, int tab, int mode) {
     const double c = (mode == 0) ? plan.descs[i].k_gram : plan.descs[i].m_pad;
     total += static_cast<double>(pre[i + 1] - pre[i]) * c;
   }
-  XcdSplit sp;
-  sp.start[0] = 0;
-  sp.start[8] = pre[n];
+  int32_t start[9];
+  start[0] = 0;
+  start[8] = pre[n];
   int i = 0;
   double before = 0.0;  // cost of matrices 0..i-1
   for (int x = 1; x < 8; ++x) {
@@ -415,11 +427,33 @@ XcdSplit make_split(const Plan& plan, int tab, int mode) {
       const int64_t lo = pre[i], hi = pre[i + 1];
       w = static_cast<int>(std::min(hi, std::max(lo, lo + k)));
     }
-    sp.start[x] = std::max(w, sp.start[x - 1]);
+    start[x] = std::max(w, start[x - 1]);
   }
+  XcdSplit sp;
   sp.max_len = 0;
-  for (int x = 0; x < 8; ++x) sp.max_len = std::max(sp.max_len, sp.start[x + 1] - sp.start[x]);
+  for (int x = 0; x < 8; ++x) {
+    sp.begin[x] = start[x];
+    sp.end[x] = start[x + 1];
+    sp.max_len = std::max(sp.max_len, start[x + 1] - start[x]);
+  }
   return sp;
+}
+
+// Round r of a split cut into rounds of at most `len` work items per XCD.
+XcdSplit split_round(const XcdSplit& sp, int r, int len) {
+  XcdSplit o;
+  o.max_len = 0;
+  for (int x = 0; x < 8; ++x) {
+    o.begin[x] = std::min(sp.end[x], sp.begin[x] + r * len);
+    o.end[x] = std::min(sp.end[x], o.begin[x] + len);
+    o.max_len = std::max(o.max_len, o.end[x] - o.begin[x]);
+  }
+  return o;
+}
+
+int env_int(const char* name) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : 0;
 }
 
 muon_status_t hip_fail(hipError_t e, const char* where) {
@@ -462,14 +496,20 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
       for (int c = 0; c < kNumCfg; ++c) {
         const int tab = mode == 2 ? tab_bx(c) : tab_sym(c);
         if (plan.tot[tab] == 0) continue;
-        const XcdSplit sp = make_split(plan, tab, mode);
+        const XcdSplit full = make_split(plan, tab, mode);
         const bool wide = c == kCfgG256 || c == kCfgW160;
         const int kmode = (wide && last && mode == 2) ? 3 : mode;  // 3: BX with the update applied
-        e = run_stage(kmode == 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
-          return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, s)
-                      : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
-        });
-        if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
+        static const int round_len[3] = {env_int("MUON_ROUND_GRAM"), env_int("MUON_ROUND_POLY"),
+                                         env_int("MUON_ROUND_BX")};
+        const int len = round_len[mode] > 0 ? round_len[mode] : full.max_len;
+        for (int r = 0; r * len < full.max_len; ++r) {
+          const XcdSplit sp = split_round(full, r, len);
+          e = run_stage(kmode == 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
+            return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, s)
+                        : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
+          });
+          if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
+        }
       }
     }
     if (plan.tot[kTabSmallGram] > 0) {

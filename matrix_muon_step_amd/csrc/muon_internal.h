@@ -76,15 +76,17 @@ struct MatDesc {
   int32_t sym_cfg;     // kernel configuration of the Gram / polynomial stages
   int32_t bx_cfg;      // kernel configuration of the BX stage
   int32_t k_gram;      // reduction length of the Gram product: n rounded up to 32
+  int32_t bx_group;    // BX tile order: Gram-side tile rows per group (see gemm32)
 };
 
 // Split of one grouped GEMM launch over the 8 XCDs: work-groups are dealt
 // to XCDs round-robin (block id % 8), and XCD x runs the contiguous work
-// range [start[x], start[x+1]), chosen on the host so every XCD gets the
-// same estimated cost (tiles differ in reduction length).  Blocks beyond
-// their XCD's range exit at once; the grid is 8 * max range length.
+// range [begin[x], end[x]), chosen on the host so every XCD gets the same
+// estimated cost (tiles differ in reduction length).  Blocks beyond their
+// XCD's range exit at once; the grid is 8 * max range length.
 struct XcdSplit {
-  int32_t start[9];
+  int32_t begin[8];
+  int32_t end[8];
   int32_t max_len;
 };
 
