@@ -26,9 +26,11 @@
 // the in-flight direct-to-LDS loads without a blanket wait.  Each wave
 // waits for its own loads (vmcnt) and a barrier publishes a stage.
 // Operand rows are 64 bytes in LDS with the four 16-byte k-chunks
-// XOR-swizzled by row ((r >> 1) ^ (r >> 3)), conflict-free for the 32-row
-// fragment reads; rows 32 apart share the swizzle, so one base address per
-// k16 half serves every fragment of a wave (+2048 bytes per 32 rows).
+// XOR-swizzled by row ((r >> 1) ^ (r >> 2)): measured conflict-free on
+// gfx950 for the 32x32x16 and 16x16x32 fragment reads (the (r >> 1) ^
+// (r >> 3) form runs at half the LDS rate).  The swizzle repeats every 8
+// rows, so one base address per k16 half serves every fragment of a wave
+// (+2048 bytes per 32 rows).
 //
 // Epilogues: a 32x32 accumulator holds, per lane, column (lane & 31) and
 // rows 8g + 4 (lane >> 5) + r (g, r = 0..3): four runs of four consecutive
@@ -62,7 +64,7 @@ constexpr float kCoefC = 2.0315f;
 // mode) straight from the epilogue.
 enum Mode { GRAM = 0, POLY = 1, BXM = 2, BXL = 3 };
 
-template <int BM_, int BN_, int NWM_, int NWN_>
+template <int BM_, int BN_, int NWM_, int NWN_, int NSTAGE_>
 struct G32 {
   static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
   static constexpr int NW = NWM * NWN;
@@ -74,7 +76,7 @@ struct G32 {
   static constexpr int QBMAX = (QB + NW - 1) / NW;
   static constexpr int OPA = BM * 64, OPB = BN * 64;      // bytes per stage
   static constexpr int STAGEB = OPA + OPB;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = NSTAGE_;                  // ring of LDS stages
   static constexpr int SLICE_LD = WN + 8;                 // Gram/poly epilogue slice row stride (bf16)
   static constexpr int TP = 36;                           // BX epilogue tile pitch (floats), see bx_epilogue
   static constexpr int SLICEB_SYM = 32 * SLICE_LD * 2;
@@ -86,7 +88,7 @@ struct G32 {
   static_assert(NW == 4 || NW == 8, "swizzle invariance of the load slots assumes 4 or 8 waves");
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
 __device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
   int lo = 0, hi = nmats - 1;
@@ -112,7 +114,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 template <int PER>
 __device__ __forceinline__ void wait_newer(int newer) {
   if (newer <= 0) MUON_WAIT_VM(0);
-  else MUON_WAIT_VM(PER);
+  else if (newer == 1) MUON_WAIT_VM(PER);
+  else if (newer == 2) MUON_WAIT_VM(2 * PER);
+  else MUON_WAIT_VM(3 * PER);
 }
 
 template <class C>
@@ -142,35 +146,120 @@ __device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, cons
   }
 }
 
-// One 32-deep k-step: optionally queue a future step's loads into `dst`,
-// then multiply the fragments of the stage at `src`.
+// Fragments of one k16 half of a stage: A rows of the wave (BMB blocks of
+// 32) and B rows (BNB blocks), one 16-byte LDS read each.
 template <class C>
-__device__ __forceinline__ void kstep(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
-                                      const Slots<C>& sl, int kfut, bool queue,
-                                      LAS unsigned char* __restrict__ dst,
-                                      const LAS unsigned char* __restrict__ src,
-                                      f32x16_t (&acc)[C::BMB][C::BNB], int wave,
-                                      const int (&abase)[2], const int (&bbase)[2]) {
-  if (queue) issue_loads<C>(Aop, Bop, sl, kfut, dst, wave);
-  bf16x8_t a[2][C::BMB], b[2][C::BNB];
+__device__ __forceinline__ void read_half(const LAS unsigned char* __restrict__ src, int h, const int (&abase)[2],
+                                          const int (&bbase)[2], bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int j = 0; j < C::BNB; ++j) b[j] = *(const LAS bf16x8_t*)(src + bbase[h] + j * 2048);
 #pragma unroll
-    for (int j = 0; j < C::BNB; ++j) b[h][j] = *(const LAS bf16x8_t*)(src + bbase[h] + j * 2048);
-#pragma unroll
-    for (int i = 0; i < C::BMB; ++i) a[h][i] = *(const LAS bf16x8_t*)(src + abase[h] + i * 2048);
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int i = 0; i < C::BMB; ++i)
-#pragma unroll
-      for (int j = 0; j < C::BNB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+  for (int i = 0; i < C::BMB; ++i) a[i] = *(const LAS bf16x8_t*)(src + abase[h] + i * 2048);
 }
 
-// Loads of one 32-row block of the BX epilogue inputs (the X^T pair at the
-// positions bx_epilogue's X^T-major pass visits).
+template <class C>
+__device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf16x8_t (&b)[C::BNB],
+                                          f32x16_t (&acc)[C::BMB][C::BNB]) {
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// After the barrier of a step: queue a future step's loads into the ring
+// slot just released (`dst`) and read the first k16 half of the next stage
+// (`src`).  The two slots always differ; __restrict__ lets the compiler
+// order the LDS reads against the in-flight direct-to-LDS loads without a
+// blanket wait.
+template <class C>
+__device__ __forceinline__ void refill_and_read(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                                const Slots<C>& sl, int kfut, bool queue,
+                                                LAS unsigned char* __restrict__ dst,
+                                                const LAS unsigned char* __restrict__ src, int wave,
+                                                const int (&abase)[2], const int (&bbase)[2],
+                                                bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
+  if (queue) issue_loads<C>(Aop, Bop, sl, kfut, dst, wave);
+  read_half<C>(src, 0, abase, bbase, a, b);
+}
+
+// Scheduling pattern for a block of first-half products and second-half
+// fragment reads: one LDS read after each product, so the reads stream out
+// while the matrix core works and the products never wait on them.
+template <class C>
+__device__ __forceinline__ void interleave() {
+  constexpr int NR = C::BMB + C::BNB;      // fragment reads of a half
+  constexpr int NM = C::BMB * C::BNB;      // products of a half
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Main loop, software pipelined by k16 halves.  Step kt: multiply the first
+// half of stage kt (read before) while reading its second half, then (after this
+// wave's loads of step kt+1 have landed and its own reads of stage kt have
+// completed) a barrier publishes stage kt+1 and frees stage kt, which is
+// refilled with step kt+NSTAGE; the first half of stage kt+1 is read while
+// the second half of step kt is multiplied.  The barrier's wait is thus
+// covered by queued matrix-core work and the next step's first reads.
+// PER (this wave's loads per step) is a template parameter and the steady
+// phase has a fixed number of steps in flight, so the loop body has no
+// branches and every wait count is an immediate.
+template <class C, int PER>
+__device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                          const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave,
+                                          const int (&abase)[2], const int (&bbase)[2],
+                                          f32x16_t (&acc)[C::BMB][C::BNB]) {
+#pragma unroll
+  for (int st = 0; st < C::NSTAGE; ++st)
+    if (st < nk) issue_loads<C>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
+  wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  bf16x8_t fa0[C::BMB], fb0[C::BNB], fa1[C::BMB], fb1[C::BNB];
+  read_half<C>(lds, 0, abase, bbase, fa0, fb0);
+  int kt = 0;
+  // Steady phase: every step refills its slot and leaves NSTAGE-2 later
+  // steps in flight.
+  for (; kt < nk - C::NSTAGE; ++kt) {
+    LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
+    mfma_half<C>(fa0, fb0, acc);
+    read_half<C>(cur, 1, abase, bbase, fa1, fb1);
+    interleave<C>();
+    MUON_WAIT_VM((C::NSTAGE - 2) * PER);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    refill_and_read<C>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur, lds + ((kt + 1) % C::NSTAGE) * C::STAGEB,
+                       wave, abase, bbase, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half<C>(fa1, fb1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Drain phase: no refills; the steps still in flight land one by one.
+  for (; kt + 1 < nk; ++kt) {
+    LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
+    mfma_half<C>(fa0, fb0, acc);
+    read_half<C>(cur, 1, abase, bbase, fa1, fb1);
+    interleave<C>();
+    wait_newer<PER>(nk - 2 - kt);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_half<C>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, abase, bbase, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half<C>(fa1, fb1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  read_half<C>(lds + ((nk - 1) % C::NSTAGE) * C::STAGEB, 1, abase, bbase, fa1, fb1);
+  mfma_half<C>(fa0, fb0, acc);
+  mfma_half<C>(fa1, fb1, acc);
+}
+
 template <class C>
 __device__ __forceinline__ void bx_load_block(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
                                               uint4 (&hi)[4], uint4 (&lo)[4]) {
@@ -187,9 +276,10 @@ __device__ __forceinline__ void bx_load_block(const MatDesc& d, int buf, int m_p
 // BX epilogue of one 32-row block of a wave's sub-tile (32 Gram-side rows
 // gi0.., WN = 64 long-side columns wj0..), X' = a (X_hi + X_lo) + P X_hi.
 //
-// The accumulators (column gj per lane, four runs of four rows) go to a
-// wave-private float32 tile T[gj][gi] in LDS (pitch TP = 36 floats: 16-byte
-// writes of 16 consecutive columns hit all 64 banks once).  Two passes then
+// The accumulators (column gj per lane, four runs of four rows) have gone
+// to a wave-private float32 tile T[gj][gi] in LDS (bx_stage_acc; pitch
+// TP = 36 floats: 16-byte writes of 16 consecutive columns hit all 64 banks
+// once).  Two passes then
 // read T back so that every global access is 16 bytes per lane on
 // contiguous memory:
 //   X^T-major pass: lane (gj, 8 consecutive gi) -> the X^T pair (read and
@@ -199,17 +289,10 @@ __device__ __forceinline__ void bx_load_block(const MatDesc& d, int buf, int m_p
 //     (128 contiguous bytes per row), or W's row gi on the last iteration.
 // A wave's LDS operations complete in order; the compiler barriers keep the
 // cross-lane exchanges through T in program order.
-template <class C, int MODE>
-__device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int n_pad, int gi0, int wj0,
-                                            int lane, const f32x16_t (&acc)[C::BNB], float* T,
-                                            const uint4 (&hi)[4], const uint4 (&lo)[4]) {
+template <class C>
+__device__ __forceinline__ void bx_stage_acc(int lane, const f32x16_t (&acc)[C::BNB], float* T) {
   const int col = lane & 31;
   const int rq = 4 * (lane >> 5);
-  const bool tr = d.flags & kTransposed;
-  const bool ortho = d.flags & kOrthoOnly;
-  const float ls = d.lr_scale;
-  const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
-  // accumulators -> T
 #pragma unroll
   for (int j = 0; j < C::BNB; ++j)
 #pragma unroll
@@ -218,6 +301,15 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
       *reinterpret_cast<float4*>(T + (j * 32 + col) * C::TP + 8 * g + rq) = v;
     }
   asm volatile("" ::: "memory");
+}
+
+template <class C, int MODE>
+__device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int n_pad, int gi0, int wj0,
+                                            int lane, float* T, const uint4 (&hi)[4], const uint4 (&lo)[4]) {
+  const bool tr = d.flags & kTransposed;
+  const bool ortho = d.flags & kOrthoOnly;
+  const float ls = d.lr_scale;
+  const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
   // X^T-major pass
   const bool need_xmajor = (MODE == BXM) || !tr;
 #pragma unroll
@@ -407,22 +499,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
 
   const int nk = K / 32;
   LAS unsigned char* lds = (LAS unsigned char*)smem;
-  issue_loads<C>(Aop, Bop, sl, 0, lds, wave);
-  if (nk > 1) issue_loads<C>(Aop, Bop, sl, 32, lds + C::STAGEB, wave);
-
   constexpr int PER_FULL = C::QAMAX + C::QBMAX;
-  for (int kt = 0; kt < nk; ++kt) {
-    // Outstanding: steps kt and (if it exists) kt+1; wait for the older.
-    const int newer = (kt + 1 < nk) ? 1 : 0;
-    if (per == PER_FULL) wait_newer<PER_FULL>(newer);
-    else if (per == PER_FULL - 1) wait_newer<PER_FULL - 1>(newer);
-    else wait_newer<PER_FULL - 2>(newer);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // keep LDS reads and refills of this step below the barrier
-    const int fut = kt + 2;
-    kstep<C>(Aop, Bop, sl, fut * 32, fut < nk, lds + (fut % 3) * C::STAGEB, lds + (kt % 3) * C::STAGEB,
-             acc, wave, abase, bbase);
-  }
+  if (per == PER_FULL) main_loop<C, PER_FULL>(Aop, Bop, sl, nk, lds, wave, abase, bbase, acc);
+  else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1>(Aop, Bop, sl, nk, lds, wave, abase, bbase, acc);
+  else main_loop<C, PER_FULL - 2>(Aop, Bop, sl, nk, lds, wave, abase, bbase, acc);
   __syncthreads();
 
   // ---- epilogue (wave-local).
@@ -434,8 +514,11 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     bx_load_block<C>(d, buf, m_pad, wi0, wj0, lane, hi[0], lo[0]);
 #pragma unroll
     for (int i = 0; i < C::BMB; ++i) {
+      // Block i's accumulators go to the LDS tile first, so their registers
+      // are free before the next block's inputs are requested.
+      bx_stage_acc<C>(lane, acc[i], T);
       if (i + 1 < C::BMB) bx_load_block<C>(d, buf, m_pad, wi0 + (i + 1) * 32, wj0, lane, hi[(i + 1) & 1], lo[(i + 1) & 1]);
-      bx_epilogue<C, MODE>(d, buf, m_pad, n_pad, wi0 + i * 32, wj0, lane, acc[i], T, hi[i & 1], lo[i & 1]);
+      bx_epilogue<C, MODE>(d, buf, m_pad, n_pad, wi0 + i * 32, wj0, lane, T, hi[i & 1], lo[i & 1]);
     }
     return;
   }
@@ -531,8 +614,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   }
 }
 
-using G256 = G32<256, 256, 2, 4>;
-using W160 = G32<160, 256, 1, 4>;
+using G256 = G32<256, 256, 2, 4, 4>;
+using W160 = G32<160, 256, 1, 4, 3>;
+using W320 = G32<320, 256, 2, 4, 4>;
 
 template <class C, int MODE>
 hipError_t launch(const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp, int buf, hipStream_t s) {
@@ -553,6 +637,8 @@ hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* 
   }
   if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, s);
   if (cfg == kCfgW160 && mode == BXL) return launch<W160, BXL>(d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgW320 && mode == BXM) return launch<W320, BXM>(d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgW320 && mode == BXL) return launch<W320, BXL>(d, prefix, nmats, split, buf, s);
   return hipErrorInvalidValue;
 }
 

@@ -30,8 +30,9 @@
 // registers stage the operands and two steps of matrix work cover the load
 // latency.  Each wave waits for its own loads (vmcnt) and a barrier makes a
 // stage visible to all.  An LDS row holds the 32 k-values of one operand row
-// as four 16-byte chunks whose positions are XOR-swizzled by the row index,
-// which keeps the 16-lane fragment reads free of bank conflicts.
+// as four 16-byte chunks whose positions are XOR-swizzled by the row index
+// ((r >> 1) ^ (r >> 2), measured free of bank conflicts on gfx950 for these
+// fragment reads).
 //
 // Tile order.  Work-groups are dealt to the 8 XCDs round-robin; the block id
 // is remapped so each XCD walks a contiguous range of (matrix, tile) work,
@@ -89,7 +90,7 @@ struct Cfg {
 };
 
 // Chunk position of k-chunk c (0..3) in LDS row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
 // s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
 // lgkmcnt[11:8], vmcnt[5:4] in [15:14]).

@@ -103,25 +103,29 @@ int64_t upper_tiles(int64_t mp, int t) {
 // combination with the least estimated time, i.e. padded matrix-core work
 // (upper tiles for the symmetric products) divided by each configuration's
 // sustained rate on gfx950 (measured: 32x32 wide tiles ~1.1 PF/s, 16x16
-// 160-tiles ~0.85, 128-tiles ~0.7).  MUON_GEMM_CFG=g256|w160|t160|t128
+// 160-tiles ~0.85, 128-tiles ~0.7).  MUON_GEMM_CFG=g256|w160|t160|t128|w320
 // forces one combination (tuning).
 MatCfg choose_cfg(int64_t m, int64_t n) {
   struct Cand { const char* name; int sym, bx; };
   static const Cand cands[] = {
       {"g256", kCfgG256, kCfgG256}, {"w160", kCfgT160, kCfgW160},
-      {"t160", kCfgT160, kCfgT160}, {"t128", kCfgT128, kCfgT128}};
-  static const double rate[kNumCfg] = {1.10, 1.00, 0.85, 0.70};
+      {"t160", kCfgT160, kCfgT160}, {"t128", kCfgT128, kCfgT128}, {"w320", kCfgT160, kCfgW320}};
+  constexpr int kCands = sizeof(cands) / sizeof(cands[0]);
+  static const double rate[kNumCfg] = {1.10, 1.00, 0.85, 0.70, 0.99};
   static const int forced = [] {
     const char* e = getenv("MUON_GEMM_CFG");
     if (!e) return -1;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kCands; ++i)
       if (strcmp(e, cands[i].name) == 0) return i;
     return -1;
   }();
+  // A forced combination applies only where it fits the matrix.
+  int only = -1;
+  if (forced >= 0 && round_up(m, kCfgRows[cands[forced].sym]) % kCfgRows[cands[forced].bx] == 0) only = forced;
   MatCfg best{};
   double best_cost = 0.0;
-  for (int i = 0; i < 4; ++i) {
-    if (forced >= 0 && i != forced) continue;
+  for (int i = 0; i < kCands; ++i) {
+    if (only >= 0 && i != only) continue;
     const Cand& c = cands[i];
     const int64_t mp = round_up(m, kCfgRows[c.sym]);
     if (mp % kCfgRows[c.bx] != 0) continue;
@@ -195,7 +199,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.k_gram = static_cast<int32_t>(round_up(nn, 32));
     d.bx_group = small ? 0 : bx_group(cfg);
     // The wide-tile BX kernels apply the update from their last launch.
-    const bool fused = !small && ns_steps > 0 && (cfg.bx == kCfgG256 || cfg.bx == kCfgW160);
+    const bool fused = !small && ns_steps > 0 && cfg_wide(cfg.bx);
     d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0) | (fused ? kFusedUpd : 0);
     d.lr_scale = it.lr_scale;
     d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
@@ -497,7 +501,7 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
         const int tab = mode == 2 ? tab_bx(c) : tab_sym(c);
         if (plan.tot[tab] == 0) continue;
         const XcdSplit full = make_split(plan, tab, mode);
-        const bool wide = c == kCfgG256 || c == kCfgW160;
+        const bool wide = cfg_wide(c);
         const int kmode = (wide && last && mode == 2) ? 3 : mode;  // 3: BX with the update applied
         static const int round_len[3] = {env_int("MUON_ROUND_GRAM"), env_int("MUON_ROUND_POLY"),
                                          env_int("MUON_ROUND_BX")};

@@ -25,13 +25,16 @@ __device__ __forceinline__ void gst(void* p, T v) {
 // Matrix-core kernel configurations (tile rows x tile columns, MFMA shape):
 //   G256: 256 x 256, 32x32x16   (Gram, polynomial, BX)
 //   W160: 160 x 256, 32x32x16   (BX only; Gram side a multiple of 160)
+//   W320: 320 x 256, 32x32x16   (BX only; Gram side a multiple of 320)
 //   T160: 160 x 160, 16x16x32   (Gram, polynomial, BX)
 //   T128: 128 x 128, 16x16x32   (Gram, polynomial, BX)
 // Every iterate / Gram buffer is zero padded to multiples of its matrix's
 // tile edges, so the GEMM kernels never bounds-check.
-enum GemmCfg : int32_t { kCfgG256 = 0, kCfgW160 = 1, kCfgT160 = 2, kCfgT128 = 3, kNumCfg = 4 };
-constexpr int kCfgRows[kNumCfg] = {256, 160, 160, 128};   // tile rows (Gram side)
-constexpr int kCfgCols[kNumCfg] = {256, 256, 160, 128};   // tile columns (long side for BX)
+enum GemmCfg : int32_t { kCfgG256 = 0, kCfgW160 = 1, kCfgT160 = 2, kCfgT128 = 3, kCfgW320 = 4, kNumCfg = 5 };
+constexpr int kCfgRows[kNumCfg] = {256, 160, 160, 128, 320};   // tile rows (Gram side)
+constexpr int kCfgCols[kNumCfg] = {256, 256, 160, 128, 256};   // tile columns (long side for BX)
+// Configurations served by the 32x32x16 wide-tile kernels.
+constexpr bool cfg_wide(int c) { return c == kCfgG256 || c == kCfgW160 || c == kCfgW320; }
 // Tile edge of the layout kernels (normalise/transpose, update).
 constexpr int kEwTile = 64;
 // Elements per work-group of the momentum/norm kernel.
