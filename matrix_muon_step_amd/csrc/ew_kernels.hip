@@ -207,23 +207,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
     }
     return;
   }
-  // Row-major X_hi (Gram operand) when the iteration runs at all.
-  if (d.x_hi) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int il = ty + 16 * k;
-      if (i0 + il >= m_pad || j0 + tx * 4 >= n_pad) continue;
-      __bf16 h[4];
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int jl = tx * 4 + c4;
-        h[c4] = static_cast<__bf16>(sigma * (tr ? tile[jl][il] : tile[il][jl]));
-      }
-      uint2 hv;
-      __builtin_memcpy(&hv, h, 8);
-      gst(d.x_hi + static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4, hv);
-    }
-  }
   // X^T as the bf16 pair: row j of X^T holds column j of X.
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

@@ -37,9 +37,8 @@
 // rows.  Gram and polynomial tiles are stored transposed straight from
 // registers (8-byte writes, the mirror half) and row-major through a
 // private 32-row LDS slice per wave.  The BX epilogue (bx_epilogue) passes
-// the float32 results through a wave-private LDS tile so that the X^T pair,
-// the row-major X_hi copy and W are all read and written 16 bytes per lane
-// along contiguous rows.  The last BX of a step (mode BXL) applies the
+// the float32 results through a wave-private LDS tile so that the X^T pair
+// and W are read and written 16 bytes per lane along contiguous rows.  The last BX of a step (mode BXL) applies the
 // parameter update of the synthesis note's section 4, W <- W - lr*scale*O,
 // from the float32 values directly; the iterate itself is not stored then.
 #include "muon_internal.h"
@@ -49,6 +48,7 @@ namespace muon {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 #define GAS __attribute__((address_space(1)))
@@ -119,11 +119,14 @@ __device__ __forceinline__ void wait_newer(int newer) {
   else MUON_WAIT_VM(3 * PER);
 }
 
+// Direct-to-LDS load slots of one lane: element offsets of its A and B
+// loads within a step, and the element distance between steps (32 along a
+// row for row-major operands, 32 rows for the transposed Gram operand).
 template <class C>
 struct Slots {
-  int a0, b0;       // element offset of this lane's first A / B load slot
-  int astr, bstr;   // element stride between its successive slots
-  int na, nb;       // slots per step (A, B)
+  int aoff[C::QAMAX];
+  int boff[C::QBMAX];
+  int kmul;
 };
 
 template <class C>
@@ -134,27 +137,59 @@ __device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, cons
   for (int i = 0; i < C::QAMAX; ++i) {
     const int q = wave + i * C::NW;
     if (i < C::QAMAX - 1 || q < C::QA)
-      __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.a0 + i * sl.astr + k0),
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.aoff[i] + k0 * sl.kmul),
                                        (LAS void*)(dst + q * 1024), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::QBMAX; ++i) {
     const int q = wave + i * C::NW;
     if (i < C::QBMAX - 1 || q < C::QB)
-      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.b0 + i * sl.bstr + k0),
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.boff[i] + k0 * sl.kmul),
                                        (LAS void*)(dst + C::OPA + q * 1024), 16, 0, 0);
   }
 }
 
-// Fragments of one k16 half of a stage: A rows of the wave (BMB blocks of
-// 32) and B rows (BNB blocks), one 16-byte LDS read each.
+// LDS fragment addresses of a lane (bytes within a stage).  Row-major
+// operands: one base per k16 half, +2048 per 32-row block.  Transposed
+// (Gram) operands: one base per 32-row block; a k16 half adds 16 k-rows.
 template <class C>
-__device__ __forceinline__ void read_half(const LAS unsigned char* __restrict__ src, int h, const int (&abase)[2],
-                                          const int (&bbase)[2], bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
+struct Frag {
+  int a[C::BMB > 2 ? C::BMB : 2];
+  int b[C::BNB > 2 ? C::BNB : 2];
+};
+
+__device__ __forceinline__ bf16x8_t join4(bf16x4_t lo, bf16x4_t hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Fragments of one k16 half of a stage: A rows of the wave (BMB blocks of
+// 32) and B rows (BNB blocks).  Row-major operands: one 16-byte LDS read
+// each.  Transposed operands (TR, Gram from X^T): two transposing 8-byte
+// reads (ds_read_b64_tr_b16) give the 4 + 4 consecutive k of the lane's row.
+template <class C, bool TR>
+__device__ __forceinline__ void read_half(const LAS unsigned char* __restrict__ src, int h, const Frag<C>& f,
+                                          bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
+  if constexpr (TR) {
+    constexpr int RP = 2 * C::BM;  // k-row pitch (bytes); A and B are equally wide here
+    const int ho = h * 16 * RP;
 #pragma unroll
-  for (int j = 0; j < C::BNB; ++j) b[j] = *(const LAS bf16x8_t*)(src + bbase[h] + j * 2048);
+    for (int j = 0; j < C::BNB; ++j) {
+      const LAS unsigned char* p = src + f.b[j] + ho;
+      b[j] = join4(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
+                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)));
+    }
 #pragma unroll
-  for (int i = 0; i < C::BMB; ++i) a[i] = *(const LAS bf16x8_t*)(src + abase[h] + i * 2048);
+    for (int i = 0; i < C::BMB; ++i) {
+      const LAS unsigned char* p = src + f.a[i] + ho;
+      a[i] = join4(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
+                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j) b[j] = *(const LAS bf16x8_t*)(src + f.b[h] + j * 2048);
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) a[i] = *(const LAS bf16x8_t*)(src + f.a[h] + i * 2048);
+  }
 }
 
 template <class C>
@@ -172,15 +207,14 @@ __device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf1
 // (`src`).  The two slots always differ; __restrict__ lets the compiler
 // order the LDS reads against the in-flight direct-to-LDS loads without a
 // blanket wait.
-template <class C>
+template <class C, bool TR>
 __device__ __forceinline__ void refill_and_read(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                                 const Slots<C>& sl, int kfut, bool queue,
                                                 LAS unsigned char* __restrict__ dst,
                                                 const LAS unsigned char* __restrict__ src, int wave,
-                                                const int (&abase)[2], const int (&bbase)[2],
-                                                bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
+                                                const Frag<C>& f, bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
   if (queue) issue_loads<C>(Aop, Bop, sl, kfut, dst, wave);
-  read_half<C>(src, 0, abase, bbase, a, b);
+  read_half<C, TR>(src, 0, f, a, b);
 }
 
 // Scheduling pattern for a block of first-half products and second-half
@@ -209,11 +243,10 @@ __device__ __forceinline__ void interleave() {
 // PER (this wave's loads per step) is a template parameter and the steady
 // phase has a fixed number of steps in flight, so the loop body has no
 // branches and every wait count is an immediate.
-template <class C, int PER>
+template <class C, int PER, bool TR>
 __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave,
-                                          const int (&abase)[2], const int (&bbase)[2],
-                                          f32x16_t (&acc)[C::BMB][C::BNB]) {
+                                          const Frag<C>& f, f32x16_t (&acc)[C::BMB][C::BNB]) {
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
     if (st < nk) issue_loads<C>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
@@ -221,21 +254,21 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   bf16x8_t fa0[C::BMB], fb0[C::BNB], fa1[C::BMB], fb1[C::BNB];
-  read_half<C>(lds, 0, abase, bbase, fa0, fb0);
+  read_half<C, TR>(lds, 0, f, fa0, fb0);
   int kt = 0;
   // Steady phase: every step refills its slot and leaves NSTAGE-2 later
   // steps in flight.
   for (; kt < nk - C::NSTAGE; ++kt) {
     LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
     mfma_half<C>(fa0, fb0, acc);
-    read_half<C>(cur, 1, abase, bbase, fa1, fb1);
+    read_half<C, TR>(cur, 1, f, fa1, fb1);
     interleave<C>();
     MUON_WAIT_VM((C::NSTAGE - 2) * PER);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    refill_and_read<C>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur, lds + ((kt + 1) % C::NSTAGE) * C::STAGEB,
-                       wave, abase, bbase, fa0, fb0);
+    refill_and_read<C, TR>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur,
+                           lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, wave, f, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_half<C>(fa1, fb1, acc);
     __builtin_amdgcn_sched_barrier(0);
@@ -244,18 +277,18 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
   for (; kt + 1 < nk; ++kt) {
     LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
     mfma_half<C>(fa0, fb0, acc);
-    read_half<C>(cur, 1, abase, bbase, fa1, fb1);
+    read_half<C, TR>(cur, 1, f, fa1, fb1);
     interleave<C>();
     wait_newer<PER>(nk - 2 - kt);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    read_half<C>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, abase, bbase, fa0, fb0);
+    read_half<C, TR>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, f, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_half<C>(fa1, fb1, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  read_half<C>(lds + ((nk - 1) % C::NSTAGE) * C::STAGEB, 1, abase, bbase, fa1, fb1);
+  read_half<C, TR>(lds + ((nk - 1) % C::NSTAGE) * C::STAGEB, 1, f, fa1, fb1);
   mfma_half<C>(fa0, fb0, acc);
   mfma_half<C>(fa1, fb1, acc);
 }
@@ -285,8 +318,8 @@ __device__ __forceinline__ void bx_load_block(const MatDesc& d, int buf, int m_p
 //   X^T-major pass: lane (gj, 8 consecutive gi) -> the X^T pair (read and
 //     written 64 contiguous bytes per row), or W's row gj when the matrix
 //     is transposed and this is the last iteration;
-//   X-major pass: lane (gi, 8 consecutive gj) -> the row-major X_hi copy
-//     (128 contiguous bytes per row), or W's row gi on the last iteration.
+//   X-major pass (last iteration, matrix not transposed): lane (gi, 8
+//     consecutive gj) -> W's row gi (128 contiguous bytes per row).
 // A wave's LDS operations complete in order; the compiler barriers keep the
 // cross-lane exchanges through T in program order.
 template <class C>
@@ -311,7 +344,7 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
   const float ls = d.lr_scale;
   const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
   // X^T-major pass
-  const bool need_xmajor = (MODE == BXM) || !tr;
+  const bool need_xmajor = (MODE == BXL) && !tr;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int jl = p * 16 + (lane & 15);
@@ -377,12 +410,7 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
     for (int e = 0; e < 8; ++e) v[e] = T[(jl + e) * C::TP + il];
     const int gi = gi0 + il;
     const int gj = wj0 + jl;
-    if (MODE == BXM) {
-      uint32_t nh[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) nh[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
-      gst(d.x_hi + static_cast<int64_t>(gi) * n_pad + gj, make_uint4(nh[0], nh[1], nh[2], nh[3]));
-    } else if (gi < d.m) {
+    if (gi < d.m) {
       // non-transposed matrix, last iteration: W[gi][gj .. gj+7]
       float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
       if (gj + 7 < d.n && w16) {
@@ -443,13 +471,17 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     tj = ti + local;
   }
 
+  // Operands.  The Gram product reads X^T (n_pad x m_pad, the iterate's
+  // own layout): its tiles are 32 k-rows x BM columns, transposed on the
+  // way out of LDS.  The others read row-major rows of A, P and X^T.
+  constexpr bool TR = MODE == GRAM;
   const __bf16* __restrict__ Aop;
   const __bf16* __restrict__ Bop;
   int ld, K;
   if (MODE == GRAM) {
-    Aop = d.x_hi + static_cast<int64_t>(ti) * C::BM * n_pad;
-    Bop = d.x_hi + static_cast<int64_t>(tj) * C::BN * n_pad;
-    ld = n_pad;
+    Aop = d.xt_hi[buf] + static_cast<int64_t>(ti) * C::BM;
+    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * C::BN;
+    ld = m_pad;
     K = d.k_gram;
   } else if (MODE == POLY) {
     Aop = d.gram + static_cast<int64_t>(ti) * C::BM * m_pad;
@@ -464,30 +496,71 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / C::NWN, wc = wave - wr * C::NWN;
 
-  // Load slots: instruction q covers operand rows 16q..16q+15, lane l fills
-  // LDS position l%4 of row 16q + l/4 with the k-chunk the swizzle maps
-  // there.  Rows of one wave's successive slots are NW*16 apart, which
-  // leaves the swizzle unchanged, so slot i is slot 0 plus i*NW*16 rows.
   Slots<C> sl;
-  {
+  Frag<C> fr;
+  if constexpr (TR) {
+    // Stage layout of a transposed operand: 32 k-rows of NC = BM/8 16-byte
+    // chunks (8 consecutive columns each); chunk c of k-row k sits at
+    // position (c + 4 (k & 3)) mod NC, which keeps the transposing fragment
+    // reads free of bank conflicts (measured on gfx950).  Load instruction q
+    // fills positions 64q..64q+63 in order, one 16-byte chunk per lane.
+    static_assert(C::BM == 256 && C::BN == 256, "transposed operands assume 256-wide tiles");
+    constexpr int NC = C::BM / 8;
+    constexpr int RP = 2 * C::BM;
+#pragma unroll
+    for (int i = 0; i < C::QAMAX; ++i) {
+      const int p = (wave + i * C::NW) * 64 + lane;
+      const int k = p / NC;
+      const int c = (p - 4 * (k & 3)) & (NC - 1);
+      sl.aoff[i] = k * ld + c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < C::QBMAX; ++i) {
+      const int p = (wave + i * C::NW) * 64 + lane;
+      const int k = p / NC;
+      const int c = (p - 4 * (k & 3)) & (NC - 1);
+      sl.boff[i] = k * ld + c * 8;
+    }
+    sl.kmul = ld;
+    // Fragment reads: in each 16-lane group g, lane 4a + j' reads the 4
+    // columns 4a.. of k-row 8 (g >> 1) + j (j = (lane & 15) >> 2, the
+    // source-row index of the transposing read) so that output lane l gets
+    // row (l & 31) at 4 consecutive k.
+    const int g = lane >> 4, aa = lane & 3, j = (lane & 15) >> 2;
+    const int krow = 8 * (g >> 1) + j;
+#pragma unroll
+    for (int ib = 0; ib < C::BMB; ++ib) {
+      const int c = (wr * C::WM + 32 * ib + 16 * (g & 1) + 4 * aa) >> 3;
+      fr.a[ib] = krow * RP + ((c + 4 * j) & (NC - 1)) * 16 + (aa & 1) * 8;
+    }
+#pragma unroll
+    for (int jb = 0; jb < C::BNB; ++jb) {
+      const int c = (wc * C::WN + 32 * jb + 16 * (g & 1) + 4 * aa) >> 3;
+      fr.b[jb] = C::OPA + krow * RP + ((c + 4 * j) & (NC - 1)) * 16 + (aa & 1) * 8;
+    }
+  } else {
+    // Load slots: instruction q covers operand rows 16q..16q+15, lane l
+    // fills LDS position l%4 of row 16q + l/4 with the k-chunk the swizzle
+    // maps there.  Rows of one wave's successive slots are NW*16 apart,
+    // which leaves the swizzle unchanged.
     const int r0 = wave * 16 + (lane >> 2);
     const int c0 = swz(r0, lane & 3);
-    sl.a0 = r0 * ld + c0 * 8;
-    sl.b0 = sl.a0;
-    sl.astr = sl.bstr = C::NW * 16 * ld;
+#pragma unroll
+    for (int i = 0; i < C::QAMAX; ++i) sl.aoff[i] = (r0 + i * C::NW * 16) * ld + c0 * 8;
+#pragma unroll
+    for (int i = 0; i < C::QBMAX; ++i) sl.boff[i] = (r0 + i * C::NW * 16) * ld + c0 * 8;
+    sl.kmul = 1;
+    const int a_row0 = wr * C::WM + (lane & 31), b_row0 = wc * C::WN + (lane & 31);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h * 2 + (lane >> 5);
+      fr.a[h] = a_row0 * 64 + swz(a_row0, c) * 16;
+      fr.b[h] = C::OPA + b_row0 * 64 + swz(b_row0, c) * 16;
+    }
   }
   const int na = (C::QA - wave + C::NW - 1) / C::NW;
   const int nb = (C::QB - wave + C::NW - 1) / C::NW;
   const int per = na + nb;
-
-  const int a_row0 = wr * C::WM + (lane & 31), b_row0 = wc * C::WN + (lane & 31);
-  int abase[2], bbase[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = h * 2 + (lane >> 5);
-    abase[h] = a_row0 * 64 + swz(a_row0, c) * 16;
-    bbase[h] = C::OPA + b_row0 * 64 + swz(b_row0, c) * 16;
-  }
 
   f32x16_t acc[C::BMB][C::BNB];
 #pragma unroll
@@ -500,9 +573,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int nk = K / 32;
   LAS unsigned char* lds = (LAS unsigned char*)smem;
   constexpr int PER_FULL = C::QAMAX + C::QBMAX;
-  if (per == PER_FULL) main_loop<C, PER_FULL>(Aop, Bop, sl, nk, lds, wave, abase, bbase, acc);
-  else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1>(Aop, Bop, sl, nk, lds, wave, abase, bbase, acc);
-  else main_loop<C, PER_FULL - 2>(Aop, Bop, sl, nk, lds, wave, abase, bbase, acc);
+  if (per == PER_FULL) main_loop<C, PER_FULL, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+  else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+  else main_loop<C, PER_FULL - 2, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   __syncthreads();
 
   // ---- epilogue (wave-local).

@@ -11,14 +11,18 @@
 //   BX   : X' = a (X_hi + X_lo) + P X_hi    float32 epilogue, re-split into
 //                                       the bf16 pair
 //
-// Layout.  The iterate is kept twice so every product reads K-contiguous
-// rows of both operands ("NT" form), which is what an MFMA lane consumes:
+// Layout.  The iterate is kept once, as X^T (long side major):
 //   xt_hi / xt_lo : X^T as n_pad x m_pad bf16 (high part, rounding residual),
-//                   ping-pong between iterations; B operand of BX and the
+//                   ping-pong between iterations; B operand of BX, both
+//                   operands of GRAM (read transposed, see below) and the
 //                   source of the aX term;
-//   x_hi          : X_hi as m_pad x n_pad bf16; both operands of GRAM.
 //   gram, poly    : m_pad x m_pad bf16, stored in full (both triangles, bit
 //                   identical), so rows can be read as operands.
+// BX and the polynomial read K-contiguous operand rows, which is what an
+// MFMA lane consumes.  The Gram product contracts over the long side, which
+// is the row index of X^T: its stage tiles are 32 k-rows x T columns and
+// the fragments come out of LDS through the transposing ds_read_b64_tr_b16
+// (4 consecutive k of one column per read, two reads per fragment).
 // Every buffer is zero padded to multiples of the tile edge, so the main
 // loop never bounds-checks and padding stays exactly zero.
 //
@@ -40,9 +44,9 @@
 //
 // Epilogue.  An MFMA accumulator holds four consecutive rows of one column,
 // so outputs stored transposed (xt_*, and the mirror half of a symmetric
-// tile) go straight from registers as 8-byte stores; row-major outputs
-// (x_hi, the direct half of a symmetric tile) are staged through LDS one
-// band of rows at a time and written as 16-byte rows.  On diagonal tiles
+// tile) go straight from registers as 8-byte stores; the direct half of a
+// symmetric tile is staged through LDS one band of rows at a time and
+// written as 16-byte rows.  On diagonal tiles
 // each symmetric pair is written from the element with i <= j only.
 #include "muon_internal.h"
 
@@ -192,6 +196,53 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return static_cast<uint32_t>(ux) | (static_cast<uint32_t>(uy) << 16);
 }
 
+// Chunk rotation of k-row k in a transposed-operand stage.
+__device__ __forceinline__ int tr_rot(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// One step of the transposed (Gram) path: queue a future step's loads into
+// `dst` and read this step's fragments from `src` with transposing reads
+// (two 8-byte ds_read_b64_tr_b16 per fragment: k 0..3 and 4..7 of the lane's
+// 8).  The two ring slots always differ; __restrict__ lets the compiler order
+// the LDS reads against the in-flight direct-to-LDS loads without a blanket
+// wait.
+template <class C>
+__device__ __forceinline__ void step_tr(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                        const int (&g_off)[C::QMAX], int wave, int koff, bool queue,
+                                        LAS unsigned char* __restrict__ dst,
+                                        const LAS unsigned char* __restrict__ src, const int (&tra)[C::BMB],
+                                        const int (&trb)[C::BNB], bf16x8_t (&a)[C::BMB],
+                                        bf16x8_t (&b)[C::BNB]) {
+  if (queue) {
+#pragma unroll
+    for (int i = 0; i < C::QMAX; ++i) {
+      const int q = wave + i * C::NW;
+      if (i < C::QMAX - 1 || q < C::QN) {
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + koff), (LAS void*)(dst + q * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + koff),
+                                         (LAS void*)(dst + C::OPB + q * 1024), 16, 0, 0);
+      }
+    }
+  }
+  constexpr int RP = 2 * C::T;
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i) {
+    const LAS unsigned char* p = src + tra[i];
+    a[i] = __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
+                                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int j = 0; j < C::BNB; ++j) {
+    const LAS unsigned char* p = src + trb[j];
+    b[j] = __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
+                                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                               const int32_t* __restrict__ prefix,
@@ -230,10 +281,13 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const __bf16* __restrict__ Aop;
   const __bf16* __restrict__ Bop;
   int ld, K;
+  // The Gram product reads X^T (n_pad x m_pad, the iterate's own layout):
+  // its tiles are 32 k-rows x T columns, transposed on the way out of LDS.
+  constexpr bool TR = MODE == GRAM;
   if (MODE == GRAM) {
-    Aop = d.x_hi + static_cast<int64_t>(ti) * T * n_pad;
-    Bop = d.x_hi + static_cast<int64_t>(tj) * T * n_pad;
-    ld = n_pad;
+    Aop = d.xt_hi[buf] + static_cast<int64_t>(ti) * T;
+    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * T;
+    ld = m_pad;
     K = d.k_gram;
   } else if (MODE == POLY) {
     Aop = d.gram + static_cast<int64_t>(ti) * T * m_pad;
@@ -253,17 +307,32 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const int l16 = lane & 15;
   const int lq = lane >> 4;
 
-  // Direct-to-LDS load slots of this wave: instruction q covers operand rows
-  // 16q..16q+15; lane l fills LDS chunk slot (row 16q + l/4, position l%4)
-  // with the global k-chunk that the swizzle maps there.
+  // Direct-to-LDS load slots of this wave.  Row-major operands: instruction
+  // q covers operand rows 16q..16q+15; lane l fills LDS chunk slot (row
+  // 16q + l/4, position l%4) with the global k-chunk that the swizzle maps
+  // there.  Transposed operands (Gram): a stage holds 32 k-rows of NC = T/8
+  // chunks of 8 columns; chunk c of k-row k sits at position
+  // (c + 2 (k & 3) + 8 ((k >> 3) & 1)) mod NC, which keeps the transposing
+  // fragment reads free of bank conflicts (measured on gfx950), and
+  // instruction q fills positions 64q..64q+63 in order.
   int g_off[C::QMAX];
 #pragma unroll
   for (int i = 0; i < C::QMAX; ++i) {
     const int q = wave + i * C::NW;
-    const int r = q * 16 + (lane >> 2);
-    const int c = swz(r, lane & 3);   // swz is an involution on the chunk index
-    g_off[i] = r * ld + c * 8;
+    if constexpr (TR) {
+      constexpr int NC = T / 8;
+      const int p = q * 64 + lane;
+      const int k = p / NC;
+      const int c = (p % NC - tr_rot(k) + 2 * NC) % NC;
+      g_off[i] = k * ld + c * 8;
+    } else {
+      const int r = q * 16 + (lane >> 2);
+      const int c = swz(r, lane & 3);   // swz is an involution on the chunk index
+      g_off[i] = r * ld + c * 8;
+    }
   }
+  // Element distance between consecutive steps: 32 along a row, or 32 rows.
+  const int kmul = TR ? ld : 1;
   // Loads this wave issues per step (both operands).
   const int nq = (C::QN - wave + C::NW - 1) / C::NW;
 
@@ -273,9 +342,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
     for (int i = 0; i < C::QMAX; ++i) {
       const int q = wave + i * C::NW;
       if (i < C::QMAX - 1 || q < C::QN) {
-        __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + k0),
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + k0 * kmul),
                                          (LAS void*)(sb + q * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + k0),
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + k0 * kmul),
                                          (LAS void*)(sb + C::OPB + q * 1024), 16, 0, 0);
       }
     }
@@ -301,6 +370,26 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const int a_odd = lds0 + (a_row0 + 16) * C::ROWB + swz(a_row0 + 16, lq) * 16 - 1024;
   const int b_even = lds0 + C::OPB + b_row0 * C::ROWB + swz(b_row0, lq) * 16;
   const int b_odd = lds0 + C::OPB + (b_row0 + 16) * C::ROWB + swz(b_row0 + 16, lq) * 16 - 1024;
+  // Transposed (Gram) fragment addresses within a stage: in each 16-lane
+  // group g, lane 4a + j' reads columns 4a.. of k-row 8g + j (j = (lane &
+  // 15) >> 2, the source-row index of the transposing read), so output lane
+  // l gets row (l & 15) at 4 consecutive k; the second read is 4 k-rows on.
+  int tra[C::BMB], trb[C::BNB];
+  if constexpr (TR) {
+    constexpr int NC = T / 8;
+    const int aa = lane & 3, j = (lane & 15) >> 2;
+    const int krow = 8 * lq + j;
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) {
+      const int c = (wr * C::WM + 16 * i + 4 * aa) >> 3;
+      tra[i] = krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
+    }
+#pragma unroll
+    for (int jb = 0; jb < C::BNB; ++jb) {
+      const int c = (wc * C::WN + 16 * jb + 4 * aa) >> 3;
+      trb[jb] = C::OPB + krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
+    }
+  }
 
   for (int kt = 0; kt < nk; ++kt) {
     // Steps kt .. kt+NSTAGE-2 may be outstanding; wait for the oldest.
@@ -310,17 +399,30 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
     }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // keep LDS reads and refills of this step below the barrier
-    if (kt + C::NSTAGE - 1 < nk) issue((kt + C::NSTAGE - 1) * C::BK, (kt + C::NSTAGE - 1) % C::NSTAGE);
-    const int so = (kt % C::NSTAGE) * C::STAGEB;
-    i32x4_t af[C::BMB], bfr[C::BNB];
-    FragLoad<C::BMB, C::BNB>::run(af, bfr, a_even + so, a_odd + so, b_even + so, b_odd + so);
+    const int fut = kt + C::NSTAGE - 1;
+    if constexpr (TR) {
+      bf16x8_t af[C::BMB], bfr[C::BNB];
+      step_tr<C>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk,
+                 (LAS unsigned char*)smem_raw + (fut % C::NSTAGE) * C::STAGEB,
+                 (const LAS unsigned char*)smem_raw + (kt % C::NSTAGE) * C::STAGEB, tra, trb, af, bfr);
 #pragma unroll
-    for (int i = 0; i < C::BMB; ++i) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[i]);
+      for (int i = 0; i < C::BMB; ++i)
 #pragma unroll
-      for (int j = 0; j < C::BNB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bfr[j]),
-                                                            acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::BNB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    } else {
+      if (fut < nk) issue(fut * C::BK, fut % C::NSTAGE);
+      const int so = (kt % C::NSTAGE) * C::STAGEB;
+      i32x4_t af[C::BMB], bfr[C::BNB];
+      FragLoad<C::BMB, C::BNB>::run(af, bfr, a_even + so, a_odd + so, b_even + so, b_odd + so);
+#pragma unroll
+      for (int i = 0; i < C::BMB; ++i) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[i]);
+#pragma unroll
+        for (int j = 0; j < C::BNB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                              acc[i][j], 0, 0, 0);
+      }
     }
   }
   __syncthreads();
@@ -333,10 +435,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const int wi0 = ti * T + wr * C::WM;      // first global row of the wave's sub-tile
   const int wj0 = tj * T + wc * C::WN;      // first global column
   __bf16* slice = smem + wave * (C::EPIB / 2);
-  __bf16* rdst;
-  int64_t rld;
-  if (MODE == BXM) { rdst = d.x_hi; rld = n_pad; }
-  else { rdst = (MODE == POLY) ? d.poly : d.gram; rld = m_pad; }
+  // Gram / polynomial tiles also get a row-major copy (the mirror half);
+  // the BX output is only needed as the X^T pair.
+  __bf16* rdst = (MODE == POLY) ? d.poly : d.gram;
+  const int64_t rld = m_pad;
   constexpr int HALVES = C::WM / C::EPI_ROWS;
   constexpr int HB = C::EPI_ROWS / 16;      // row blocks per half
   // Global reads are issued a batch of PRE block rows at a time (they are
@@ -416,17 +518,22 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
           }
         }
         // row-major copy of the high parts into the wave's slice
-        const int rl = ib * 16 + lq * 4;
-        const int cl = j * 16 + l16;
-        const uint16_t hb[4] = {static_cast<uint16_t>(w0), static_cast<uint16_t>(w0 >> 16),
-                                static_cast<uint16_t>(w1), static_cast<uint16_t>(w1 >> 16)};
+        if (MODE != BXM) {
+          const int rl = ib * 16 + lq * 4;
+          const int cl = j * 16 + l16;
+          const uint16_t hb[4] = {static_cast<uint16_t>(w0), static_cast<uint16_t>(w0 >> 16),
+                                  static_cast<uint16_t>(w1), static_cast<uint16_t>(w1 >> 16)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::EPI_LD + cl, &hb[r], 2);
+          for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::EPI_LD + cl, &hb[r], 2);
+        }
       }
     }
   }
-    // Slice rows -> global rows, 16 bytes at a time (wave-local; the
-    // compiler orders this wave's LDS writes before its reads).
+    // Slice rows -> global rows, 16 bytes at a time.  A wave's LDS
+    // operations complete in order; the compiler barrier keeps the
+    // cross-lane exchange through the slice in program order.
+    if (MODE == BXM) continue;
+    asm volatile("" ::: "memory");
     constexpr int CPR = C::WN / 8;
     for (int c = lane; c < C::EPI_ROWS * CPR; c += 64) {
       const int rl = c / CPR;

@@ -260,7 +260,6 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.xt_hi[0] = reinterpret_cast<__bf16*>(off); off += xb;
     d.xt_lo[0] = reinterpret_cast<__bf16*>(off); off += xb;
     if (ns_steps > 0) {
-      d.x_hi = reinterpret_cast<__bf16*>(off); off += xb;
       d.xt_hi[1] = reinterpret_cast<__bf16*>(off); off += xb;
       d.xt_lo[1] = reinterpret_cast<__bf16*>(off); off += xb;
       d.gram = reinterpret_cast<__bf16*>(off); off += gb;
@@ -280,7 +279,6 @@ void bind_workspace(Plan& plan, uintptr_t base) {
   for (MatDesc& d : plan.descs) {
     d.partials = rebase(d.partials, base);
     d.sigma = rebase(d.sigma, base);
-    d.x_hi = rebase(d.x_hi, base);
     for (int b = 0; b < 2; ++b) {
       d.xt_hi[b] = rebase(d.xt_hi[b], base);
       d.xt_lo[b] = rebase(d.xt_lo[b], base);

@@ -60,7 +60,6 @@ struct MatDesc {
   float* W;          // update target (or O output in orthogonalise-only mode)
   const void* G;     // gradient (or M input in orthogonalise-only mode)
   float* B;          // momentum buffer (unused in orthogonalise-only mode)
-  __bf16* x_hi;      // X high part, m_pad x n_pad (row-major, Gram operand)
   __bf16* xt_hi[2];  // X^T high part, n_pad x m_pad, ping-pong
   __bf16* xt_lo[2];  // X^T rounding residual, n_pad x m_pad, ping-pong
   __bf16* gram;      // A, m_pad x m_pad (both triangles)
