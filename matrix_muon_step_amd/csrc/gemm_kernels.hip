@@ -29,12 +29,15 @@
 // Kernel.  One work-group owns a T x T output tile; its waves form an
 // NWM x NWN grid, each wave a (T/NWM) x (T/NWN) block of
 // v_mfma_f32_16x16x32_bf16 tiles with float32 accumulators.  K advances 32
-// per step through a ring of three LDS stages filled by direct-to-LDS
-// 16-byte loads (global_load_lds_dwordx4) issued two steps ahead, so no
-// registers stage the operands and two steps of matrix work cover the load
-// latency.  Each wave waits for its own loads (vmcnt) and a barrier makes a
-// stage visible to all.  An LDS row holds the 32 k-values of one operand row
-// as four 16-byte chunks whose positions are XOR-swizzled by the row index
+// per step through a ring of NSTAGE LDS stages filled by direct-to-LDS
+// 16-byte loads (global_load_lds_dwordx4), so no registers stage the
+// operands.  The loop is software pipelined: after a step's barrier the slot
+// just released is refilled NSTAGE steps ahead and the next step's
+// fragments are read in place, each right after its last use by this
+// step's products, so LDS reads overlap the matrix work (main_loop16).  Each
+// wave waits for its own loads (vmcnt) and a barrier makes a stage visible
+// to all.  A row-major LDS row holds the 32 k-values of one operand row as
+// four 16-byte chunks whose positions are XOR-swizzled by the row index
 // ((r >> 1) ^ (r >> 2), measured free of bank conflicts on gfx950 for these
 // fragment reads).
 //
@@ -103,77 +106,7 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >>
 #define GAS __attribute__((address_space(1)))
 #define LAS __attribute__((address_space(3)))
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// LDS fragment reads of one k-step.  They are written as one asm block that
-// ends with its own lgkmcnt wait: the compiler cannot see that the stage was
-// filled by direct-to-LDS loads, so it would otherwise guard every LDS read
-// with a wait on all outstanding loads, and no read leaves the block in
-// flight.  A fragment of rows r0 + 16 i sits at byte base + 1024 i, where
-// the base depends only on the parity of i (the chunk swizzle repeats every
-// 32 rows): ae/ao are the even/odd bases of the A operand, be/bo of B.
-#define MUON_DSR(n, b, off) "ds_read_b128 %" #n ", %[" #b "] offset:" #off "\n\t"
-template <int NA, int NB>
-struct FragLoad;
-
-template <>
-struct FragLoad<8, 4> {
-  static __device__ __forceinline__ void run(i32x4_t (&a)[8], i32x4_t (&b)[4], int ae, int ao, int be, int bo) {
-    asm volatile(MUON_DSR(0, ae, 0) MUON_DSR(1, ao, 1024) MUON_DSR(2, ae, 2048) MUON_DSR(3, ao, 3072)
-                 MUON_DSR(4, ae, 4096) MUON_DSR(5, ao, 5120) MUON_DSR(6, ae, 6144) MUON_DSR(7, ao, 7168)
-                 MUON_DSR(8, be, 0) MUON_DSR(9, bo, 1024) MUON_DSR(10, be, 2048) MUON_DSR(11, bo, 3072)
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
-                   "=&v"(a[6]), "=&v"(a[7]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-                 : [ae] "v"(ae), [ao] "v"(ao), [be] "v"(be), [bo] "v"(bo)
-                 : "memory");
-  }
-};
-
-template <>
-struct FragLoad<5, 5> {
-  static __device__ __forceinline__ void run(i32x4_t (&a)[5], i32x4_t (&b)[5], int ae, int ao, int be, int bo) {
-    asm volatile(MUON_DSR(0, ae, 0) MUON_DSR(1, ao, 1024) MUON_DSR(2, ae, 2048) MUON_DSR(3, ao, 3072)
-                 MUON_DSR(4, ae, 4096)
-                 MUON_DSR(5, be, 0) MUON_DSR(6, bo, 1024) MUON_DSR(7, be, 2048) MUON_DSR(8, bo, 3072)
-                 MUON_DSR(9, be, 4096)
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]),
-                   "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4])
-                 : [ae] "v"(ae), [ao] "v"(ao), [be] "v"(be), [bo] "v"(bo)
-                 : "memory");
-  }
-};
-
-template <>
-struct FragLoad<4, 4> {
-  static __device__ __forceinline__ void run(i32x4_t (&a)[4], i32x4_t (&b)[4], int ae, int ao, int be, int bo) {
-    asm volatile(MUON_DSR(0, ae, 0) MUON_DSR(1, ao, 1024) MUON_DSR(2, ae, 2048) MUON_DSR(3, ao, 3072)
-                 MUON_DSR(4, be, 0) MUON_DSR(5, bo, 1024) MUON_DSR(6, be, 2048) MUON_DSR(7, bo, 3072)
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
-                   "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
-                 : [ae] "v"(ae), [ao] "v"(ao), [be] "v"(be), [bo] "v"(bo)
-                 : "memory");
-  }
-};
-
-// Waits until at most `newer` steps of this wave's direct-to-LDS loads are
-// outstanding (each step issues 2*QMAX or 2*(QMAX-1) loads per wave).
-template <class C>
-__device__ __forceinline__ void wait_steps(int newer, bool full) {
-  if (full) {
-    if (newer <= 0) MUON_WAIT_VM(0);
-    else if (newer == 1) MUON_WAIT_VM(2 * C::QMAX);
-    else if (newer == 2) MUON_WAIT_VM(4 * C::QMAX);
-    else MUON_WAIT_VM(6 * C::QMAX);
-  } else {
-    if (newer <= 0) MUON_WAIT_VM(0);
-    else if (newer == 1) MUON_WAIT_VM(2 * (C::QMAX - 1));
-    else if (newer == 2) MUON_WAIT_VM(4 * (C::QMAX - 1));
-    else MUON_WAIT_VM(6 * (C::QMAX - 1));
-  }
-}
 
 __device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
   int lo = 0, hi = nmats - 1;
@@ -201,46 +134,155 @@ __device__ __forceinline__ int tr_rot(int k) { return 2 * (k & 3) + 8 * ((k >> 3
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-// One step of the transposed (Gram) path: queue a future step's loads into
-// `dst` and read this step's fragments from `src` with transposing reads
-// (two 8-byte ds_read_b64_tr_b16 per fragment: k 0..3 and 4..7 of the lane's
-// 8).  The two ring slots always differ; __restrict__ lets the compiler order
-// the LDS reads against the in-flight direct-to-LDS loads without a blanket
-// wait.
+// LDS fragment addresses of a lane (bytes within a stage), one per 16-row
+// block of the wave's A and B operands.
 template <class C>
-__device__ __forceinline__ void step_tr(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
-                                        const int (&g_off)[C::QMAX], int wave, int koff, bool queue,
-                                        LAS unsigned char* __restrict__ dst,
-                                        const LAS unsigned char* __restrict__ src, const int (&tra)[C::BMB],
-                                        const int (&trb)[C::BNB], bf16x8_t (&a)[C::BMB],
-                                        bf16x8_t (&b)[C::BNB]) {
-  if (queue) {
+struct Frag16 {
+  int a[C::BMB];
+  int b[C::BNB];
+};
+
+// Direct-to-LDS loads of one step into `dst` (both operands).
+template <class C>
+__device__ __forceinline__ void issue16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                        const int (&g_off)[C::QMAX], int wave, int koff,
+                                        LAS unsigned char* __restrict__ dst) {
 #pragma unroll
-    for (int i = 0; i < C::QMAX; ++i) {
-      const int q = wave + i * C::NW;
-      if (i < C::QMAX - 1 || q < C::QN) {
-        __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + koff), (LAS void*)(dst + q * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + koff),
-                                         (LAS void*)(dst + C::OPB + q * 1024), 16, 0, 0);
-      }
+  for (int i = 0; i < C::QMAX; ++i) {
+    const int q = wave + i * C::NW;
+    if (i < C::QMAX - 1 || q < C::QN) {
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + koff), (LAS void*)(dst + q * 1024), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + koff),
+                                       (LAS void*)(dst + C::OPB + q * 1024), 16, 0, 0);
     }
   }
-  constexpr int RP = 2 * C::T;
-#pragma unroll
-  for (int i = 0; i < C::BMB; ++i) {
-    const LAS unsigned char* p = src + tra[i];
-    a[i] = __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
+}
+
+template <class C, bool TR>
+__device__ __forceinline__ bf16x8_t frag16(const LAS unsigned char* p) {
+  if constexpr (TR) {
+    constexpr int RP = 2 * C::T;
+    return __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
                                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)),
                                    0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    return *(const LAS bf16x8_t*)p;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma16(const bf16x8_t (&a)[C::BMB], const bf16x8_t (&b)[C::BNB],
+                                       f32x4_t (&acc)[C::BMB][C::BNB]) {
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// The products of one step with the next step's fragments read in place:
+// a row block's A fragment is re-read as soon as its row of products is
+// issued, and during the last row each B fragment right after its last use,
+// so the reads overlap the matrix work with a single set of fragment
+// registers.  Optionally queues a future step's loads into `dst` first.
+// `dst` (the slot just released) and `src` (the next stage) always differ;
+// __restrict__ lets the compiler order the LDS reads against the in-flight
+// direct-to-LDS loads without a blanket wait.
+template <class C, bool TR>
+__device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                                const int (&g_off)[C::QMAX], int wave, int koff, bool queue,
+                                                LAS unsigned char* __restrict__ dst,
+                                                const LAS unsigned char* __restrict__ src, const Frag16<C>& f,
+                                                bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB],
+                                                f32x4_t (&acc)[C::BMB][C::BNB]) {
+  if (queue) issue16<C>(Aop, Bop, g_off, wave, koff, dst);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < C::BMB - 1; ++i) {
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    a[i] = frag16<C, TR>(src + f.a[i]);
+  }
+  constexpr int L = C::BMB - 1;
+#pragma unroll
+  for (int j = 0; j < C::BNB; ++j) {
+    acc[L][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[L], b[j], acc[L][j], 0, 0, 0);
+    b[j] = frag16<C, TR>(src + f.b[j]);
+  }
+  a[L] = frag16<C, TR>(src + f.a[L]);
+  // Keep that order: a row of products, then the re-read of its A fragment;
+  // in the last row one product, then one B re-read.
+  constexpr int RPF = TR ? 2 : 1;  // LDS reads per fragment
+#pragma unroll
+  for (int i = 0; i < C::BMB - 1; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, C::BNB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
   }
 #pragma unroll
   for (int j = 0; j < C::BNB; ++j) {
-    const LAS unsigned char* p = src + trb[j];
-    b[j] = __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
-                                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)),
-                                   0, 1, 2, 3, 4, 5, 6, 7);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One pipelined step kt (fragments of kt in a/b): wait for this wave's loads
+// of step kt+1 (NEWER later steps may stay in flight) and for its own reads
+// of stage kt, barrier (stage kt+1 visible to all, stage kt free), refill
+// stage kt with step kt+NSTAGE, multiply while reading step kt+1's
+// fragments.
+template <class C, int PER, bool TR>
+__device__ __forceinline__ void step16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                       const int (&g_off)[C::QMAX], int kmul, int nk, int kt, int newer,
+                                       LAS unsigned char* lds, int wave, const Frag16<C>& f,
+                                       bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB],
+                                       f32x4_t (&acc)[C::BMB][C::BNB]) {
+  if (newer >= 2) MUON_WAIT_VM(2 * PER);
+  else if (newer == 1) MUON_WAIT_VM(PER);
+  else MUON_WAIT_VM(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const int fut = kt + C::NSTAGE;
+  mfma_and_read16<C, TR>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk, lds + (kt % C::NSTAGE) * C::STAGEB,
+                         lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, f, a, b, acc);
+}
+
+// Main loop: the prologue fills every ring slot; steady steps keep
+// NSTAGE-2 later steps in flight with immediate wait counts; draining steps
+// stop refilling; the last step only multiplies.
+template <class C, int PER, bool TR>
+__device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                            const int (&g_off)[C::QMAX], int kmul, int nk,
+                                            LAS unsigned char* lds, int wave, const Frag16<C>& f,
+                                            f32x4_t (&acc)[C::BMB][C::BNB]) {
+  static_assert(C::NSTAGE >= 3 && C::NSTAGE <= 4, "wait counts assume 3 or 4 stages");
+#pragma unroll
+  for (int st = 0; st < C::NSTAGE; ++st)
+    if (st < nk) issue16<C>(Aop, Bop, g_off, wave, st * C::BK * kmul, lds + st * C::STAGEB);
+  {
+    const int newer = nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1;
+    if (newer >= 3) MUON_WAIT_VM(3 * PER);
+    else if (newer == 2) MUON_WAIT_VM(2 * PER);
+    else if (newer == 1) MUON_WAIT_VM(PER);
+    else MUON_WAIT_VM(0);
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  bf16x8_t a[C::BMB], b[C::BNB];
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i) a[i] = frag16<C, TR>(lds + f.a[i]);
+#pragma unroll
+  for (int j = 0; j < C::BNB; ++j) b[j] = frag16<C, TR>(lds + f.b[j]);
+  int kt = 0;
+  for (; kt < nk - C::NSTAGE; ++kt)
+    step16<C, PER, TR>(Aop, Bop, g_off, kmul, nk, kt, C::NSTAGE - 2, lds, wave, f, a, b, acc);
+  for (; kt + 1 < nk; ++kt)
+    step16<C, PER, TR>(Aop, Bop, g_off, kmul, nk, kt, nk - 2 - kt, lds, wave, f, a, b, acc);
+  mfma16<C>(a, b, acc);
 }
 
 template <class C, int MODE>
@@ -259,7 +301,6 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const MatDesc& d = descs[mi];
   int local = work - prefix[mi];
   const int m_pad = d.m_pad;
-  const int n_pad = d.n_pad;
 
   int ti, tj;
   if (MODE == BXM) {
@@ -336,95 +377,47 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   // Loads this wave issues per step (both operands).
   const int nq = (C::QN - wave + C::NW - 1) / C::NW;
 
-  auto issue = [&](int k0, int stage) __attribute__((always_inline)) {
-    unsigned char* sb = smem_raw + stage * C::STAGEB;
-#pragma unroll
-    for (int i = 0; i < C::QMAX; ++i) {
-      const int q = wave + i * C::NW;
-      if (i < C::QMAX - 1 || q < C::QN) {
-        __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + k0 * kmul),
-                                         (LAS void*)(sb + q * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + k0 * kmul),
-                                         (LAS void*)(sb + C::OPB + q * 1024), 16, 0, 0);
-      }
-    }
-  };
-
   f32x4_t acc[C::BMB][C::BNB];
 #pragma unroll
   for (int i = 0; i < C::BMB; ++i)
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / C::BK;
-#pragma unroll
-  for (int st = 0; st < C::NSTAGE - 1; ++st)
-    if (st < nk) issue(st * C::BK, st);
-
-  // Fragment bases (LDS byte addresses within stage 0) for even / odd row
-  // blocks of this wave; a stage adds stage * STAGEB.
-  const int a_row0 = wr * C::WM + l16;
-  const int b_row0 = wc * C::WN + l16;
-  const int lds0 = static_cast<int>(reinterpret_cast<uintptr_t>((LAS void*)smem_raw));
-  const int a_even = lds0 + a_row0 * C::ROWB + swz(a_row0, lq) * 16;
-  const int a_odd = lds0 + (a_row0 + 16) * C::ROWB + swz(a_row0 + 16, lq) * 16 - 1024;
-  const int b_even = lds0 + C::OPB + b_row0 * C::ROWB + swz(b_row0, lq) * 16;
-  const int b_odd = lds0 + C::OPB + (b_row0 + 16) * C::ROWB + swz(b_row0 + 16, lq) * 16 - 1024;
-  // Transposed (Gram) fragment addresses within a stage: in each 16-lane
-  // group g, lane 4a + j' reads columns 4a.. of k-row 8g + j (j = (lane &
-  // 15) >> 2, the source-row index of the transposing read), so output lane
-  // l gets row (l & 15) at 4 consecutive k; the second read is 4 k-rows on.
-  int tra[C::BMB], trb[C::BNB];
+  // Fragment addresses (bytes within a stage).
+  Frag16<C> fr;
   if constexpr (TR) {
+    // In each 16-lane group g, lane 4a + j' reads columns 4a.. of k-row
+    // 8g + j (j = (lane & 15) >> 2, the source-row index of the transposing
+    // read), so output lane l gets row (l & 15) at 4 consecutive k; the
+    // second read is 4 k-rows on.
     constexpr int NC = T / 8;
     const int aa = lane & 3, j = (lane & 15) >> 2;
     const int krow = 8 * lq + j;
 #pragma unroll
     for (int i = 0; i < C::BMB; ++i) {
       const int c = (wr * C::WM + 16 * i + 4 * aa) >> 3;
-      tra[i] = krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
+      fr.a[i] = krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
     }
 #pragma unroll
     for (int jb = 0; jb < C::BNB; ++jb) {
       const int c = (wc * C::WN + 16 * jb + 4 * aa) >> 3;
-      trb[jb] = C::OPB + krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
+      fr.b[jb] = C::OPB + krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
     }
+  } else {
+    // Row r of a 16-row block at r*64 + swizzled chunk; the swizzle repeats
+    // every 8 rows, so block i is block 0 plus 1024 i bytes.
+    const int a_row0 = wr * C::WM + l16;
+    const int b_row0 = wc * C::WN + l16;
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) fr.a[i] = a_row0 * C::ROWB + swz(a_row0, lq) * 16 + 1024 * i;
+#pragma unroll
+    for (int jb = 0; jb < C::BNB; ++jb) fr.b[jb] = C::OPB + b_row0 * C::ROWB + swz(b_row0, lq) * 16 + 1024 * jb;
   }
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // Steps kt .. kt+NSTAGE-2 may be outstanding; wait for the oldest.
-    {
-      const int newer = (nk - 1 - kt < C::NSTAGE - 2) ? nk - 1 - kt : C::NSTAGE - 2;
-      wait_steps<C>(newer, nq == C::QMAX);
-    }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");  // keep LDS reads and refills of this step below the barrier
-    const int fut = kt + C::NSTAGE - 1;
-    if constexpr (TR) {
-      bf16x8_t af[C::BMB], bfr[C::BNB];
-      step_tr<C>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk,
-                 (LAS unsigned char*)smem_raw + (fut % C::NSTAGE) * C::STAGEB,
-                 (const LAS unsigned char*)smem_raw + (kt % C::NSTAGE) * C::STAGEB, tra, trb, af, bfr);
-#pragma unroll
-      for (int i = 0; i < C::BMB; ++i)
-#pragma unroll
-        for (int j = 0; j < C::BNB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    } else {
-      if (fut < nk) issue(fut * C::BK, fut % C::NSTAGE);
-      const int so = (kt % C::NSTAGE) * C::STAGEB;
-      i32x4_t af[C::BMB], bfr[C::BNB];
-      FragLoad<C::BMB, C::BNB>::run(af, bfr, a_even + so, a_odd + so, b_even + so, b_odd + so);
-#pragma unroll
-      for (int i = 0; i < C::BMB; ++i) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, af[i]);
-#pragma unroll
-        for (int j = 0; j < C::BNB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bfr[j]),
-                                                              acc[i][j], 0, 0, 0);
-      }
-    }
-  }
+  const int nk = K / C::BK;
+  LAS unsigned char* lds = (LAS unsigned char*)smem_raw;
+  if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+  else main_loop16<C, 2 * (C::QMAX - 1), TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
   __syncthreads();
 
   // ---- epilogue.  16x16 accumulator layout: lane holds column (lane & 15),
