@@ -74,9 +74,11 @@ def load_traffic(kernel_files, workload):
 
 BX_KERNEL_RE = {
     # (Gram-side tile rows, long-side tile columns) -> rocprofv3 kernel-name pattern of the BX launch
-    (160, 256): r"ns_gemm32_kernel<[^<]*G32<160, 256, 1, 4>, 2>",
-    (256, 256): r"ns_gemm32_kernel<[^<]*G32<256, 256, 2, 4>, 2>",
+    (160, 256): r"ns_gemm32_kernel<[^<]*G32<160, 256, 1, 4, 3>, 2>",
+    (256, 256): r"ns_gemm32_kernel<[^<]*G32<256, 256, 2, 4, 4>, 2>",
+    (320, 256): r"ns_gemm32_kernel<[^<]*G32<320, 256, 2, 4, 4>, 2>",
 }
+BX_KERNEL_NAME = {(160, 256): "W160", (256, 256): "G256", (320, 256): "W320"}
 CALIB_RE = r"sqrt"
 
 
@@ -104,7 +106,7 @@ def record_traffic(workload, fetch_csv, write_csv, calib_bytes):
     import matrix_muon_step_amd as mm
     w = synth.WORKLOADS[workload]
     shapes = [(s.rows, s.cols) for s in w.matrices]
-    cfgs = sorted({(p["tile"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
+    cfgs = sorted({(p["bx_tile_rows"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
     assert len(cfgs) == 1 and cfgs[0] in BX_KERNEL_RE, cfgs
     pat = re.compile(BX_KERNEL_RE[cfgs[0]])
     rec = {"workload": workload, "kernel_pattern": BX_KERNEL_RE[cfgs[0]],
@@ -263,10 +265,9 @@ def main():
     bx_avg_ms = prof["bx"][0] / bx_iters if bx_iters and bx_launches else None
     bx_flops_per_launch = ns_flops(big, "bx")
     bx_tflops = bx_flops_per_launch / (bx_avg_ms * 1e-3) / 1e12 if bx_avg_ms else None
-    bx_cfgs = sorted({(p["tile"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
-    bx_kernel = {(160, 256): "W160", (256, 256): "G256"}
-    kname = "+".join(f"ns_gemm32_kernel<{bx_kernel[c]}, BX>" if c in bx_kernel else f"ns_gemm_kernel<T{c[0]}, BX>"
-                     for c in bx_cfgs)
+    bx_cfgs = sorted({(p["bx_tile_rows"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
+    kname = "+".join(f"ns_gemm32_kernel<{BX_KERNEL_NAME[c]}, BX>" if c in BX_KERNEL_NAME
+                     else f"ns_gemm_kernel<T{c[0]}, BX>" for c in bx_cfgs)
     traffic = load_traffic(TRAFFIC_SOURCES, w.name)
     n_el = w.n_params
     g_bytes = 2 if w.g_dtype == "bf16" else 4

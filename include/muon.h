@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -152,10 +152,12 @@ typedef struct muon_matrix_plan {
   int32_t m_pad;        /* padded Gram side of the iterate buffers (zeros)        */
   int32_t n_pad;        /* padded long side of the iterate buffers (zeros)        */
   int32_t tile;         /* tile edge of the symmetric products; 0 = float32 path  */
+  int32_t bx_tile_rows; /* Gram-side tile height of the BX product (0 on float32) */
   int32_t bx_tile_cols; /* long-side tile width of the BX product (0 on float32)  */
   int32_t fused_update; /* 1: the last BX launch writes W (or O) itself, from the  */
                         /* float32 accumulator; 0: a separate update pass reads   */
                         /* the final iterate pair (hi + lo)                       */
+  int32_t reserved;
   int64_t x_offset;     /* byte offset of the iterate buffers in the workspace    */
 } muon_matrix_plan_t;
 

@@ -74,8 +74,10 @@ class muon_matrix_plan_t(ctypes.Structure):
         ("m_pad", ctypes.c_int32),
         ("n_pad", ctypes.c_int32),
         ("tile", ctypes.c_int32),
+        ("bx_tile_rows", ctypes.c_int32),
         ("bx_tile_cols", ctypes.c_int32),
         ("fused_update", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("x_offset", ctypes.c_int64),
     ]
 
@@ -288,7 +290,7 @@ def muon_plan_query(shapes: Sequence[Tuple[int, int]], ns_steps=5, g_dtype=MUON_
     per = (muon_matrix_plan_t * max(1, n))()
     _check(lib().muon_plan_query(arr, n, ctypes.byref(hp), ctypes.byref(info), per))
     mats = [dict(transposed=p.transposed, m=p.m, n=p.n, m_pad=p.m_pad, n_pad=p.n_pad,
-                 tile=p.tile, bx_tile_cols=p.bx_tile_cols, fp32_path=int(p.tile == 0),
+                 tile=p.tile, bx_tile_rows=p.bx_tile_rows, bx_tile_cols=p.bx_tile_cols, fp32_path=int(p.tile == 0),
                  fused_update=p.fused_update, x_offset=p.x_offset) for p in list(per)[:n]]
     return {f: getattr(info, f) for f, _ in muon_plan_info_t._fields_ if f != "reserved"}, mats
 

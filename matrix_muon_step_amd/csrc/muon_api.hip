@@ -102,8 +102,9 @@ int64_t upper_tiles(int64_t mp, int t) {
 // Choice of kernel configurations for a Gram side m and long side n: the
 // combination with the least estimated time, i.e. padded matrix-core work
 // (upper tiles for the symmetric products) divided by each configuration's
-// sustained rate on gfx950 (measured: 32x32 wide tiles ~1.1 PF/s, 16x16
-// 160-tiles ~0.85, 128-tiles ~0.7).  MUON_GEMM_CFG=g256|w160|t160|t128|w320
+// relative sustained rate on gfx950, from measurements of these kernels:
+// 32x32 256-tiles 1.10, 320x256 BX tiles 1.04, 160x256 BX tiles 1.00,
+// 16x16 160-tiles 0.85, 128-tiles 0.70.  MUON_GEMM_CFG=g256|w160|t160|t128|w320
 // forces one combination (tuning).
 MatCfg choose_cfg(int64_t m, int64_t n) {
   struct Cand { const char* name; int sym, bx; };
@@ -111,7 +112,7 @@ MatCfg choose_cfg(int64_t m, int64_t n) {
       {"g256", kCfgG256, kCfgG256}, {"w160", kCfgT160, kCfgW160},
       {"t160", kCfgT160, kCfgT160}, {"t128", kCfgT128, kCfgT128}, {"w320", kCfgT160, kCfgW320}};
   constexpr int kCands = sizeof(cands) / sizeof(cands[0]);
-  static const double rate[kNumCfg] = {1.10, 1.00, 0.85, 0.70, 0.99};
+  static const double rate[kNumCfg] = {1.10, 1.00, 0.85, 0.70, 1.04};
   static const int forced = [] {
     const char* e = getenv("MUON_GEMM_CFG");
     if (!e) return -1;
@@ -745,6 +746,7 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
       p.m_pad = d.m_pad;
       p.n_pad = d.n_pad;
       p.tile = (d.flags & kSmall) ? 0 : kCfgRows[d.sym_cfg];
+      p.bx_tile_rows = (d.flags & kSmall) ? 0 : kCfgRows[d.bx_cfg];
       p.bx_tile_cols = (d.flags & kSmall) ? 0 : kCfgCols[d.bx_cfg];
       p.fused_update = (d.flags & kFusedUpd) ? 1 : 0;
       p.x_offset = plan.x_offset[i];

@@ -36,7 +36,7 @@ def test_stage_names_match_header():
 
 
 def test_abi_version_and_strings():
-    assert mm.muon_abi_version() == 2
+    assert mm.muon_abi_version() == 3
     assert mm.muon_status_string(0) == "MUON_OK"
     assert mm.muon_status_string(-4) == "MUON_ERR_ALIAS"
 
@@ -165,12 +165,14 @@ def test_plan_transpose_rule_and_padding():
             assert m["tile"] == 0 and m["fp32_path"] == 1 and m["m_pad"] == 64
             assert m["n_pad"] % 256 == 0 and m["n"] <= m["n_pad"] < m["n"] + 256
         else:
-            t, tc = m["tile"], m["bx_tile_cols"]
+            t, tr, tc = m["tile"], m["bx_tile_rows"], m["bx_tile_cols"]
             assert t in (128, 160, 256) and tc in (128, 160, 256) and m["fp32_path"] == 0
-            assert m["m_pad"] % t == 0 and m["m"] <= m["m_pad"] < m["m"] + t
+            assert tr in (128, 160, 256, 320)
+            assert m["m_pad"] % t == 0 and m["m_pad"] % tr == 0 and m["m"] <= m["m_pad"] < m["m"] + max(t, tr)
             assert m["n_pad"] % tc == 0 and m["n"] <= m["n_pad"] < m["n"] + tc
-    # Tile choice: exact fits are preferred (1600 = 10 x 160, 2048 = 8 x 256).
+    # Tile choice: exact fits are preferred (1600 = 10 x 160 = 5 x 320, 2048 = 8 x 256).
     assert [m["tile"] for m in mats] == [160, 160, 160, 0, 0, 0, 256, 256, 128]
+    assert [m["bx_tile_rows"] for m in mats] == [320, 320, 320, 0, 0, 0, 256, 256, 128]
 
 
 def test_plan_small_path_threshold():
@@ -187,7 +189,7 @@ def test_plan_tile_counts_and_workspace():
     shapes = [(1600, 1600)] * 4 + [(1600, 6400), (6400, 1600)]
     info, mats = mm.muon_plan_query(shapes, ns_steps=5)
     sym = sum((m["m_pad"] // m["tile"]) * (m["m_pad"] // m["tile"] + 1) // 2 for m in mats)
-    bx = sum((m["m_pad"] // m["tile"]) * (m["n_pad"] // m["bx_tile_cols"]) for m in mats)
+    bx = sum((m["m_pad"] // m["bx_tile_rows"]) * (m["n_pad"] // m["bx_tile_cols"]) for m in mats)
     assert info["gram_tiles"] == sym == info["poly_tiles"]
     assert info["bx_tiles"] == bx
     assert info["launches"] == 3 + _update_launch(mats) + 3 * 5
