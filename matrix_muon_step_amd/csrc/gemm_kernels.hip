@@ -129,8 +129,23 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return static_cast<uint32_t>(ux) | (static_cast<uint32_t>(uy) << 16);
 }
 
-// Chunk rotation of k-row k in a transposed-operand stage.
-__device__ __forceinline__ int tr_rot(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+// Position of chunk c (8 columns) within k-row k of a transposed-operand
+// stage of width T (NC = T/8 chunks per row); a bijection on each row,
+// chosen so the transposing fragment reads are free of bank conflicts at
+// every row-block offset (measured on gfx950).  320-byte rows (T = 160)
+// already fall on different banks per k-row and take an XOR inside aligned
+// groups of 4 chunks; 256-byte rows (T = 128) alias and take a rotation
+// across the row.  chunk_tr inverts pos_tr.
+template <int T>
+__device__ __forceinline__ int pos_tr(int k, int c) {
+  if constexpr (T == 160) return c ^ (((k >> 1) ^ (k >> 2)) & 3);
+  else return (c + 2 * (k & 3) + 8 * ((k >> 3) & 1)) & (T / 8 - 1);
+}
+template <int T>
+__device__ __forceinline__ int chunk_tr(int k, int p) {
+  if constexpr (T == 160) return p ^ (((k >> 1) ^ (k >> 2)) & 3);
+  else return (p - 2 * (k & 3) - 8 * ((k >> 3) & 1)) & (T / 8 - 1);
+}
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
@@ -140,6 +155,8 @@ template <class C>
 struct Frag16 {
   int a[C::BMB];
   int b[C::BNB];
+  int a1[C::BMB];  // transposed operands: address of the second read (k + 4)
+  int b1[C::BNB];
 };
 
 // Direct-to-LDS loads of one step into `dst` (both operands).
@@ -159,12 +176,13 @@ __device__ __forceinline__ void issue16(const __bf16* __restrict__ Aop, const __
   }
 }
 
+// One fragment: a 16-byte read (row-major), or two transposing 8-byte
+// reads (k 0..3 at p, k 4..7 at p1).
 template <class C, bool TR>
-__device__ __forceinline__ bf16x8_t frag16(const LAS unsigned char* p) {
+__device__ __forceinline__ bf16x8_t frag16(const LAS unsigned char* p, const LAS unsigned char* p1) {
   if constexpr (TR) {
-    constexpr int RP = 2 * C::T;
     return __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p),
-                                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)(p + 4 * RP)),
+                                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LAS bf16x4_t*)p1),
                                    0, 1, 2, 3, 4, 5, 6, 7);
   } else {
     return *(const LAS bf16x8_t*)p;
@@ -203,15 +221,15 @@ __device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, 
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    a[i] = frag16<C, TR>(src + f.a[i]);
+    a[i] = frag16<C, TR>(src + f.a[i], src + f.a1[i]);
   }
   constexpr int L = C::BMB - 1;
 #pragma unroll
   for (int j = 0; j < C::BNB; ++j) {
     acc[L][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[L], b[j], acc[L][j], 0, 0, 0);
-    b[j] = frag16<C, TR>(src + f.b[j]);
+    b[j] = frag16<C, TR>(src + f.b[j], src + f.b1[j]);
   }
-  a[L] = frag16<C, TR>(src + f.a[L]);
+  a[L] = frag16<C, TR>(src + f.a[L], src + f.a1[L]);
   // Keep that order: a row of products, then the re-read of its A fragment;
   // in the last row one product, then one B re-read.
   constexpr int RPF = TR ? 2 : 1;  // LDS reads per fragment
@@ -274,9 +292,9 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
   asm volatile("" ::: "memory");
   bf16x8_t a[C::BMB], b[C::BNB];
 #pragma unroll
-  for (int i = 0; i < C::BMB; ++i) a[i] = frag16<C, TR>(lds + f.a[i]);
+  for (int i = 0; i < C::BMB; ++i) a[i] = frag16<C, TR>(lds + f.a[i], lds + f.a1[i]);
 #pragma unroll
-  for (int j = 0; j < C::BNB; ++j) b[j] = frag16<C, TR>(lds + f.b[j]);
+  for (int j = 0; j < C::BNB; ++j) b[j] = frag16<C, TR>(lds + f.b[j], lds + f.b1[j]);
   int kt = 0;
   for (; kt < nk - C::NSTAGE; ++kt)
     step16<C, PER, TR>(Aop, Bop, g_off, kmul, nk, kt, C::NSTAGE - 2, lds, wave, f, a, b, acc);
@@ -352,10 +370,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   // q covers operand rows 16q..16q+15; lane l fills LDS chunk slot (row
   // 16q + l/4, position l%4) with the global k-chunk that the swizzle maps
   // there.  Transposed operands (Gram): a stage holds 32 k-rows of NC = T/8
-  // chunks of 8 columns; chunk c of k-row k sits at position
-  // (c + 2 (k & 3) + 8 ((k >> 3) & 1)) mod NC, which keeps the transposing
-  // fragment reads free of bank conflicts (measured on gfx950), and
-  // instruction q fills positions 64q..64q+63 in order.
+  // chunks of 8 columns; chunk c of k-row k sits at position pos_tr(k, c),
+  // and instruction q fills positions 64q..64q+63 in order.
   int g_off[C::QMAX];
 #pragma unroll
   for (int i = 0; i < C::QMAX; ++i) {
@@ -364,7 +380,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
       constexpr int NC = T / 8;
       const int p = q * 64 + lane;
       const int k = p / NC;
-      const int c = (p % NC - tr_rot(k) + 2 * NC) % NC;
+      const int c = chunk_tr<T>(k, p % NC);
       g_off[i] = k * ld + c * 8;
     } else {
       const int r = q * 16 + (lane >> 2);
@@ -396,12 +412,14 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
 #pragma unroll
     for (int i = 0; i < C::BMB; ++i) {
       const int c = (wr * C::WM + 16 * i + 4 * aa) >> 3;
-      fr.a[i] = krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
+      fr.a[i] = krow * 2 * T + pos_tr<T>(krow, c) * 16 + (aa & 1) * 8;
+      fr.a1[i] = (krow + 4) * 2 * T + pos_tr<T>(krow + 4, c) * 16 + (aa & 1) * 8;
     }
 #pragma unroll
     for (int jb = 0; jb < C::BNB; ++jb) {
       const int c = (wc * C::WN + 16 * jb + 4 * aa) >> 3;
-      fr.b[jb] = C::OPB + krow * 2 * T + ((c + tr_rot(krow)) % NC) * 16 + (aa & 1) * 8;
+      fr.b[jb] = C::OPB + krow * 2 * T + pos_tr<T>(krow, c) * 16 + (aa & 1) * 8;
+      fr.b1[jb] = C::OPB + (krow + 4) * 2 * T + pos_tr<T>(krow + 4, c) * 16 + (aa & 1) * 8;
     }
   } else {
     // Row r of a 16-row block at r*64 + swizzled chunk; the swizzle repeats
@@ -412,6 +430,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
     for (int i = 0; i < C::BMB; ++i) fr.a[i] = a_row0 * C::ROWB + swz(a_row0, lq) * 16 + 1024 * i;
 #pragma unroll
     for (int jb = 0; jb < C::BNB; ++jb) fr.b[jb] = C::OPB + b_row0 * C::ROWB + swz(b_row0, lq) * 16 + 1024 * jb;
+#pragma unroll
+    for (int i = 0; i < C::BMB; ++i) fr.a1[i] = fr.a[i];
+#pragma unroll
+    for (int jb = 0; jb < C::BNB; ++jb) fr.b1[jb] = fr.b[jb];
   }
 
   const int nk = K / C::BK;
