@@ -16,6 +16,8 @@
  *       (a, b, c) = (3.4445, -4.7750, 2.0315)
  *   O  =  X, transposed back when rows > cols
  *   W  <- W - lr * scale * O                parameter update
+ *   W  <- W - lr * (lambda * W + scale * O)  with decoupled weight decay
+ *                                            lambda (hp->weight_decay)
  *
  * Precision: G is float32 or bfloat16; W and B are float32 and updated in
  * place in float32.  For a Gram side m > 64 every matrix product of the
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -92,7 +94,12 @@ typedef struct muon_matrix {
  * eps: added to the Frobenius norm (finite, >= 0; 1e-7 is customary);
  * ns_steps: Newton-Schulz iterations, 0..MUON_MAX_NS_STEPS (5 is the usual);
  * nesterov: 0 = orthogonalise the momentum buffer, 1 = G + mu * B;
- * g_dtype: MUON_F32 or MUON_BF16. */
+ * g_dtype: MUON_F32 or MUON_BF16;
+ * weight_decay: decoupled ("AdamW-style") weight decay lambda of the
+ *   Moonlight results section of the synthesis note (finite; 0 = none):
+ *   W <- W - lr * (lambda * W + scale * O), formed as
+ *   fma(-lr*scale, O, fma(-lr*lambda, W, W)) with lr*scale and lr*lambda
+ *   rounded to float32 on the host. */
 typedef struct muon_hparams {
   float mu;
   float lr;
@@ -100,6 +107,7 @@ typedef struct muon_hparams {
   int32_t ns_steps;
   int32_t nesterov;
   int32_t g_dtype;
+  float weight_decay;
 } muon_hparams_t;
 
 #define MUON_MAX_NS_STEPS 64

@@ -50,6 +50,7 @@ class muon_hparams_t(ctypes.Structure):
         ("ns_steps", ctypes.c_int32),
         ("nesterov", ctypes.c_int32),
         ("g_dtype", ctypes.c_int32),
+        ("weight_decay", ctypes.c_float),
     ]
 
 
@@ -152,8 +153,10 @@ def _check(status: int) -> None:
         raise MuonError(status, muon_last_error())
 
 
-def hparams(mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False, g_dtype=MUON_F32) -> muon_hparams_t:
-    return muon_hparams_t(float(mu), float(lr), float(eps), int(ns_steps), int(bool(nesterov)), int(g_dtype))
+def hparams(mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False, g_dtype=MUON_F32,
+            weight_decay=0.0) -> muon_hparams_t:
+    return muon_hparams_t(float(mu), float(lr), float(eps), int(ns_steps), int(bool(nesterov)), int(g_dtype),
+                          float(weight_decay))
 
 
 def raw_matrix_array(entries: Sequence[Tuple[int, int, int, int, int, float]]):
@@ -215,10 +218,11 @@ def _alloc_workspace(nbytes: int, device):
 
 
 # ---------------------------------------------------------------- entry points
-def muon_workspace_bytes(matrices, mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False) -> int:
+def muon_workspace_bytes(matrices, mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False,
+                         weight_decay=0.0) -> int:
     entries, gd = _tensor_entries(matrices)
     arr = raw_matrix_array(entries)
-    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
     nbytes = lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp))
     if nbytes == 0 and entries:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
@@ -226,13 +230,15 @@ def muon_workspace_bytes(matrices, mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, neste
 
 
 def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
-              workspace=None, stream=None) -> None:
-    """One Muon step on a list of (W, G, B[, scale]) tensors; W, B updated in place."""
+              workspace=None, stream=None, weight_decay=0.0) -> None:
+    """One Muon step on a list of (W, G, B[, scale]) tensors; W, B updated in place.
+
+    weight_decay is the decoupled decay lambda: W <- W - lr * (lambda * W + scale * O)."""
     entries, gd = _tensor_entries(matrices)
     if not entries:
         return
     arr = raw_matrix_array(entries)
-    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
     need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())

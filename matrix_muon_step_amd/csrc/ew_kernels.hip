@@ -282,6 +282,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
   }
   __syncthreads();
   const float ls = d.lr_scale;
+  const float lwd = d.lr_wd;
   float* __restrict__ W = d.W;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -294,7 +295,12 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
       if (c >= cols) continue;
       const float o = direct ? tile[rl][cl] : tile[cl][rl];
       const int64_t e = r * cols + c;
-      gst(W + e, ortho ? o : fmaf(-ls, o, gld<float>(W + e)));
+      if (ortho) {
+        gst(W + e, o);
+      } else {
+        const float w = gld<float>(W + e);
+        gst(W + e, fmaf(-ls, o, fmaf(-lwd, w, w)));  // W - lr*wd*W - lr*scale*O
+      }
     }
   }
 }

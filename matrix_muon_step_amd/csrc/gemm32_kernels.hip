@@ -342,6 +342,7 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
   const bool tr = d.flags & kTransposed;
   const bool ortho = d.flags & kOrthoOnly;
   const float ls = d.lr_scale;
+  const float lwd = d.lr_wd;
   const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
   // X^T-major pass
   const bool need_xmajor = (MODE == BXL) && !tr;
@@ -382,14 +383,18 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
             float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
             if (!ortho) {
               const float4 w = gld<float4>(wp + 4 * h);
-              o = make_float4(fmaf(-ls, o.x, w.x), fmaf(-ls, o.y, w.y), fmaf(-ls, o.z, w.z), fmaf(-ls, o.w, w.w));
+              o = make_float4(fmaf(-ls, o.x, fmaf(-lwd, w.x, w.x)), fmaf(-ls, o.y, fmaf(-lwd, w.y, w.y)),
+                            fmaf(-ls, o.z, fmaf(-lwd, w.z, w.z)), fmaf(-ls, o.w, fmaf(-lwd, w.w, w.w)));
             }
             gst(wp + 4 * h, o);
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (gi + e < d.m) gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], gld<float>(wp + e)));
+            if (gi + e < d.m) {
+              const float w = gld<float>(wp + e);
+              gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], fmaf(-lwd, w, w)));
+            }
         }
       }
     }
@@ -419,14 +424,18 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
           float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
           if (!ortho) {
             const float4 w = gld<float4>(wp + 4 * h);
-            o = make_float4(fmaf(-ls, o.x, w.x), fmaf(-ls, o.y, w.y), fmaf(-ls, o.z, w.z), fmaf(-ls, o.w, w.w));
+            o = make_float4(fmaf(-ls, o.x, fmaf(-lwd, w.x, w.x)), fmaf(-ls, o.y, fmaf(-lwd, w.y, w.y)),
+                            fmaf(-ls, o.z, fmaf(-lwd, w.z, w.z)), fmaf(-ls, o.w, fmaf(-lwd, w.w, w.w)));
           }
           gst(wp + 4 * h, o);
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gj + e < d.n) gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], gld<float>(wp + e)));
+          if (gj + e < d.n) {
+              const float w = gld<float>(wp + e);
+              gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], fmaf(-lwd, w, w)));
+            }
       }
     }
   }

@@ -35,6 +35,7 @@ struct Item {
   float* B;
   int64_t rows, cols;
   float lr_scale;
+  float lr_wd;
   int32_t flags;
 };
 
@@ -183,8 +184,8 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     const int64_t nn = tr ? it.rows : it.cols;
     if (m > MUON_MAX_GRAM)
       return fail(MUON_ERR_UNSUPPORTED, "muon: matrix " + std::to_string(i) + " has min(rows, cols) > MUON_MAX_GRAM");
-    if (!finite(it.lr_scale))
-      return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a non-finite lr*scale");
+    if (!finite(it.lr_scale) || !finite(it.lr_wd))
+      return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a non-finite lr*scale or lr*weight_decay");
     MatDesc& d = plan.descs[i];
     memset(&d, 0, sizeof(d));
     const bool small = m <= kSmallGram;
@@ -203,6 +204,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     const bool fused = !small && ns_steps > 0 && cfg_wide(cfg.bx);
     d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0) | (fused ? kFusedUpd : 0);
     d.lr_scale = it.lr_scale;
+    d.lr_wd = it.lr_wd;
     d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
     const int64_t elems = it.rows * it.cols;
     d.mom_blocks = static_cast<int32_t>((elems + kMomChunk - 1) / kMomChunk);
@@ -540,8 +542,8 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
 
 muon_status_t check_hparams(const muon_hparams_t* hp) {
   if (!hp) return fail(MUON_ERR_INVALID_ARG, "muon: hp is NULL");
-  if (!finite(hp->mu) || !finite(hp->lr) || !finite(hp->eps) || hp->eps < 0.f)
-    return fail(MUON_ERR_INVALID_ARG, "muon: mu, lr and eps must be finite and eps >= 0");
+  if (!finite(hp->mu) || !finite(hp->lr) || !finite(hp->eps) || hp->eps < 0.f || !finite(hp->weight_decay))
+    return fail(MUON_ERR_INVALID_ARG, "muon: mu, lr, eps and weight_decay must be finite and eps >= 0");
   if (hp->ns_steps < 0 || hp->ns_steps > MUON_MAX_NS_STEPS)
     return fail(MUON_ERR_INVALID_ARG, "muon: ns_steps outside 0..MUON_MAX_NS_STEPS");
   if (hp->nesterov != 0 && hp->nesterov != 1)
@@ -576,6 +578,7 @@ muon_status_t items_from_step(const muon_matrix_t* mats, int64_t n, const muon_h
     it.rows = mt.rows;
     it.cols = mt.cols;
     it.lr_scale = hp->lr * mt.scale;
+    it.lr_wd = hp->lr * hp->weight_decay;
     it.flags = (hp->g_dtype == MUON_BF16 ? kGBf16 : 0) | (hp->nesterov ? kNesterov : 0);
   }
   return MUON_OK;
@@ -658,6 +661,7 @@ static muon_status_t ortho_items(const float* const* M, float* const* O, const i
     it.rows = rows[i];
     it.cols = cols[i];
     it.lr_scale = 0.f;
+    it.lr_wd = 0.f;
     it.flags = kOrthoOnly;
     if (check_ptrs) {
       if (!it.W || !it.G)

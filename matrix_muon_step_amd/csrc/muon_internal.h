@@ -74,6 +74,7 @@ struct MatDesc {
   int32_t flags;
   int32_t mom_blocks;  // work-groups of the momentum kernel for this matrix
   float lr_scale;      // lr * scale, formed in float32 on the host
+  float lr_wd;         // lr * weight_decay (float32), 0 in orthogonalise-only mode
   int32_t s_chunks;    // small path: column chunks (n_pad / kSmallChunk)
   int32_t sym_cfg;     // kernel configuration of the Gram / polynomial stages
   int32_t bx_cfg;      // kernel configuration of the BX stage

@@ -28,6 +28,12 @@ Readings where the page is silent (all listed again in the design notes):
 * ``scale`` is a caller-supplied per-matrix multiplier of the learning rate
   (the "consistent update RMS" adjustment of the Moonlight results section
   has no formula on the pages).
+* Weight decay: the Moonlight results section (key experiments, result 2)
+  adds decoupled weight decay in the AdamW manner, without a formula.  The
+  plain reading of "decoupled" is that the decay acts on the weights
+  directly, outside the momentum and the orthogonalisation:
+  ``W_new = W - lr * (weight_decay * W + scale * O)``, with the old W in
+  both terms.  ``weight_decay = 0`` is plain Muon.
 
 Parity pins (tests/test_oracle_pins.py) tie every function here to
 mathematics rather than to itself: the SVD closed form of the iteration,
@@ -92,15 +98,23 @@ def newton_schulz(M: np.ndarray, steps: int = 5, eps: float = 1e-7,
     return X.T.copy() if transposed else X
 
 
-def apply_update(W: np.ndarray, O: np.ndarray, lr: float, scale: float = 1.0) -> np.ndarray:
-    """Parameter update, section 4: ``W_{t+1} = W_t - lr * scale * O_t``."""
-    return np.asarray(W, dtype=np.float64) - (lr * scale) * np.asarray(O, dtype=np.float64)
+def apply_update(W: np.ndarray, O: np.ndarray, lr: float, scale: float = 1.0,
+                 weight_decay: float = 0.0) -> np.ndarray:
+    """Parameter update, section 4: ``W_{t+1} = W_t - lr * scale * O_t``.
+
+    With ``weight_decay`` (the decoupled decay of the Moonlight results,
+    key experiments result 2) the step also shrinks the old weights:
+    ``W_{t+1} = W_t - lr * (weight_decay * W_t + scale * O_t)``.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    O = np.asarray(O, dtype=np.float64)
+    return W - lr * (weight_decay * W + scale * O)
 
 
 def muon_step(W: np.ndarray, G: np.ndarray, B: np.ndarray, mu: float, lr: float,
               scale: float = 1.0, ns_steps: int = 5, nesterov: bool = False,
-              eps: float = 1e-7):
+              eps: float = 1e-7, weight_decay: float = 0.0):
     """One Muon step on one matrix.  Returns ``(W_new, B_new, O)`` in float64."""
     B_new, M = momentum(B, G, mu, nesterov)
     O = newton_schulz(M, ns_steps, eps)
-    return apply_update(W, O, lr, scale), B_new, O
+    return apply_update(W, O, lr, scale, weight_decay), B_new, O

@@ -36,7 +36,7 @@ def test_stage_names_match_header():
 
 
 def test_abi_version_and_strings():
-    assert mm.muon_abi_version() == 3
+    assert mm.muon_abi_version() == 4
     assert mm.muon_status_string(0) == "MUON_OK"
     assert mm.muon_status_string(-4) == "MUON_ERR_ALIAS"
 
@@ -108,6 +108,8 @@ def test_workspace_overlap_is_alias():
     (dict(mu=float("inf")), mm.MUON_ERR_INVALID_ARG),
     (dict(lr=float("nan")), mm.MUON_ERR_INVALID_ARG),
     (dict(g_dtype=7), mm.MUON_ERR_INVALID_ARG),
+    (dict(weight_decay=float("nan")), mm.MUON_ERR_INVALID_ARG),
+    (dict(weight_decay=float("inf")), mm.MUON_ERR_INVALID_ARG),
 ])
 def test_hparam_errors(kw, status):
     assert step([good()], hp=bd.hparams(**kw)) == status

@@ -229,3 +229,36 @@ def test_update_is_linear_in_direction():
     # First step from a zero buffer: the buffer is the gradient itself.
     assert np.array_equal(B2, G)
     assert rel(O, svd_closed_form(G, 5)) <= 1e-12
+
+
+def test_weight_decay_zero_direction_shrinks_weights():
+    # Zero gradient from a zero buffer gives a zero direction (the eps-guarded
+    # normalisation), so the decoupled decay alone acts: W <- (1 - lr * wd) W.
+    rng = np.random.default_rng(15)
+    W = rng.standard_normal((6, 9))
+    Z = np.zeros((6, 9))
+    W2, B2, O = orc.muon_step(W, Z, Z, mu=0.95, lr=0.1, weight_decay=0.3)
+    assert not O.any() and not B2.any()
+    assert rel(W2, (1.0 - 0.1 * 0.3) * W) <= 1e-15
+    # lr * wd == 1 removes the weights entirely.
+    W3, _, _ = orc.muon_step(W, Z, Z, mu=0.95, lr=0.5, weight_decay=2.0)
+    assert np.abs(W3).max() <= 1e-15
+
+
+def test_weight_decay_acts_on_old_weights_outside_direction():
+    # The decay is decoupled: it shrinks the pre-step W and leaves the
+    # orthogonalised direction untouched (the closed form through the SVD),
+    # so a decay applied after the direction step, or fed into the momentum,
+    # fails here.
+    rng = np.random.default_rng(16)
+    W = rng.standard_normal((5, 8))
+    G = rng.standard_normal((5, 8))
+    Bz = np.zeros((5, 8))
+    lr, wd, s = 0.1, 0.5, 0.75
+    W2, B2, O = orc.muon_step(W, G, Bz, mu=0.9, lr=lr, scale=s, weight_decay=wd)
+    assert np.array_equal(B2, G)
+    assert rel(O, svd_closed_form(G, 5)) <= 1e-12
+    assert rel(W2, (1.0 - lr * wd) * W - lr * s * svd_closed_form(G, 5)) <= 1e-12
+    # Without decay the step is the plain update.
+    W0, _, _ = orc.muon_step(W, G, Bz, mu=0.9, lr=lr, scale=s, weight_decay=0.0)
+    assert rel(W0, W - lr * s * svd_closed_form(G, 5)) <= 1e-12

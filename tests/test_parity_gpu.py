@@ -123,7 +123,7 @@ def test_orthogonalize_grouped_mixed_shapes(mm):
 
 
 # ------------------------------------------------------------------ full step helpers
-def run_workload(mm, w, steps=None, nesterov=False, indices=None):
+def run_workload(mm, w, steps=None, nesterov=False, indices=None, weight_decay=0.0):
     """Runs `steps` Muon steps of workload w on the GPU and the oracle."""
     steps = w.steps if steps is None else steps
     idx = list(range(len(w.matrices))) if indices is None else list(indices)
@@ -137,10 +137,11 @@ def run_workload(mm, w, steps=None, nesterov=False, indices=None):
                                    [w.wid, i, t, 0]) for i in idx]
         G = [g_tensor(g, w.g_dtype) for g in gs]
         mm.muon_step([(W[k], G[k], B[k], w.scale) for k in range(len(idx))], mu=w.mu, lr=w.lr,
-                     ns_steps=5, nesterov=nesterov)
+                     ns_steps=5, nesterov=nesterov, weight_decay=weight_decay)
         for k, g in enumerate(gs):
             g64 = synth.gradient_as_f64(g, w.g_dtype)
-            Wref[k], Bref[k], _ = orc.muon_step(Wref[k], g64, Bref[k], w.mu, w.lr, w.scale, 5, nesterov)
+            Wref[k], Bref[k], _ = orc.muon_step(Wref[k], g64, Bref[k], w.mu, w.lr, w.scale, 5, nesterov,
+                                                weight_decay=weight_decay)
     torch.cuda.synchronize()
     return host, W, B, Wref, Bref
 
@@ -190,7 +191,41 @@ def test_update_routes_fp32(mm, shape):
     _check_update_against_direction(mm, W0, G, 0.95, 0.02, 1.5)
 
 
-def _check_update_against_direction(mm, W0, G, mu, lr, scale, offset=4):
+@pytest.mark.parametrize("shape", UPDATE_SHAPES)
+def test_update_routes_weight_decay_fp32(mm, shape):
+    log_case(f"update route {shape}, weight decay 0.1")
+    r, c = shape
+    rng = np.random.default_rng([72, r, c])
+    W0 = (0.02 * rng.standard_normal((r, c))).astype(np.float32)
+    G = synth.numpy_gradient(r, c, 8, 0.1, "f32", [72, r, c, 1])
+    _check_update_against_direction(mm, W0, G, 0.95, 0.02, 1.5, weight_decay=0.1)
+
+
+@pytest.mark.parametrize("shape", [(130, 1000), (1000, 132), (2048, 512), (300, 520), (33, 17)])
+def test_weight_decay_alone_bit_exact(mm, shape):
+    """A zero gradient gives a zero direction, so the step is the decay alone.
+    With lr * weight_decay a power of two the float32 result is the single
+    rounding of W * (1 - 2^-7), which float64 holds exactly."""
+    log_case(f"weight decay alone {shape}")
+    r, c = shape
+    rng = np.random.default_rng([73, r, c])
+    W0 = rng.standard_normal((r, c)).astype(np.float32)
+    Wd = dev(W0)
+    Gd, Bd = torch.zeros_like(Wd), torch.zeros_like(Wd)
+    mm.muon_step([(Wd, Gd, Bd, 1.0)], lr=2.0 ** -4, weight_decay=2.0 ** -3, ns_steps=5)
+    torch.cuda.synchronize()
+    expect = (W0.astype(np.float64) * (1.0 - 2.0 ** -7)).astype(np.float32)
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect.view(np.uint32))
+    assert torch.count_nonzero(Bd).item() == 0
+
+
+def test_weight_decay_multi_step(mm):
+    log_case("gpt2s_fc 3 steps, weight decay 0.1")
+    w = synth.WORKLOADS["gpt2s_fc_10step"]
+    check_step_results(*run_workload(mm, w, steps=3, weight_decay=0.1), w.lr)
+
+
+def _check_update_against_direction(mm, W0, G, mu, lr, scale, offset=4, weight_decay=0.0):
     """W sits inside a larger buffer (16-byte aligned, as the ABI requires)
     with guard bands on both sides that must stay untouched."""
     r, c = W0.shape
@@ -198,11 +233,13 @@ def _check_update_against_direction(mm, W0, G, mu, lr, scale, offset=4):
     Wd = store[offset:offset + r * c].view(r, c)
     Wd.copy_(dev(W0))
     Gd, Bd = dev(G), torch.zeros(r, c, dtype=torch.float32, device="cuda")
-    mm.muon_step([(Wd, Gd, Bd, scale)], mu=mu, lr=lr, ns_steps=5)
+    mm.muon_step([(Wd, Gd, Bd, scale)], mu=mu, lr=lr, ns_steps=5, weight_decay=weight_decay)
     O = mm.muon_orthogonalize([Bd.clone()], ns_steps=5)[0]
     torch.cuda.synchronize()
     O64 = O.cpu().numpy().astype(np.float64)
-    expect = W0.astype(np.float64) - np.float64(np.float32(lr * scale)) * O64
+    W64 = W0.astype(np.float64)
+    lwd = np.float64(np.float32(np.float32(lr) * np.float32(weight_decay)))
+    expect = W64 - lwd * W64 - np.float64(np.float32(lr * scale)) * O64
     step = expect - W0
     err = np.linalg.norm(Wd.cpu().numpy() - expect) / np.linalg.norm(step)
     assert err <= FP32_TOL, err
