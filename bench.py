@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_xl_1p5b", choices=list(synth.ORDER))
     ap.add_argument("--ns-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--diag-steps", type=int, default=5,
+                    help="after the timed steps, time this many steps with the per-matrix "
+                         "diagnostics (muon_step_diag) and report their cost; 0 = skip")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -247,6 +250,33 @@ def main():
     ms_per_step = gpu_ms / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
 
+    # ---- the same step with per-matrix diagnostics (reported apart; the
+    # metric above is the plain step)
+    diag_info = None
+    if args.diag_steps > 0:
+        dbuf = torch.zeros(len(shapes), 8, dtype=torch.int32, device=dev)
+
+        def dstep():
+            mm.muon_step_diag(mats, mu=w.mu, lr=w.lr, ns_steps=args.ns_steps, workspace=ws, diag=dbuf)
+
+        dstep()
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for k in range(args.diag_steps):
+            dstep()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        d_ms = d0.elapsed_time(d1) / args.diag_steps
+        recs = mm.diag_records(dbuf, len(shapes))
+        urms = [r["update_rms"] for r in recs]
+        diag_info = {"steps": args.diag_steps, "ms_per_step": round(d_ms, 4),
+                     "overhead_ms": round(d_ms - ms_per_step, 4),
+                     "nonfinite_matrices": sum(1 for r in recs if r["nonfinite"]),
+                     "update_rms_min": min(urms), "update_rms_max": max(urms)}
+        log(f"[bench] with diagnostics: {d_ms:.3f} ms/step")
+
     # ---- per-stage figures (HIP events around every launch, same stream)
     big = [s for s in shapes if min(s) > 64]
     stage_ms = {k: v[0] / args.steps for k, v in prof.items()}
@@ -318,6 +348,7 @@ def main():
         "launches_per_step": launches,
         "elementwise": {k: (round(v, 1) if v else None) for k, v in ew.items()},
         "hbm_peak_gbps": PEAK_HBM_GBPS,
+        "diagnostics": diag_info,
     }
 
     del mats, ws

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 4
+#define MUON_ABI_VERSION 5
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -129,6 +129,40 @@ size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n, const muon_hpa
 muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-matrix diagnostics of one step: the layer-wise quantities that the
+ * practice checklist of the synthesis note asks a Muon run to record
+ * (item 4 of its local-discussion part: update RMS per matrix shape,
+ * weight RMS, norm dynamics), plus a
+ * non-finite flag.  With N = rows * cols:
+ *   momentum_norm  ||M||_F, M the Newton-Schulz input (section 4), from the
+ *                  same float32 block sums as the normalisation
+ *   direction_rms  ||O||_F / sqrt(N), O the orthogonalised direction as the
+ *                  update applies it, before lr and scale
+ *   update_rms     ||W_new - W_old||_F / sqrt(N), the step actually applied
+ *                  (decay included), each difference formed in float32
+ *   weight_rms     ||W_new||_F / sqrt(N)
+ *   nonfinite      bit 0: M holds a NaN or an infinity; bit 1: W_new does
+ * The sums of squares are accumulated in float32 per lane and in float64
+ * across lanes and work-groups, in a fixed order (repeatable bit for bit).
+ * 32 bytes per entry; reserved words are written as 0. */
+typedef struct muon_diag {
+  float momentum_norm;
+  float direction_rms;
+  float update_rms;
+  float weight_rms;
+  int32_t nonfinite;
+  int32_t reserved[3];
+} muon_diag_t;
+
+/* muon_step plus diagnostics: identical W and B results, and diag[i]
+ * (DEVICE memory, n entries, 4-byte aligned, caller-owned, disjoint from
+ * every other buffer of the call) describes matrix i once the stream
+ * reaches the end of the call.  Needs the same workspace as muon_step; one
+ * extra launch (stage MUON_STAGE_DIAG).  diag == NULL is MUON_ERR_INVALID_ARG. */
+muon_status_t muon_step_diag(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                             muon_diag_t* diag, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Orthogonalisation alone: O[i] = NS(M[i]) for float32 row-major inputs
  * M[i] (rows[i] x cols[i]) into float32 outputs O[i] of the same shape,
  * with the same normalisation, transpose rule and iteration as muon_step.
@@ -188,7 +222,8 @@ typedef enum muon_stage {
   MUON_STAGE_UPLOAD = 7,   /* descriptor table copy                    */
   MUON_STAGE_BX_UPDATE = 8, /* last X = a X + P X with W -= lr*scale*O  */
                             /* applied in the same launch (wide tiles)  */
-  MUON_STAGE_COUNT = 9
+  MUON_STAGE_DIAG = 9,      /* per-matrix diagnostics (muon_step_diag)  */
+  MUON_STAGE_COUNT = 10
 } muon_stage_t;
 
 muon_status_t muon_profile_enable(int32_t on);

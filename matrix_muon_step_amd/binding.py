@@ -27,7 +27,7 @@ MUON_BF16 = 1
 MUON_MAX_NS_STEPS = 64
 MUON_MAX_DIM = 65536
 MUON_MAX_GRAM = 16384
-STAGES = ("momentum", "norm", "prep", "gram", "poly", "bx", "update", "upload", "bx_update")
+STAGES = ("momentum", "norm", "prep", "gram", "poly", "bx", "update", "upload", "bx_update", "diag")
 MUON_STAGE_COUNT = len(STAGES)
 
 
@@ -52,6 +52,20 @@ class muon_hparams_t(ctypes.Structure):
         ("g_dtype", ctypes.c_int32),
         ("weight_decay", ctypes.c_float),
     ]
+
+
+class muon_diag_t(ctypes.Structure):
+    _fields_ = [
+        ("momentum_norm", ctypes.c_float),
+        ("direction_rms", ctypes.c_float),
+        ("update_rms", ctypes.c_float),
+        ("weight_rms", ctypes.c_float),
+        ("nonfinite", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
+    ]
+
+
+DIAG_FIELDS = ("momentum_norm", "direction_rms", "update_rms", "weight_rms", "nonfinite")
 
 
 class muon_plan_info_t(ctypes.Structure):
@@ -110,6 +124,10 @@ def lib() -> ctypes.CDLL:
                 L.muon_step.restype = ctypes.c_int
                 L.muon_step.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                L.muon_step_diag.restype = ctypes.c_int
+                L.muon_step_diag.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p]
                 L.muon_orthogonalize_workspace_bytes.restype = ctypes.c_size_t
                 L.muon_orthogonalize_workspace_bytes.argtypes = [
                     P(ctypes.c_int64), P(ctypes.c_int64), ctypes.c_int64, ctypes.c_int32]
@@ -246,6 +264,49 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
         workspace = _alloc_workspace(need, matrices[0][0].device)
     _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                            workspace.numel() * workspace.element_size(), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
+                   workspace=None, stream=None, weight_decay=0.0, diag=None):
+    """muon_step plus per-matrix diagnostics.  Returns the device buffer of
+    muon_diag_t records (int32, n x 8; `diag` may supply it); read it with
+    diag_records() after the stream is synchronised."""
+    import torch
+
+    entries, gd = _tensor_entries(matrices)
+    n = len(entries)
+    if diag is None:
+        dev = matrices[0][0].device if n else torch.device("cuda")
+        diag = torch.zeros(max(1, n), 8, dtype=torch.int32, device=dev)
+    if not diag.is_cuda or diag.dtype != torch.int32 or not diag.is_contiguous() or diag.numel() < 8 * n:
+        raise ValueError("diag must be a contiguous int32 GPU tensor of at least n x 8 entries")
+    if not entries:
+        return diag
+    arr = raw_matrix_array(entries)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
+    need = int(lib().muon_workspace_bytes(arr, n, ctypes.byref(hp)))
+    if need == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+    if workspace is None:
+        workspace = _alloc_workspace(need, matrices[0][0].device)
+    _check(lib().muon_step_diag(arr, n, ctypes.byref(hp), ctypes.c_void_p(diag.data_ptr()),
+                                ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(),
+                                ctypes.c_void_p(_stream_handle(stream))))
+    return diag
+
+
+def diag_records(diag, n=None) -> List[dict]:
+    """Decodes muon_diag_t records (an int32 n x 8 tensor or array) on the host."""
+    import numpy as np
+
+    a = diag.cpu().numpy() if hasattr(diag, "cpu") else np.asarray(diag)
+    a = np.ascontiguousarray(a, dtype=np.int32).reshape(-1, 8)
+    if n is not None:
+        a = a[:n]
+    f = a.view(np.float32)
+    return [dict(momentum_norm=float(f[i, 0]), direction_rms=float(f[i, 1]), update_rms=float(f[i, 2]),
+                 weight_rms=float(f[i, 3]), nonfinite=int(a[i, 4])) for i in range(a.shape[0])]
 
 
 def muon_orthogonalize_workspace_bytes(shapes: Sequence[Tuple[int, int]], ns_steps=5) -> int:

@@ -3,7 +3,9 @@
 //   split into the bf16 iterate pair, and the final parameter update.
 // The method's steps are those of the Muon synthesis note (papers.chlience.com),
 // section 4: momentum accumulation, Frobenius normalisation, transpose to the
-// smaller Gram side, and W <- W - lr * O.
+// smaller Gram side, and W <- W - lr * O; the optional per-matrix diagnostics
+// follow the note's practice checklist (update RMS, weight RMS, norms).
+#include "muon.h"
 #include "muon_internal.h"
 
 namespace muon {
@@ -32,6 +34,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---------------------------------------------------------------- momentum
 // B <- mu * B + G;  M = B (or G + mu * B);  partials[block] = sum of M^2 over
 // the block's 4096 elements.  Orthogonalise-only mode: M is read from G.
+// With diagnostics, mom_bad[block] = 1 if one of the block's M is NaN or
+// infinite.
 __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __restrict__ descs,
                                                             const int32_t* __restrict__ prefix,
                                                             int nmats, float mu) {
@@ -48,6 +52,7 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
   const bool nest = flags & kNesterov;
   float* __restrict__ B = d.B;
   float acc = 0.f;
+  uint32_t bad = 0;
 #pragma unroll
   for (int it = 0; it < kMomChunk / 1024; ++it) {
     const int64_t e = base + (static_cast<int64_t>(it) * 256 + threadIdx.x) * 4;
@@ -97,18 +102,28 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc = fmaf(mval[k], mval[k], acc);
+    for (int k = 0; k < 4; ++k) {
+      acc = fmaf(mval[k], mval[k], acc);
+      bad |= (__float_as_uint(mval[k]) & 0x7f800000u) == 0x7f800000u;
+    }
   }
   __shared__ float red[4];
   acc = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
+  if (flags & kDiag) {
+    // Block-uniform branch: the flag comes from the matrix descriptor.
+    const int any_bad = __syncthreads_or(bad != 0);
+    if (threadIdx.x == 0) gst(d.mom_bad + local, any_bad ? 1 : 0);
+  } else {
+    __syncthreads();
+  }
   if (threadIdx.x == 0) gst(d.partials + local, ((red[0] + red[1]) + red[2]) + red[3]);
 }
 
 // ---------------------------------------------------------------- norm
 // One work-group per matrix: fixed-order float64 sum of the block partials,
-// then sigma = 1 / (sqrt(sum) + eps).
+// then sigma = 1 / (sqrt(sum) + eps).  With diagnostics it also keeps
+// ||M||_F and the OR of the blocks' non-finite flags in mstat.
 __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ descs, float eps) {
   const MatDesc& d = descs[blockIdx.x];
   const int nb = d.mom_blocks;
@@ -122,9 +137,20 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
+  const bool diag = d.flags & kDiag;
+  int any_bad = 0;
+  if (diag) {
+    int b = 0;
+    for (int i = threadIdx.x; i < nb; i += 256) b |= gld<int32_t>(d.mom_bad + i);
+    any_bad = __syncthreads_or(b != 0);
+  }
   if (threadIdx.x == 0) {
     const double nrm = sqrt(red[0]);
     gst(d.sigma, static_cast<float>(1.0 / (nrm + static_cast<double>(eps))));
+    if (diag) {
+      gst(d.mstat, static_cast<float>(nrm));
+      gst(d.mstat + 1, __int_as_float(any_bad ? 1 : 0));
+    }
   }
 }
 
@@ -232,6 +258,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
 // ---------------------------------------------------------------- update
 // W <- W - (lr * scale) * O with O = X_hi + X_lo mapped back to rows x cols
 // (transposed when rows > cols).  Orthogonalise-only mode stores O instead.
+// DG: each wave also sums the diagnostics of the W it writes into
+// diag_part[block * 4 + wave].
+template <bool DG>
 __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__ descs,
                                                      const int32_t* __restrict__ prefix, int nmats,
                                                      int buf) {
@@ -284,6 +313,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
   const float ls = d.lr_scale;
   const float lwd = d.lr_wd;
   float* __restrict__ W = d.W;
+  DiagAcc da;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int rl = ty + 16 * k;
@@ -299,9 +329,55 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
         gst(W + e, o);
       } else {
         const float w = gld<float>(W + e);
-        gst(W + e, fmaf(-ls, o, fmaf(-lwd, w, w)));  // W - lr*wd*W - lr*scale*O
+        const float nw = fmaf(-ls, o, fmaf(-lwd, w, w));  // W - lr*wd*W - lr*scale*O
+        if constexpr (DG) diag_add(da, o, w, nw);
+        gst(W + e, nw);
       }
     }
+  }
+  if constexpr (DG) diag_flush(da, d.diag_part + local * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+// ---------------------------------------------------------------- diagnostics
+// One work-group per matrix: float64 sums of the per-wave partials in a
+// fixed order (strided per thread, then a tree), and the muon_diag_t record.
+__global__ __launch_bounds__(256) void diag_kernel(const MatDesc* __restrict__ descs,
+                                                   muon_diag_t* __restrict__ out) {
+  const MatDesc& d = descs[blockIdx.x];
+  const int ns = d.diag_slots;
+  double o2 = 0.0, d2 = 0.0, w2 = 0.0;
+  int bad = 0;
+  for (int i = threadIdx.x; i < ns; i += 256) {
+    const DiagPart p = gld<DiagPart>(d.diag_part + i);
+    o2 += static_cast<double>(p.o2);
+    d2 += static_cast<double>(p.d2);
+    w2 += static_cast<double>(p.w2);
+    bad |= p.bad;
+  }
+  __shared__ double red[3][256];
+  red[0][threadIdx.x] = o2;
+  red[1][threadIdx.x] = d2;
+  red[2][threadIdx.x] = w2;
+  const int any_bad = __syncthreads_or(bad != 0);
+#pragma unroll
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+      red[2][threadIdx.x] += red[2][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double inv = 1.0 / sqrt(static_cast<double>(d.rows) * static_cast<double>(d.cols));
+    muon_diag_t r;
+    r.momentum_norm = gld<float>(d.mstat);
+    r.direction_rms = static_cast<float>(sqrt(red[0][0]) * inv);
+    r.update_rms = static_cast<float>(sqrt(red[1][0]) * inv);
+    r.weight_rms = static_cast<float>(sqrt(red[2][0]) * inv);
+    r.nonfinite = (__float_as_int(gld<float>(d.mstat + 1)) ? 1 : 0) | (any_bad ? 2 : 0);
+    r.reserved[0] = r.reserved[1] = r.reserved[2] = 0;
+    gst(out + blockIdx.x, r);
   }
 }
 
@@ -325,8 +401,16 @@ hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int t
 }
 
 hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(update_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, buf);
+                         bool diag, hipStream_t s) {
+  if (diag)
+    hipLaunchKernelGGL(update_kernel<true>, dim3(total), dim3(256), 0, s, d, prefix, nmats, buf);
+  else
+    hipLaunchKernelGGL(update_kernel<false>, dim3(total), dim3(256), 0, s, d, prefix, nmats, buf);
+  return hipGetLastError();
+}
+
+hipError_t launch_diag(const MatDesc* d, int nmats, void* out, hipStream_t s) {
+  hipLaunchKernelGGL(diag_kernel, dim3(nmats), dim3(256), 0, s, d, static_cast<muon_diag_t*>(out));
   return hipGetLastError();
 }
 

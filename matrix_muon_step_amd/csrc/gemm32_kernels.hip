@@ -61,8 +61,9 @@ constexpr float kCoefC = 2.0315f;
 
 // BXL: the last BX of a step; instead of storing the iterate it applies the
 // parameter update W -= lr * scale * O (or stores O in orthogonalise-only
-// mode) straight from the epilogue.
-enum Mode { GRAM = 0, POLY = 1, BXM = 2, BXL = 3 };
+// mode) straight from the epilogue.  BXD: BXL that also sums the per-matrix
+// diagnostics of the W it writes (one DiagPart per wave).
+enum Mode { GRAM = 0, POLY = 1, BXM = 2, BXL = 3, BXD = 4 };
 
 template <int BM_, int BN_, int NWM_, int NWN_, int NSTAGE_>
 struct G32 {
@@ -336,16 +337,50 @@ __device__ __forceinline__ void bx_stage_acc(int lane, const f32x16_t (&acc)[C::
   asm volatile("" ::: "memory");
 }
 
+// W <- W - lr*wd*W - lr*scale*O, as fma(-ls, O, fma(-lwd, W, W)), on four
+// consecutive elements (16-byte aligned) or one; orthogonalise-only mode
+// stores O itself.
+template <bool DG>
+__device__ __forceinline__ void upd4(float* wp, float4 o, float ls, float lwd, bool ortho, DiagAcc& da) {
+  if (ortho) {
+    gst(wp, o);
+    return;
+  }
+  const float4 w = gld<float4>(wp);
+  const float4 nw = make_float4(fmaf(-ls, o.x, fmaf(-lwd, w.x, w.x)), fmaf(-ls, o.y, fmaf(-lwd, w.y, w.y)),
+                                fmaf(-ls, o.z, fmaf(-lwd, w.z, w.z)), fmaf(-ls, o.w, fmaf(-lwd, w.w, w.w)));
+  if constexpr (DG) {
+    diag_add(da, o.x, w.x, nw.x);
+    diag_add(da, o.y, w.y, nw.y);
+    diag_add(da, o.z, w.z, nw.z);
+    diag_add(da, o.w, w.w, nw.w);
+  }
+  gst(wp, nw);
+}
+template <bool DG>
+__device__ __forceinline__ void upd1(float* wp, float o, float ls, float lwd, bool ortho, DiagAcc& da) {
+  if (ortho) {
+    gst(wp, o);
+    return;
+  }
+  const float w = gld<float>(wp);
+  const float nw = fmaf(-ls, o, fmaf(-lwd, w, w));
+  if constexpr (DG) diag_add(da, o, w, nw);
+  gst(wp, nw);
+}
+
 template <class C, int MODE>
 __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int n_pad, int gi0, int wj0,
-                                            int lane, float* T, const uint4 (&hi)[4], const uint4 (&lo)[4]) {
+                                            int lane, float* T, const uint4 (&hi)[4], const uint4 (&lo)[4],
+                                            DiagAcc& da) {
+  constexpr bool DG = MODE == BXD;
   const bool tr = d.flags & kTransposed;
   const bool ortho = d.flags & kOrthoOnly;
   const float ls = d.lr_scale;
   const float lwd = d.lr_wd;
   const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
   // X^T-major pass
-  const bool need_xmajor = (MODE == BXL) && !tr;
+  const bool need_xmajor = (MODE >= BXL) && !tr;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int jl = p * 16 + (lane & 15);
@@ -379,22 +414,13 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
         float* wp = d.W + static_cast<int64_t>(gj) * d.cols + gi;
         if (gi + 7 < d.m && w16) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
-            if (!ortho) {
-              const float4 w = gld<float4>(wp + 4 * h);
-              o = make_float4(fmaf(-ls, o.x, fmaf(-lwd, w.x, w.x)), fmaf(-ls, o.y, fmaf(-lwd, w.y, w.y)),
-                            fmaf(-ls, o.z, fmaf(-lwd, w.z, w.z)), fmaf(-ls, o.w, fmaf(-lwd, w.w, w.w)));
-            }
-            gst(wp + 4 * h, o);
-          }
+          for (int h = 0; h < 2; ++h)
+            upd4<DG>(wp + 4 * h, make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]), ls, lwd,
+                     ortho, da);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (gi + e < d.m) {
-              const float w = gld<float>(wp + e);
-              gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], fmaf(-lwd, w, w)));
-            }
+            if (gi + e < d.m) upd1<DG>(wp + e, v[e], ls, lwd, ortho, da);
         }
       }
     }
@@ -420,22 +446,13 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
       float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
       if (gj + 7 < d.n && w16) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
-          if (!ortho) {
-            const float4 w = gld<float4>(wp + 4 * h);
-            o = make_float4(fmaf(-ls, o.x, fmaf(-lwd, w.x, w.x)), fmaf(-ls, o.y, fmaf(-lwd, w.y, w.y)),
-                            fmaf(-ls, o.z, fmaf(-lwd, w.z, w.z)), fmaf(-ls, o.w, fmaf(-lwd, w.w, w.w)));
-          }
-          gst(wp + 4 * h, o);
-        }
+        for (int h = 0; h < 2; ++h)
+          upd4<DG>(wp + 4 * h, make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]), ls, lwd,
+                   ortho, da);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gj + e < d.n) {
-              const float w = gld<float>(wp + e);
-              gst(wp + e, ortho ? v[e] : fmaf(-ls, v[e], fmaf(-lwd, w, w)));
-            }
+          if (gj + e < d.n) upd1<DG>(wp + e, v[e], ls, lwd, ortho, da);
       }
     }
   }
@@ -593,6 +610,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   if constexpr (MODE >= BXM) {
     float* T = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
     uint4 hi[2][4], lo[2][4];
+    DiagAcc da;
     bx_load_block<C>(d, buf, m_pad, wi0, wj0, lane, hi[0], lo[0]);
 #pragma unroll
     for (int i = 0; i < C::BMB; ++i) {
@@ -600,8 +618,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       // are free before the next block's inputs are requested.
       bx_stage_acc<C>(lane, acc[i], T);
       if (i + 1 < C::BMB) bx_load_block<C>(d, buf, m_pad, wi0 + (i + 1) * 32, wj0, lane, hi[(i + 1) & 1], lo[(i + 1) & 1]);
-      bx_epilogue<C, MODE>(d, buf, m_pad, n_pad, wi0 + i * 32, wj0, lane, T, hi[i & 1], lo[i & 1]);
+      bx_epilogue<C, MODE>(d, buf, m_pad, n_pad, wi0 + i * 32, wj0, lane, T, hi[i & 1], lo[i & 1], da);
     }
+    if constexpr (MODE == BXD) diag_flush(da, d.diag_part + local * C::NW + wave, lane);
     return;
   }
   const bool diag = ti == tj;
@@ -715,12 +734,16 @@ hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* 
     if (mode == GRAM) return launch<G256, GRAM>(d, prefix, nmats, split, buf, s);
     if (mode == POLY) return launch<G256, POLY>(d, prefix, nmats, split, buf, s);
     if (mode == BXM) return launch<G256, BXM>(d, prefix, nmats, split, buf, s);
-    return launch<G256, BXL>(d, prefix, nmats, split, buf, s);
+    if (mode == BXL) return launch<G256, BXL>(d, prefix, nmats, split, buf, s);
+    if (mode == BXD) return launch<G256, BXD>(d, prefix, nmats, split, buf, s);
+    return hipErrorInvalidValue;
   }
   if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, s);
   if (cfg == kCfgW160 && mode == BXL) return launch<W160, BXL>(d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgW160 && mode == BXD) return launch<W160, BXD>(d, prefix, nmats, split, buf, s);
   if (cfg == kCfgW320 && mode == BXM) return launch<W320, BXM>(d, prefix, nmats, split, buf, s);
   if (cfg == kCfgW320 && mode == BXL) return launch<W320, BXL>(d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgW320 && mode == BXD) return launch<W320, BXD>(d, prefix, nmats, split, buf, s);
   return hipErrorInvalidValue;
 }
 

@@ -173,6 +173,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
   plan.table_bytes = off;
 
   int64_t total_partials = 0;
+  int64_t total_slots = 0;
   for (int64_t i = 0; i < n; ++i) {
     const Item& it = items[i];
     if (it.rows < 1 || it.cols < 1)
@@ -221,6 +222,9 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
       work[tab_sym(cfg.sym)] = upper_tiles(d.m_pad, kCfgRows[cfg.sym]);
       work[tab_bx(cfg.bx)] = (d.m_pad / kCfgRows[cfg.bx]) * (d.n_pad / kCfgCols[cfg.bx]);
     }
+    // Diagnostics partials: one per wave of the kernel that writes W.
+    d.diag_slots = static_cast<int32_t>(fused ? work[tab_bx(cfg.bx)] * kCfgWaves[cfg.bx] : work[kTabUpd] * 4);
+    total_slots += d.diag_slots;
     const int64_t lim = (int64_t{1} << 31) - 1;
     for (int k = 0; k < kNumTables; ++k) {
       plan.pre[k][i] = static_cast<int32_t>(plan.tot[k]);
@@ -230,17 +234,28 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
   }
   for (int k = 0; k < kNumTables; ++k) plan.pre[k][n] = static_cast<int32_t>(plan.tot[k]);
 
-  // Partials and sigma.
+  // Partials and sigma, and the scratch of the diagnostics (always
+  // reserved, so one workspace size serves muon_step and muon_step_diag).
   const size_t partial_off = off;
   off += align_up(sizeof(float) * total_partials);
   const size_t sigma_off = off;
   off += align_up(sizeof(float) * n);
-  int64_t pcur = 0;
+  const size_t bad_off = off;
+  off += align_up(sizeof(int32_t) * total_partials);
+  const size_t mstat_off = off;
+  off += align_up(sizeof(float) * 2 * n);
+  const size_t slot_off = off;
+  off += align_up(sizeof(DiagPart) * total_slots);
+  int64_t pcur = 0, scur = 0;
   for (int64_t i = 0; i < n; ++i) {
     MatDesc& d = plan.descs[i];
     d.partials = reinterpret_cast<float*>(partial_off + sizeof(float) * pcur);
+    d.mom_bad = reinterpret_cast<int32_t*>(bad_off + sizeof(int32_t) * pcur);
     pcur += d.mom_blocks;
     d.sigma = reinterpret_cast<float*>(sigma_off + sizeof(float) * i);
+    d.mstat = reinterpret_cast<float*>(mstat_off + sizeof(float) * 2 * i);
+    d.diag_part = reinterpret_cast<DiagPart*>(slot_off + sizeof(DiagPart) * scur);
+    scur += d.diag_slots;
   }
   // Iterate and Gram buffers.
   for (int64_t i = 0; i < n; ++i) {
@@ -282,6 +297,9 @@ void bind_workspace(Plan& plan, uintptr_t base) {
   for (MatDesc& d : plan.descs) {
     d.partials = rebase(d.partials, base);
     d.sigma = rebase(d.sigma, base);
+    d.mom_bad = rebase(d.mom_bad, base);
+    d.mstat = rebase(d.mstat, base);
+    d.diag_part = rebase(d.diag_part, base);
     for (int b = 0; b < 2; ++b) {
       d.xt_hi[b] = rebase(d.xt_hi[b], base);
       d.xt_lo[b] = rebase(d.xt_lo[b], base);
@@ -467,10 +485,16 @@ muon_status_t hip_fail(hipError_t e, const char* where) {
 
 // Launch sequence of one call.  The descriptor table is uploaded into the
 // workspace, then every stage is one grouped launch over all matrices.
-muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStream_t s) {
+// With `diag_out` (a device muon_diag_t array) the W-writing kernels also
+// sum the diagnostics and a last launch reduces them.
+muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStream_t s,
+                      void* diag_out = nullptr) {
   const int n = static_cast<int>(plan.descs.size());
   const uintptr_t base = reinterpret_cast<uintptr_t>(workspace);
   bind_workspace(plan, base);
+  const bool diag = diag_out != nullptr;
+  if (diag)
+    for (MatDesc& d : plan.descs) d.flags |= kDiag;
 
   std::vector<unsigned char> table(plan.table_bytes, 0);
   memcpy(table.data(), plan.descs.data(), sizeof(MatDesc) * n);
@@ -503,13 +527,14 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
         if (plan.tot[tab] == 0) continue;
         const XcdSplit full = make_split(plan, tab, mode);
         const bool wide = cfg_wide(c);
-        const int kmode = (wide && last && mode == 2) ? 3 : mode;  // 3: BX with the update applied
+        // 3: BX with the update applied; 4: the same with diagnostics
+        const int kmode = (wide && last && mode == 2) ? (diag ? 4 : 3) : mode;
         static const int round_len[3] = {env_int("MUON_ROUND_GRAM"), env_int("MUON_ROUND_POLY"),
                                          env_int("MUON_ROUND_BX")};
         const int len = round_len[mode] > 0 ? round_len[mode] : full.max_len;
         for (int r = 0; r * len < full.max_len; ++r) {
           const XcdSplit sp = split_round(full, r, len);
-          e = run_stage(kmode == 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
+          e = run_stage(kmode >= 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
             return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, s)
                         : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
           });
@@ -534,8 +559,14 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
     buf ^= 1;
   }
   if (plan.tot[kTabUpd] > 0) {
-    e = run_stage(MUON_STAGE_UPDATE, s, [&] { return launch_update(d_desc, ptab(kTabUpd), n, ttot(kTabUpd), buf, s); });
+    e = run_stage(MUON_STAGE_UPDATE, s, [&] {
+      return launch_update(d_desc, ptab(kTabUpd), n, ttot(kTabUpd), buf, diag, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "update launch");
+  }
+  if (diag) {
+    e = run_stage(MUON_STAGE_DIAG, s, [&] { return launch_diag(d_desc, n, diag_out, s); });
+    if (e != hipSuccess) return hip_fail(e, "diagnostics launch");
   }
   return MUON_OK;
 }
@@ -617,9 +648,8 @@ size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n, const muon_hpa
   return plan.total_bytes;
 }
 
-muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+static muon_status_t step_impl(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                               muon_diag_t* diag, void* workspace, size_t workspace_bytes, void* stream) {
   std::vector<Item> items;
   muon_status_t st = items_from_step(mats, n, hp, true, items);
   if (st != MUON_OK) return st;
@@ -638,10 +668,27 @@ muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams
     rs.push_back({reinterpret_cast<uintptr_t>(items[i].G), reinterpret_cast<uintptr_t>(items[i].G) + gsz * e, false, "G", i});
   }
   rs.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + plan.total_bytes, true, "workspace", -1});
+  if (diag)
+    rs.push_back({reinterpret_cast<uintptr_t>(diag), reinterpret_cast<uintptr_t>(diag + n), true, "diag", -1});
   st = check_aliasing(rs);
   if (st != MUON_OK) return st;
   fill_ptrs(plan, items);
-  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream));
+  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream), diag);
+}
+
+muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return step_impl(mats, n, hp, nullptr, workspace, workspace_bytes, stream);
+}
+
+muon_status_t muon_step_diag(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
+                             muon_diag_t* diag, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_last_error.clear();
+  if (!diag) return fail(MUON_ERR_INVALID_ARG, "muon: diag is NULL");
+  if (reinterpret_cast<uintptr_t>(diag) & 3u) return fail(MUON_ERR_ALIGN, "muon: diag is not 4-byte aligned");
+  return step_impl(mats, n, hp, diag, workspace, workspace_bytes, stream);
 }
 
 static muon_status_t ortho_items(const float* const* M, float* const* O, const int64_t* rows,

@@ -33,6 +33,7 @@ __device__ __forceinline__ void gst(void* p, T v) {
 enum GemmCfg : int32_t { kCfgG256 = 0, kCfgW160 = 1, kCfgT160 = 2, kCfgT128 = 3, kCfgW320 = 4, kNumCfg = 5 };
 constexpr int kCfgRows[kNumCfg] = {256, 160, 160, 128, 320};   // tile rows (Gram side)
 constexpr int kCfgCols[kNumCfg] = {256, 256, 160, 128, 256};   // tile columns (long side for BX)
+constexpr int kCfgWaves[kNumCfg] = {8, 4, 4, 4, 8};            // waves per work-group
 // Configurations served by the 32x32x16 wide-tile kernels.
 constexpr bool cfg_wide(int c) { return c == kCfgG256 || c == kCfgW160 || c == kCfgW320; }
 // Tile edge of the layout kernels (normalise/transpose, update).
@@ -53,7 +54,44 @@ enum GFlags : int32_t {
   kOrthoOnly = 8,   // muon_orthogonalize: read M, write O, no momentum/update
   kSmall = 16,      // m <= kSmallGram: float32 iterate and Gram path
   kFusedUpd = 32,   // the last BX launch applies the update (no update_kernel work)
+  kDiag = 64,       // collect the per-matrix diagnostics of this call
 };
+
+// Per-wave partial sums of the diagnostics, written by the kernel that
+// writes W (fused last BX or update pass); reduced in a fixed order.
+struct DiagPart {
+  float o2;     // sum of O^2
+  float d2;     // sum of (W_new - W_old)^2
+  float w2;     // sum of W_new^2
+  int32_t bad;  // 1 if some W_new is NaN or infinite
+};
+
+// A lane's running diagnostics over the W elements it writes: float32 sums
+// of squares of O, of the applied step and of the new weights, and whether
+// a new weight is NaN or infinite (exponent field all ones).
+struct DiagAcc {
+  float o2 = 0.f, d2 = 0.f, w2 = 0.f;
+  uint32_t bad = 0;
+};
+__device__ __forceinline__ void diag_add(DiagAcc& a, float o, float w_old, float w_new) {
+  a.o2 = fmaf(o, o, a.o2);
+  const float dl = w_new - w_old;
+  a.d2 = fmaf(dl, dl, a.d2);
+  a.w2 = fmaf(w_new, w_new, a.w2);
+  a.bad |= (__float_as_uint(w_new) & 0x7f800000u) == 0x7f800000u;
+}
+// Sums a wave's accumulators (fixed butterfly order) into one DiagPart.
+__device__ __forceinline__ void diag_flush(const DiagAcc& a, DiagPart* dst, int lane) {
+  float o2 = a.o2, d2 = a.d2, w2 = a.w2;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    o2 += __shfl_xor(o2, off, 64);
+    d2 += __shfl_xor(d2, off, 64);
+    w2 += __shfl_xor(w2, off, 64);
+  }
+  const int bad = __any(a.bad != 0) ? 1 : 0;
+  if (lane == 0) gst(dst, DiagPart{o2, d2, w2, bad});
+}
 
 // One matrix of a call, as the kernels see it (lives in the workspace).
 struct MatDesc {
@@ -69,6 +107,9 @@ struct MatDesc {
   float* spoly;      // small path: P, kSmallGram x kSmallGram float32
   float* partials;   // per-block sums of squares of M
   float* sigma;      // 1 / (||M||_F + eps)
+  int32_t* mom_bad;  // diagnostics: per momentum block, 1 if M holds a non-finite value
+  float* mstat;      // diagnostics: [0] = ||M||_F, [1] = non-finite flag of M (int bits)
+  DiagPart* diag_part;  // diagnostics: per-wave partials of the W-writing kernel
   int64_t rows, cols;
   int32_t m, n, m_pad, n_pad;
   int32_t flags;
@@ -80,6 +121,7 @@ struct MatDesc {
   int32_t bx_cfg;      // kernel configuration of the BX stage
   int32_t k_gram;      // reduction length of the Gram product: n rounded up to 32
   int32_t bx_group;    // BX tile order: Gram-side tile rows per group (see gemm32)
+  int32_t diag_slots;  // entries of diag_part (work-groups x waves of the W writer)
 };
 
 // Split of one grouped GEMM launch over the 8 XCDs: work-groups are dealt
@@ -103,8 +145,12 @@ hipError_t launch_norm(const MatDesc* d, int nmats, float eps, hipStream_t s);
 hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
                        hipStream_t s);
 hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
-                         hipStream_t s);
-// Matrix-core GEMM stage (mode 0 = Gram, 1 = polynomial, 2 = BX) for the
+                         bool diag, hipStream_t s);
+// Final reduction of the diagnostics: one work-group per matrix writes out[i]
+// (a muon_diag_t array).
+hipError_t launch_diag(const MatDesc* d, int nmats, void* out, hipStream_t s);
+// Matrix-core GEMM stage (mode 0 = Gram, 1 = polynomial, 2 = BX; wide tiles
+// also 3 = last BX with the update, 4 = the same with diagnostics) for the
 // matrices whose configuration for that stage is `cfg` (16x16 kernels:
 // T160, T128; 32x32 kernels: G256, W160).
 hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,

@@ -39,7 +39,8 @@ Parity pins (tests/test_oracle_pins.py) tie every function here to
 mathematics rather than to itself: the SVD closed form of the iteration,
 transpose equivariance, singular vectors, the polynomial band, rank-one,
 partial-permutation and zero special cases, the momentum closed form and
-the update's linearity.
+the update's linearity; the diagnostics by rank-one and scaled-orthogonal
+closed forms, the decay-only step and the non-finite cases.
 """
 from __future__ import annotations
 
@@ -118,3 +119,41 @@ def muon_step(W: np.ndarray, G: np.ndarray, B: np.ndarray, mu: float, lr: float,
     B_new, M = momentum(B, G, mu, nesterov)
     O = newton_schulz(M, ns_steps, eps)
     return apply_update(W, O, lr, scale, weight_decay), B_new, O
+
+
+def diagnostics(W_old: np.ndarray, W_new: np.ndarray, M: np.ndarray, O: np.ndarray) -> dict:
+    """Per-matrix diagnostics of one step, the layer-wise quantities the
+    practice checklist of the synthesis note asks a Muon run to record
+    (item 4 of its local-discussion part: update RMS per matrix shape,
+    weight RMS, norm dynamics), each by its plain definition with
+    N = rows * cols:
+
+    * ``momentum_norm``: ``||M||_F`` of the Newton-Schulz input;
+    * ``direction_rms``: ``||O||_F / sqrt(N)``, the orthogonalised direction
+      before the learning rate and scale;
+    * ``update_rms``: ``||W_new - W_old||_F / sqrt(N)``, the step applied;
+    * ``weight_rms``: ``||W_new||_F / sqrt(N)``;
+    * ``nonfinite``: bit 0 if M holds a NaN or an infinity, bit 1 if W_new does.
+    """
+    W_old = np.asarray(W_old, dtype=np.float64)
+    W_new = np.asarray(W_new, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    O = np.asarray(O, dtype=np.float64)
+    root_n = np.sqrt(float(W_new.size))
+    return dict(
+        momentum_norm=float(np.sqrt(np.sum(M * M))),
+        direction_rms=float(np.sqrt(np.sum(O * O)) / root_n),
+        update_rms=float(np.sqrt(np.sum((W_new - W_old) ** 2)) / root_n),
+        weight_rms=float(np.sqrt(np.sum(W_new * W_new)) / root_n),
+        nonfinite=(0 if np.isfinite(M).all() else 1) | (0 if np.isfinite(W_new).all() else 2),
+    )
+
+
+def muon_step_diag(W: np.ndarray, G: np.ndarray, B: np.ndarray, mu: float, lr: float,
+                   scale: float = 1.0, ns_steps: int = 5, nesterov: bool = False,
+                   eps: float = 1e-7, weight_decay: float = 0.0):
+    """``muon_step`` plus ``diagnostics``: returns ``(W_new, B_new, O, diag)``."""
+    B_new, M = momentum(B, G, mu, nesterov)
+    O = newton_schulz(M, ns_steps, eps)
+    W_new = apply_update(W, O, lr, scale, weight_decay)
+    return W_new, B_new, O, diagnostics(W, W_new, M, O)

@@ -36,7 +36,7 @@ def test_stage_names_match_header():
 
 
 def test_abi_version_and_strings():
-    assert mm.muon_abi_version() == 4
+    assert mm.muon_abi_version() == 5
     assert mm.muon_status_string(0) == "MUON_OK"
     assert mm.muon_status_string(-4) == "MUON_ERR_ALIAS"
 

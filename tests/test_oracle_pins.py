@@ -262,3 +262,79 @@ def test_weight_decay_acts_on_old_weights_outside_direction():
     # Without decay the step is the plain update.
     W0, _, _ = orc.muon_step(W, G, Bz, mu=0.9, lr=lr, scale=s, weight_decay=0.0)
     assert rel(W0, W - lr * s * svd_closed_form(G, 5)) <= 1e-12
+
+
+# ------------------------------------------------------------------ diagnostics
+def test_diagnostics_rank_one_closed_form():
+    # M = s u v^T: ||M||_F = s, and every singular value of the normalised
+    # input is s / (s + eps), so O = p^5(s / (s + eps)) u v^T.
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal(6)
+    u /= np.linalg.norm(u)
+    v = rng.standard_normal(10)
+    v /= np.linalg.norm(v)
+    s = 3.0
+    G = s * np.outer(u, v)
+    W = np.zeros((6, 10))
+    lr, sc = 0.1, 0.5
+    W2, B2, O, dg = orc.muon_step_diag(W, G, np.zeros((6, 10)), mu=0.9, lr=lr, scale=sc)
+    q = p_iter(s / (s + EPS), 5)
+    root_n = np.sqrt(60.0)
+    assert abs(dg["momentum_norm"] - s) <= 1e-14 * s
+    assert abs(dg["direction_rms"] - q / root_n) <= 1e-12 * q / root_n
+    assert abs(dg["update_rms"] - lr * sc * q / root_n) <= 1e-12 * lr * sc * q / root_n
+    assert abs(dg["weight_rms"] - lr * sc * q / root_n) <= 1e-12 * lr * sc * q / root_n
+    assert dg["nonfinite"] == 0
+
+
+@pytest.mark.parametrize("n", [4, 9])
+def test_diagnostics_scaled_orthogonal(n):
+    # M = c Q (Q orthogonal, n x n): ||M||_F = c sqrt(n); the normalised
+    # singular values are all c / (c sqrt(n) + eps), so
+    # ||O||_F = sqrt(n) p^5(c / (c sqrt(n) + eps)) and the RMS divides by n.
+    rng = np.random.default_rng([18, n])
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    c = 0.25
+    M = c * Q
+    W = rng.standard_normal((n, n))
+    lr, wd = 0.05, 0.2
+    W2, _, O, dg = orc.muon_step_diag(W, M, np.zeros((n, n)), mu=0.5, lr=lr, weight_decay=wd)
+    q = p_iter(c / (c * np.sqrt(n) + EPS), 5)
+    assert abs(dg["momentum_norm"] - c * np.sqrt(n)) <= 1e-13
+    assert abs(dg["direction_rms"] - q / np.sqrt(n)) <= 1e-12
+    # step = -lr (wd W + O): its RMS by the same definition, with O = q Q.
+    step = lr * (wd * W + q * Q)
+    assert abs(dg["update_rms"] - np.linalg.norm(step) / n) <= 1e-12
+    assert abs(dg["weight_rms"] - np.linalg.norm(W - step) / n) <= 1e-12
+
+
+def test_diagnostics_decay_only():
+    # A zero gradient: no direction, the step is the decay alone, so the
+    # update RMS is lr * wd times the old weight RMS and the new weight RMS
+    # is (1 - lr * wd) times it.
+    rng = np.random.default_rng(19)
+    W = rng.standard_normal((7, 5))
+    Z = np.zeros((7, 5))
+    lr, wd = 0.1, 0.3
+    _, _, _, dg = orc.muon_step_diag(W, Z, Z, mu=0.95, lr=lr, weight_decay=wd)
+    rms = np.sqrt(np.mean(W * W))
+    assert dg["momentum_norm"] == 0.0 and dg["direction_rms"] == 0.0
+    assert abs(dg["update_rms"] - lr * wd * rms) <= 1e-14
+    assert abs(dg["weight_rms"] - (1 - lr * wd) * rms) <= 1e-14
+
+
+@pytest.mark.parametrize("bad,where,flags", [(np.nan, "G", 3), (np.inf, "G", 3), (-np.inf, "B", 3),
+                                             (np.nan, "W", 2)])
+def test_diagnostics_nonfinite_flags(bad, where, flags):
+    # A non-finite gradient or momentum entry makes M non-finite, and the
+    # iteration spreads it to every entry of O and so of W; a non-finite
+    # weight leaves M finite and shows up in W_new only.
+    rng = np.random.default_rng(20)
+    arrs = {k: rng.standard_normal((4, 6)) for k in ("W", "G", "B")}
+    arrs[where][1, 2] = bad
+    with np.errstate(invalid="ignore"):  # inf / inf in the normalisation
+        W2, _, _, dg = orc.muon_step_diag(arrs["W"], arrs["G"], arrs["B"], mu=0.9, lr=0.02)
+    assert dg["nonfinite"] == flags
+    _, _, _, ok = orc.muon_step_diag(rng.standard_normal((4, 6)), rng.standard_normal((4, 6)),
+                                     np.zeros((4, 6)), mu=0.9, lr=0.02)
+    assert ok["nonfinite"] == 0
