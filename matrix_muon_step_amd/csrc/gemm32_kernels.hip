@@ -79,7 +79,7 @@ struct G32 {
   static constexpr int STAGEB = OPA + OPB;
   static constexpr int NSTAGE = NSTAGE_;                  // ring of LDS stages
   static constexpr int SLICE_LD = WN + 8;                 // Gram/poly epilogue slice row stride (bf16)
-  static constexpr int TP = 36;                           // BX epilogue tile pitch (floats), see bx_epilogue
+  static constexpr int TP = 68;                           // BX epilogue tile pitch (floats), see bx_epilogue
   static constexpr int SLICEB_SYM = 32 * SLICE_LD * 2;
   static constexpr int SLICEB_BX = WN * TP * 4;
   static constexpr int SLICEB = SLICEB_SYM > SLICEB_BX ? SLICEB_SYM : SLICEB_BX;  // bytes per wave
@@ -294,35 +294,62 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
   mfma_half<C>(fa1, fb1, acc);
 }
 
-template <class C>
-__device__ __forceinline__ void bx_load_block(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
-                                              uint4 (&hi)[4], uint4 (&lo)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int gj = wj0 + p * 16 + (lane & 15);
-    const int gi = gi0 + (lane >> 4) * 8;
-    const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-    hi[p] = gld<uint4>(d.xt_hi[buf] + off);
-    lo[p] = gld<uint4>(d.xt_lo[buf] + off);
+// ---------------------------------------------------------------- BX epilogue
+// X' = a (X_hi + X_lo) + P X_hi for a wave's sub-tile (WM Gram-side rows
+// wi0.., WN = 64 long-side columns wj0..), block by block of 32 rows.
+//
+// The accumulators of a 32x32 product hold, per lane, column (lane & 31)
+// and four runs of four rows; they go to a wave-private float32 tile
+// T[jl][il] in LDS (jl: long side, 64 rows; il: Gram side, 64 columns;
+// pitch TP = 68 floats, so 16-byte accesses of 16 consecutive rows, or of
+// two rows of 8 chunks, hit all 64 banks once).  Passes over T then make
+// every global access 16 bytes per lane along contiguous memory.
+//
+// A row of X^T holds bf16 values, so 32 Gram-side columns are only half of
+// a 128-byte line.  Blocks are therefore handled in units: two blocks that
+// together cover one 64-aligned line of columns ("pair", W = 64: 8 lanes
+// read or write one whole line of each X^T array), or a block alone where
+// its neighbour belongs to another wave or tile ("single", W = 32).  With
+// WM = 160 a wave has two pairs and one single; with WM = 128, two pairs.
+//   X^T-major pass: lane (jl, 8 consecutive il) -> the X^T pair, or W's row
+//     gj when the matrix is transposed and this is the last iteration
+//     (float32: 32 columns already fill a line);
+//   X-major pass (last iteration, matrix not transposed): lane (il, 8
+//     consecutive jl) -> W's row gi (256 contiguous bytes per row).
+// A wave's LDS operations complete in order; the compiler barriers keep the
+// cross-lane exchanges through T in program order.
+
+// Inputs of one unit: the X^T pair at the unit's W Gram-side columns.
+template <int W>
+struct XPair {
+  uint4 hi[W / 8], lo[W / 8];
+};
+
+// Lane -> (row jl, first of 8 columns il) of 16-byte access p of a unit; the
+// same map addresses the X^T pair in memory and the tile T.
+template <int W>
+__device__ __forceinline__ void unit_pos(int p, int lane, int& jl, int& il) {
+  if constexpr (W == 64) {
+    jl = p * 8 + (lane >> 3);
+    il = (lane & 7) * 8;
+  } else {
+    jl = p * 16 + (lane & 15);
+    il = (lane >> 4) * 8;
   }
 }
 
-// BX epilogue of one 32-row block of a wave's sub-tile (32 Gram-side rows
-// gi0.., WN = 64 long-side columns wj0..), X' = a (X_hi + X_lo) + P X_hi.
-//
-// The accumulators (column gj per lane, four runs of four rows) have gone
-// to a wave-private float32 tile T[gj][gi] in LDS (bx_stage_acc; pitch
-// TP = 36 floats: 16-byte writes of 16 consecutive columns hit all 64 banks
-// once).  Two passes then
-// read T back so that every global access is 16 bytes per lane on
-// contiguous memory:
-//   X^T-major pass: lane (gj, 8 consecutive gi) -> the X^T pair (read and
-//     written 64 contiguous bytes per row), or W's row gj when the matrix
-//     is transposed and this is the last iteration;
-//   X-major pass (last iteration, matrix not transposed): lane (gi, 8
-//     consecutive gj) -> W's row gi (128 contiguous bytes per row).
-// A wave's LDS operations complete in order; the compiler barriers keep the
-// cross-lane exchanges through T in program order.
+// Group q (one 16-byte access per lane) of a unit's inputs.
+template <int W>
+__device__ __forceinline__ void bx_load_group(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
+                                              XPair<W>& x, int q) {
+  int jl, il;
+  unit_pos<W>(q, lane, jl, il);
+  const int64_t off = static_cast<int64_t>(wj0 + jl) * m_pad + gi0 + il;
+  x.hi[q] = gld<uint4>(d.xt_hi[buf] + off);
+  x.lo[q] = gld<uint4>(d.xt_lo[buf] + off);
+}
+
+// Accumulators of one 32-row block -> T columns co..co+31.
 template <class C>
 __device__ __forceinline__ void bx_stage_acc(int lane, const f32x16_t (&acc)[C::BNB], float* T) {
   const int col = lane & 31;
@@ -369,28 +396,36 @@ __device__ __forceinline__ void upd1(float* wp, float o, float ls, float lwd, bo
   gst(wp, nw);
 }
 
-template <class C, int MODE>
-__device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int n_pad, int gi0, int wj0,
-                                            int lane, float* T, const uint4 (&hi)[4], const uint4 (&lo)[4],
-                                            DiagAcc& da) {
+// The passes of one unit (W Gram-side columns gi0.., staged in T).  While
+// its W / 8 row groups are finished, the inputs of the next unit (W2
+// columns at gi0n; W2 = 0: none) are requested group by group, so about
+// one unit of inputs is in flight at any time.
+template <class C, int MODE, int W, int W2>
+__device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
+                                        float* T, const XPair<W>& x, DiagAcc& da, XPair<(W2 > 0 ? W2 : 32)>& nx,
+                                        int gi0n) {
   constexpr bool DG = MODE == BXD;
   const bool tr = d.flags & kTransposed;
   const bool ortho = d.flags & kOrthoOnly;
   const float ls = d.lr_scale;
   const float lwd = d.lr_wd;
   const bool w16 = (d.cols & 3) == 0;  // W rows 16-byte aligned (W itself is, per the API)
-  // X^T-major pass
   const bool need_xmajor = (MODE >= BXL) && !tr;
+  // X^T-major pass
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int jl = p * 16 + (lane & 15);
-    const int il = (lane >> 4) * 8;
+  for (int p = 0; p < W / 8; ++p) {
+    if constexpr (W2 > 0) {
+#pragma unroll
+      for (int q = p * W2 / W; q < (p + 1) * W2 / W; ++q) bx_load_group<W2>(d, buf, m_pad, gi0n, wj0, lane, nx, q);
+    }
+    int jl, il;
+    unit_pos<W>(p, lane, jl, il);
     float* tp = T + jl * C::TP + il;
     const float4 t0 = *reinterpret_cast<const float4*>(tp);
     const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
     float v[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-    const uint32_t hw[4] = {hi[p].x, hi[p].y, hi[p].z, hi[p].w};
-    const uint32_t lw[4] = {lo[p].x, lo[p].y, lo[p].z, lo[p].w};
+    const uint32_t hw[4] = {x.hi[p].x, x.hi[p].y, x.hi[p].z, x.hi[p].w};
+    const uint32_t lw[4] = {x.lo[p].x, x.lo[p].y, x.lo[p].z, x.lo[p].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v[2 * q] = fmaf(kCoefA, bf_lo(hw[q]) + bf_lo(lw[q]), v[2 * q]);
@@ -428,13 +463,16 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
       *reinterpret_cast<float4*>(tp) = make_float4(v[0], v[1], v[2], v[3]);
       *reinterpret_cast<float4*>(tp + 4) = make_float4(v[4], v[5], v[6], v[7]);
     }
+    // Keep the accesses of one row group together: hoisting every group's
+    // tile reads ahead would hold W / 8 rows of values at once.
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (!need_xmajor) return;
   asm volatile("" ::: "memory");
   // X-major pass
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int il = p * 8 + (lane & 7);
+  for (int q = 0; q < W / 8; ++q) {
+    const int il = q * 8 + (lane & 7);
     const int jl = (lane >> 3) * 8;
     float v[8];
 #pragma unroll
@@ -457,6 +495,51 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
     }
   }
   asm volatile("" ::: "memory");
+}
+
+// Unit I of a wave whose first block starts at an odd (PH = 1) or even
+// (PH = 0) multiple of 32 Gram-side rows: a pair when block I starts a
+// 64-aligned line and block I + 1 exists, else a single.
+template <class C, int PH, int I>
+struct Unit {
+  static constexpr bool pair = ((PH + I) % 2 == 0) && (I + 1 < C::BMB);
+  static constexpr int W = pair ? 64 : 32;
+  static constexpr int NEXT = I + (pair ? 2 : 1);
+};
+
+// Unit I is staged in T and its inputs are requested (or in flight): its
+// passes run while the next unit's inputs are requested, then the next
+// unit's accumulators go to T (after this unit's last read of T).
+template <class C, int MODE, int PH, int I>
+__device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
+                                         const f32x16_t (&acc)[C::BMB][C::BNB],
+                                         const XPair<Unit<C, PH, I>::W>& cur, DiagAcc& da) {
+  using U = Unit<C, PH, I>;
+  if constexpr (U::NEXT < C::BMB) {
+    using N = Unit<C, PH, U::NEXT>;
+    XPair<N::W> nxt;
+    bx_pass<C, MODE, U::W, N::W>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, da, nxt, wi0 + 32 * U::NEXT);
+    bx_stage_acc<C>(lane, acc[U::NEXT], T);
+    if constexpr (N::pair) bx_stage_acc<C>(lane, acc[U::NEXT + 1], T + 32);
+    bx_units<C, MODE, PH, U::NEXT>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da);
+  } else {
+    XPair<32> none;
+    bx_pass<C, MODE, U::W, 0>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, da, none, 0);
+  }
+}
+
+// The epilogue of a wave: the first unit's accumulators go to T (freeing
+// their registers), its inputs are requested, then the units run in turn.
+template <class C, int MODE, int PH>
+__device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
+                                            const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da) {
+  using U = Unit<C, PH, 0>;
+  bx_stage_acc<C>(lane, acc[0], T);
+  if constexpr (U::pair) bx_stage_acc<C>(lane, acc[1], T + 32);
+  XPair<U::W> x0;
+#pragma unroll
+  for (int q = 0; q < U::W / 8; ++q) bx_load_group<U::W>(d, buf, m_pad, wi0, wj0, lane, x0, q);
+  bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da);
 }
 
 template <class C, int MODE>
@@ -609,17 +692,12 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int wj0 = tj * C::BN + wc * C::WN;   // first global column
   if constexpr (MODE >= BXM) {
     float* T = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
-    uint4 hi[2][4], lo[2][4];
     DiagAcc da;
-    bx_load_block<C>(d, buf, m_pad, wi0, wj0, lane, hi[0], lo[0]);
-#pragma unroll
-    for (int i = 0; i < C::BMB; ++i) {
-      // Block i's accumulators go to the LDS tile first, so their registers
-      // are free before the next block's inputs are requested.
-      bx_stage_acc<C>(lane, acc[i], T);
-      if (i + 1 < C::BMB) bx_load_block<C>(d, buf, m_pad, wi0 + (i + 1) * 32, wj0, lane, hi[(i + 1) & 1], lo[(i + 1) & 1]);
-      bx_epilogue<C, MODE>(d, buf, m_pad, n_pad, wi0 + i * 32, wj0, lane, T, hi[i & 1], lo[i & 1], da);
-    }
+    // Wave-uniform: whether the wave's first block starts a 64-row line.
+    if (((wi0 >> 5) & 1) == 0)
+      bx_epilogue<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, da);
+    else
+      bx_epilogue<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, da);
     if constexpr (MODE == BXD) diag_flush(da, d.diag_part + local * C::NW + wave, lane);
     return;
   }
