@@ -319,14 +319,15 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
 // A wave's LDS operations complete in order; the compiler barriers keep the
 // cross-lane exchanges through T in program order.
 
-// Inputs of one unit: the X^T pair at the unit's W Gram-side columns.
-template <int W>
-struct XPair {
-  uint4 hi[W / 8], lo[W / 8];
+// Inputs of a unit: NG row groups (one 16-byte access of each X^T array
+// per lane and group).
+template <int NG>
+struct XIn {
+  uint4 hi[NG], lo[NG];
 };
 
-// Lane -> (row jl, first of 8 columns il) of 16-byte access p of a unit; the
-// same map addresses the X^T pair in memory and the tile T.
+// Lane -> (row jl, first of 8 columns il) of 16-byte access p of a unit of
+// W columns; the same map addresses the X^T pair in memory and the tile T.
 template <int W>
 __device__ __forceinline__ void unit_pos(int p, int lane, int& jl, int& il) {
   if constexpr (W == 64) {
@@ -338,12 +339,12 @@ __device__ __forceinline__ void unit_pos(int p, int lane, int& jl, int& il) {
   }
 }
 
-// Group q (one 16-byte access per lane) of a unit's inputs.
-template <int W>
+// Row group p0 + q of a W-column unit at Gram-side column gi0 -> x[q].
+template <int W, int NG>
 __device__ __forceinline__ void bx_load_group(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
-                                              XPair<W>& x, int q) {
+                                              XIn<NG>& x, int q, int p0) {
   int jl, il;
-  unit_pos<W>(q, lane, jl, il);
+  unit_pos<W>(p0 + q, lane, jl, il);
   const int64_t off = static_cast<int64_t>(wj0 + jl) * m_pad + gi0 + il;
   x.hi[q] = gld<uint4>(d.xt_hi[buf] + off);
   x.lo[q] = gld<uint4>(d.xt_lo[buf] + off);
@@ -396,14 +397,16 @@ __device__ __forceinline__ void upd1(float* wp, float o, float ls, float lwd, bo
   gst(wp, nw);
 }
 
-// The passes of one unit (W Gram-side columns gi0.., staged in T).  While
-// its W / 8 row groups are finished, the inputs of the next unit (W2
-// columns at gi0n; W2 = 0: none) are requested group by group, so about
-// one unit of inputs is in flight at any time.
-template <class C, int MODE, int W, int W2>
+// The passes over row groups p0 .. p0 + NG - 1 of a unit of W Gram-side
+// columns gi0.. staged in T (all of the unit, or one wave's half of a
+// merged unit).  While they are finished, the inputs of the next unit (NG2
+// groups of a W2-column unit at gi0n from group p0n; NG2 = 0: none) are
+// requested group by group, so about one unit of inputs is in flight at
+// any time.  The X-major pass covers Gram-side columns 8 q0 .. 8 (q0 + NG).
+template <class C, int MODE, int W, int NG, int W2, int NG2, bool MERGED>
 __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
-                                        float* T, const XPair<W>& x, DiagAcc& da, XPair<(W2 > 0 ? W2 : 32)>& nx,
-                                        int gi0n) {
+                                        float* T, const XIn<NG>& x, int p0, int q0, DiagAcc& da,
+                                        XIn<(NG2 > 0 ? NG2 : 1)>& nx, int gi0n, int p0n) {
   constexpr bool DG = MODE == BXD;
   const bool tr = d.flags & kTransposed;
   const bool ortho = d.flags & kOrthoOnly;
@@ -413,13 +416,14 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
   const bool need_xmajor = (MODE >= BXL) && !tr;
   // X^T-major pass
 #pragma unroll
-  for (int p = 0; p < W / 8; ++p) {
-    if constexpr (W2 > 0) {
+  for (int p = 0; p < NG; ++p) {
+    if constexpr (NG2 > 0) {
 #pragma unroll
-      for (int q = p * W2 / W; q < (p + 1) * W2 / W; ++q) bx_load_group<W2>(d, buf, m_pad, gi0n, wj0, lane, nx, q);
+      for (int q = p * NG2 / NG; q < (p + 1) * NG2 / NG; ++q)
+        bx_load_group<W2>(d, buf, m_pad, gi0n, wj0, lane, nx, q, p0n);
     }
     int jl, il;
-    unit_pos<W>(p, lane, jl, il);
+    unit_pos<W>(p0 + p, lane, jl, il);
     float* tp = T + jl * C::TP + il;
     const float4 t0 = *reinterpret_cast<const float4*>(tp);
     const float4 t1 = *reinterpret_cast<const float4*>(tp + 4);
@@ -468,11 +472,14 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
     __builtin_amdgcn_sched_barrier(0);
   }
   if (!need_xmajor) return;
+  // The X-major pass reads rows of T that the other wave of a merged unit
+  // wrote back (uniform over the work-group: one matrix per tile).
+  if constexpr (MERGED) __syncthreads();
   asm volatile("" ::: "memory");
   // X-major pass
 #pragma unroll
-  for (int q = 0; q < W / 8; ++q) {
-    const int il = q * 8 + (lane & 7);
+  for (int q = 0; q < NG; ++q) {
+    const int il = (q0 + q) * 8 + (lane & 7);
     const int jl = (lane >> 3) * 8;
     float v[8];
 #pragma unroll
@@ -513,33 +520,70 @@ struct Unit {
 template <class C, int MODE, int PH, int I>
 __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
                                          const f32x16_t (&acc)[C::BMB][C::BNB],
-                                         const XPair<Unit<C, PH, I>::W>& cur, DiagAcc& da) {
+                                         const XIn<Unit<C, PH, I>::W / 8>& cur, DiagAcc& da) {
   using U = Unit<C, PH, I>;
   if constexpr (U::NEXT < C::BMB) {
     using N = Unit<C, PH, U::NEXT>;
-    XPair<N::W> nxt;
-    bx_pass<C, MODE, U::W, N::W>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, da, nxt, wi0 + 32 * U::NEXT);
+    XIn<N::W / 8> nxt;
+    bx_pass<C, MODE, U::W, U::W / 8, N::W, N::W / 8, false>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, 0, 0, da,
+                                                            nxt, wi0 + 32 * U::NEXT, 0);
     bx_stage_acc<C>(lane, acc[U::NEXT], T);
     if constexpr (N::pair) bx_stage_acc<C>(lane, acc[U::NEXT + 1], T + 32);
     bx_units<C, MODE, PH, U::NEXT>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da);
   } else {
-    XPair<32> none;
-    bx_pass<C, MODE, U::W, 0>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, da, none, 0);
+    XIn<1> none;
+    bx_pass<C, MODE, U::W, U::W / 8, 32, 0, false>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, 0, 0, da, none,
+                                                   0, 0);
   }
 }
 
-// The epilogue of a wave: the first unit's accumulators go to T (freeing
-// their registers), its inputs are requested, then the units run in turn.
+// The epilogue of a wave that handles its blocks alone: the first unit's
+// accumulators go to T (freeing their registers), its inputs are
+// requested, then the units run in turn.
 template <class C, int MODE, int PH>
 __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
                                             const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da) {
   using U = Unit<C, PH, 0>;
   bx_stage_acc<C>(lane, acc[0], T);
   if constexpr (U::pair) bx_stage_acc<C>(lane, acc[1], T + 32);
-  XPair<U::W> x0;
+  XIn<U::W / 8> x0;
 #pragma unroll
-  for (int q = 0; q < U::W / 8; ++q) bx_load_group<U::W>(d, buf, m_pad, wi0, wj0, lane, x0, q);
+  for (int q = 0; q < U::W / 8; ++q) bx_load_group<U::W>(d, buf, m_pad, wi0, wj0, lane, x0, q, 0);
   bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da);
+}
+
+// The epilogue of a wave pair that splits a tile's Gram-side rows at an odd
+// multiple of 32 (two waves of WM = 160 rows in a 320-row tile): each wave
+// has two pairs of its own, and its remaining block shares a line with the
+// other wave's.  That line is merged: both blocks go to the T tile of the
+// upper wave (H = 0; the lower wave's block to columns 32..63, after a
+// barrier that ends the upper wave's own passes over that tile), and each
+// wave finishes half of the line's rows after a second barrier.  H = 0:
+// pairs (0,1), (2,3), shared block 4; H = 1: pairs (1,2), (3,4), shared
+// block 0.
+template <class C, int MODE, int H>
+__device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane,
+                                                   float* T, float* Tm, const f32x16_t (&acc)[C::BMB][C::BNB],
+                                                   DiagAcc& da) {
+  static_assert(C::BMB == 5, "merged epilogue: two pairs and one shared block per wave");
+  constexpr int I0 = H, I1 = H + 2, MB = H ? 0 : 4;
+  const int g0 = wi0 + 32 * I0, g1 = wi0 + 32 * I1;
+  const int gm = wi0 + 32 * MB - 32 * H;  // first column of the shared line
+  bx_stage_acc<C>(lane, acc[I0], T);
+  bx_stage_acc<C>(lane, acc[I0 + 1], T + 32);
+  XIn<8> x0, x1;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
+  bx_pass<C, MODE, 64, 8, 64, 8, false>(d, buf, m_pad, g0, wj0, lane, T, x0, 0, 0, da, x1, g1, 0);
+  bx_stage_acc<C>(lane, acc[I1], T);
+  bx_stage_acc<C>(lane, acc[I1 + 1], T + 32);
+  XIn<4> xm;
+  bx_pass<C, MODE, 64, 8, 64, 4, false>(d, buf, m_pad, g1, wj0, lane, T, x1, 0, 0, da, xm, gm, 4 * H);
+  __syncthreads();
+  bx_stage_acc<C>(lane, acc[MB], Tm + 32 * H);
+  __syncthreads();
+  XIn<1> none;
+  bx_pass<C, MODE, 64, 4, 32, 0, true>(d, buf, m_pad, gm, wj0, lane, Tm, xm, 4 * H, 4 * H, da, none, 0, 0);
 }
 
 template <class C, int MODE>
@@ -693,11 +737,19 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   if constexpr (MODE >= BXM) {
     float* T = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
     DiagAcc da;
-    // Wave-uniform: whether the wave's first block starts a 64-row line.
-    if (((wi0 >> 5) & 1) == 0)
+    if constexpr (C::NWM == 2 && C::WM % 64 == 32 && C::BM % 64 == 0) {
+      // The two waves of a column share the line at row WM - 32 of the tile.
+      float* Tm = reinterpret_cast<float*>(smem) + wc * (C::SLICEB / 4);
+      if (wr == 0)
+        bx_epilogue_merged<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da);
+      else
+        bx_epilogue_merged<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da);
+    } else if (((wi0 >> 5) & 1) == 0) {
+      // Wave-uniform: whether the wave's first block starts a 64-row line.
       bx_epilogue<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, da);
-    else
+    } else {
       bx_epilogue<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, da);
+    }
     if constexpr (MODE == BXD) diag_flush(da, d.diag_part + local * C::NW + wave, lane);
     return;
   }
