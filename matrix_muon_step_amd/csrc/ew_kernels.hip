@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
                                                             int nmats, float mu) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   const int local = blk - prefix[mi];
   const int flags = d.flags;
   const int64_t total = d.rows * d.cols;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
 // then sigma = 1 / (sqrt(sum) + eps).  With diagnostics it also keeps
 // ||M||_F and the OR of the blocks' non-finite flags in mstat.
 __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ descs, float eps) {
-  const MatDesc& d = descs[blockIdx.x];
+  const MatDesc d = descs[blockIdx.x];
   const int nb = d.mom_blocks;
   double s = 0.0;
   for (int i = threadIdx.x; i < nb; i += 256) s += static_cast<double>(gld<float>(d.partials + i));
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
                                                    float mu) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   const int local = blk - prefix[mi];
   // The padded extents are multiples of 32 but not always of 64: the last
   // tile row / column is partial and every write below is masked to them
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
                                                      int buf) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   const int local = blk - prefix[mi];
   const int64_t rows = d.rows, cols = d.cols;
   const int tpr = static_cast<int>((cols + kEwTile - 1) / kEwTile);
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
     if (s0 + sl >= src_rows || s1 + tx * 4 >= src_cols) continue;
     if (small) {
       const int64_t off = (s0 + sl) * d.n_pad + s1 + tx * 4;
-      const float4 v = gld<float4>(d.xf[buf] + off);
+      const float4 v = gld<float4>(pick(d.xf, buf) + off);
       tile[sl][tx * 4 + 0] = v.x;
       tile[sl][tx * 4 + 1] = v.y;
       tile[sl][tx * 4 + 2] = v.z;
@@ -302,8 +302,8 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
       continue;
     }
     const int64_t off = (s0 + sl) * d.m_pad + s1 + tx * 4;
-    const uint2 hv = gld<uint2>(d.xt_hi[buf] + off);
-    const uint2 lv = gld<uint2>(d.xt_lo[buf] + off);
+    const uint2 hv = gld<uint2>(pick(d.xt_hi, buf) + off);
+    const uint2 lv = gld<uint2>(pick(d.xt_lo, buf) + off);
     tile[sl][tx * 4 + 0] = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
     tile[sl][tx * 4 + 1] = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
     tile[sl][tx * 4 + 2] = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void update_kernel(const MatDesc* __restrict__
 // fixed order (strided per thread, then a tree), and the muon_diag_t record.
 __global__ __launch_bounds__(256) void diag_kernel(const MatDesc* __restrict__ descs,
                                                    muon_diag_t* __restrict__ out) {
-  const MatDesc& d = descs[blockIdx.x];
+  const MatDesc d = descs[blockIdx.x];
   const int ns = d.diag_slots;
   double o2 = 0.0, d2 = 0.0, w2 = 0.0;
   int bad = 0;

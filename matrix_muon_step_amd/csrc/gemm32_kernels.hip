@@ -346,8 +346,8 @@ __device__ __forceinline__ void bx_load_group(const MatDesc& d, int buf, int m_p
   int jl, il;
   unit_pos<W>(p0 + q, lane, jl, il);
   const int64_t off = static_cast<int64_t>(wj0 + jl) * m_pad + gi0 + il;
-  x.hi[q] = gld<uint4>(d.xt_hi[buf] + off);
-  x.lo[q] = gld<uint4>(d.xt_lo[buf] + off);
+  x.hi[q] = gld<uint4>(pick(d.xt_hi, buf) + off);
+  x.lo[q] = gld<uint4>(pick(d.xt_lo, buf) + off);
 }
 
 // Accumulators of one 32-row block -> T columns co..co+31.
@@ -445,8 +445,8 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
         nl[q] = pack_bf16(v[2 * q] - bf_lo(nh[q]), v[2 * q + 1] - bf_hi(nh[q]));
       }
       const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-      gst(d.xt_hi[buf ^ 1] + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
-      gst(d.xt_lo[buf ^ 1] + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
+      gst(pick(d.xt_hi, buf ^ 1) + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
+      gst(pick(d.xt_lo, buf ^ 1) + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
     } else if (tr) {
       // O^T = X'^T has W's orientation: W[gj][gi .. gi+7].
       if (gj < d.n) {
@@ -504,36 +504,48 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
   asm volatile("" ::: "memory");
 }
 
-// Unit I of a wave whose first block starts at an odd (PH = 1) or even
-// (PH = 0) multiple of 32 Gram-side rows: a pair when block I starts a
-// 64-aligned line and block I + 1 exists, else a single.
-template <class C, int PH, int I>
-struct Unit {
-  static constexpr bool pair = ((PH + I) % 2 == 0) && (I + 1 < C::BMB);
-  static constexpr int W = pair ? 64 : 32;
-  static constexpr int NEXT = I + (pair ? 2 : 1);
+// Units of a wave whose first block starts at an even (PH = 0) or odd
+// (PH = 1) multiple of 32 Gram-side rows: the line-aligned pairs first
+// (blocks 0-1, 2-3, ... or 1-2, 3-4, ...), then the blocks left alone (the
+// last one, then block 0), so the accumulators of a leading single stay in
+// registers while the pairs, which need the most input registers, run.
+template <class C, int PH>
+struct Units {
+  static constexpr int NP = PH ? (C::BMB - 1) / 2 : C::BMB / 2;
+  static constexpr bool tail = PH ? (C::BMB % 2 == 0) : (C::BMB % 2 == 1);
+  static constexpr int N = NP + (tail ? 1 : 0) + PH;
+  static constexpr bool pair(int k) { return k < NP; }
+  static constexpr int start(int k) { return k < NP ? PH + 2 * k : (k == NP && tail) ? C::BMB - 1 : 0; }
+  static constexpr int width(int k) { return pair(k) ? 64 : 32; }
 };
 
-// Unit I is staged in T and its inputs are requested (or in flight): its
+template <class C, int PH, int K>
+__device__ __forceinline__ void bx_stage_unit(int lane, const f32x16_t (&acc)[C::BMB][C::BNB], float* T) {
+  using U = Units<C, PH>;
+  bx_stage_acc<C>(lane, acc[U::start(K)], T);
+  if constexpr (U::pair(K)) bx_stage_acc<C>(lane, acc[U::start(K) + 1], T + 32);
+}
+
+// Unit K is staged in T and its inputs are requested (or in flight): its
 // passes run while the next unit's inputs are requested, then the next
 // unit's accumulators go to T (after this unit's last read of T).
-template <class C, int MODE, int PH, int I>
+template <class C, int MODE, int PH, int K>
 __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
                                          const f32x16_t (&acc)[C::BMB][C::BNB],
-                                         const XIn<Unit<C, PH, I>::W / 8>& cur, DiagAcc& da) {
-  using U = Unit<C, PH, I>;
-  if constexpr (U::NEXT < C::BMB) {
-    using N = Unit<C, PH, U::NEXT>;
-    XIn<N::W / 8> nxt;
-    bx_pass<C, MODE, U::W, U::W / 8, N::W, N::W / 8, false>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, 0, 0, da,
-                                                            nxt, wi0 + 32 * U::NEXT, 0);
-    bx_stage_acc<C>(lane, acc[U::NEXT], T);
-    if constexpr (N::pair) bx_stage_acc<C>(lane, acc[U::NEXT + 1], T + 32);
-    bx_units<C, MODE, PH, U::NEXT>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da);
+                                         const XIn<Units<C, PH>::width(K) / 8>& cur, DiagAcc& da) {
+  using U = Units<C, PH>;
+  constexpr int W = U::width(K);
+  const int gi0 = wi0 + 32 * U::start(K);
+  if constexpr (K + 1 < U::N) {
+    constexpr int W2 = U::width(K + 1);
+    XIn<W2 / 8> nxt;
+    bx_pass<C, MODE, W, W / 8, W2, W2 / 8, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, nxt,
+                                                  wi0 + 32 * U::start(K + 1), 0);
+    bx_stage_unit<C, PH, K + 1>(lane, acc, T);
+    bx_units<C, MODE, PH, K + 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da);
   } else {
     XIn<1> none;
-    bx_pass<C, MODE, U::W, U::W / 8, 32, 0, false>(d, buf, m_pad, wi0 + 32 * I, wj0, lane, T, cur, 0, 0, da, none,
-                                                   0, 0);
+    bx_pass<C, MODE, W, W / 8, 32, 0, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, none, 0, 0);
   }
 }
 
@@ -543,12 +555,12 @@ __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, i
 template <class C, int MODE, int PH>
 __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
                                             const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da) {
-  using U = Unit<C, PH, 0>;
-  bx_stage_acc<C>(lane, acc[0], T);
-  if constexpr (U::pair) bx_stage_acc<C>(lane, acc[1], T + 32);
-  XIn<U::W / 8> x0;
+  using U = Units<C, PH>;
+  constexpr int W = U::width(0);
+  bx_stage_unit<C, PH, 0>(lane, acc, T);
+  XIn<W / 8> x0;
 #pragma unroll
-  for (int q = 0; q < U::W / 8; ++q) bx_load_group<U::W>(d, buf, m_pad, wi0, wj0, lane, x0, q, 0);
+  for (int q = 0; q < W / 8; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
   bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da);
 }
 
@@ -596,9 +608,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int work = split.begin[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
   if (work >= split.end[blockIdx.x & 7]) return;
   const int mi = find_mat(prefix, nmats, work);
-  const MatDesc& d = descs[mi];
+  const MatDesc& dr = descs[mi];  // operands and sizes, read before any store
   int local = work - prefix[mi];
-  const int m_pad = d.m_pad, n_pad = d.n_pad;
+  const int m_pad = dr.m_pad, n_pad = dr.n_pad;
 
   int ti, tj;
   if (MODE >= BXM) {
@@ -608,7 +620,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     // in L2 while the group sweeps the long side.
     const int tpc = m_pad / C::BM;
     const int tpr = n_pad / C::BN;
-    const int g = d.bx_group;
+    const int g = dr.bx_group;
     const int grp = local / (g * tpr);
     const int rows = min(g, tpc - grp * g);
     const int rem = local - grp * g * tpr;
@@ -632,17 +644,17 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const __bf16* __restrict__ Bop;
   int ld, K;
   if (MODE == GRAM) {
-    Aop = d.xt_hi[buf] + static_cast<int64_t>(ti) * C::BM;
-    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * C::BN;
+    Aop = pick(dr.xt_hi, buf) + static_cast<int64_t>(ti) * C::BM;
+    Bop = pick(dr.xt_hi, buf) + static_cast<int64_t>(tj) * C::BN;
     ld = m_pad;
-    K = d.k_gram;
+    K = dr.k_gram;
   } else if (MODE == POLY) {
-    Aop = d.gram + static_cast<int64_t>(ti) * C::BM * m_pad;
-    Bop = d.gram + static_cast<int64_t>(tj) * C::BN * m_pad;
+    Aop = dr.gram + static_cast<int64_t>(ti) * C::BM * m_pad;
+    Bop = dr.gram + static_cast<int64_t>(tj) * C::BN * m_pad;
     ld = K = m_pad;
   } else {
-    Aop = d.poly + static_cast<int64_t>(ti) * C::BM * m_pad;
-    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * C::BN * m_pad;
+    Aop = dr.poly + static_cast<int64_t>(ti) * C::BM * m_pad;
+    Bop = pick(dr.xt_hi, buf) + static_cast<int64_t>(tj) * C::BN * m_pad;
     ld = K = m_pad;
   }
 
@@ -730,6 +742,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   else main_loop<C, PER_FULL - 2, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   __syncthreads();
+  // The epilogue reads the descriptor through the table: a copy (see
+  // MatDesc) measured 1% slower here.
+  const MatDesc& d = dr;
 
   // ---- epilogue (wave-local).
   const int wi0 = ti * C::BM + wr * C::WM;   // first global row of the wave's sub-tile

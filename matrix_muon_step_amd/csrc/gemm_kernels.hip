@@ -316,7 +316,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const int work = split.begin[blockIdx.x & 7] + static_cast<int>(blockIdx.x >> 3);
   if (work >= split.end[blockIdx.x & 7]) return;
   const int mi = find_mat(prefix, nmats, work);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   int local = work - prefix[mi];
   const int m_pad = d.m_pad;
 
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   // its tiles are 32 k-rows x T columns, transposed on the way out of LDS.
   constexpr bool TR = MODE == GRAM;
   if (MODE == GRAM) {
-    Aop = d.xt_hi[buf] + static_cast<int64_t>(ti) * T;
-    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * T;
+    Aop = pick(d.xt_hi, buf) + static_cast<int64_t>(ti) * T;
+    Bop = pick(d.xt_hi, buf) + static_cast<int64_t>(tj) * T;
     ld = m_pad;
     K = d.k_gram;
   } else if (MODE == POLY) {
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
     ld = K = m_pad;
   } else {
     Aop = d.poly + static_cast<int64_t>(ti) * T * m_pad;
-    Bop = d.xt_hi[buf] + static_cast<int64_t>(tj) * T * m_pad;
+    Bop = pick(d.xt_hi, buf) + static_cast<int64_t>(tj) * T * m_pad;
     ld = K = m_pad;
   }
 
@@ -474,8 +474,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
           const int gj = wj0 + j * 16 + l16;
           const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
           if (MODE == BXM) {
-            in_a[ib - b0][j] = gld<uint2>(d.xt_hi[buf] + off);
-            in_b[ib - b0][j] = gld<uint2>(d.xt_lo[buf] + off);
+            in_a[ib - b0][j] = gld<uint2>(pick(d.xt_hi, buf) + off);
+            in_b[ib - b0][j] = gld<uint2>(pick(d.xt_lo, buf) + off);
           } else {
             in_a[ib - b0][j] = gld<uint2>(d.gram + off);
           }
@@ -503,8 +503,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
           w1 = pack_bf16(v[2], v[3]);
           const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
           const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
-          gst(d.xt_hi[buf ^ 1] + off, make_uint2(w0, w1));
-          gst(d.xt_lo[buf ^ 1] + off, make_uint2(l0, l1));
+          gst(pick(d.xt_hi, buf ^ 1) + off, make_uint2(w0, w1));
+          gst(pick(d.xt_lo, buf ^ 1) + off, make_uint2(l0, l1));
         } else {
           if (MODE == POLY) {
             // A is stored symmetric: A[gi..gi+3][gj] == A[gj][gi..gi+3].

@@ -94,6 +94,11 @@ __device__ __forceinline__ void diag_flush(const DiagAcc& a, DiagPart* dst, int 
 }
 
 // One matrix of a call, as the kernels see it (lives in the workspace).
+// Kernels take a copy (const MatDesc d = descs[i]): through a reference,
+// every store into a buffer might alias the table, and the compiler would
+// reload the fields (and wait on the scalar loads) after each store.  The
+// ping-pong pairs are read through pick(): a run-time array index would
+// put the copy in scratch memory.
 struct MatDesc {
   float* W;          // update target (or O output in orthogonalise-only mode)
   const void* G;     // gradient (or M input in orthogonalise-only mode)
@@ -123,6 +128,12 @@ struct MatDesc {
   int32_t bx_group;    // BX tile order: Gram-side tile rows per group (see gemm32)
   int32_t diag_slots;  // entries of diag_part (work-groups x waves of the W writer)
 };
+
+// Buffer b (0 or 1) of a ping-pong pair, without a run-time array index.
+template <class T>
+__device__ __forceinline__ T* pick(T* const (&a)[2], int b) {
+  return b ? a[1] : a[0];
+}
 
 // Split of one grouped GEMM launch over the 8 XCDs: work-groups are dealt
 // to XCDs round-robin (block id % 8), and XCD x runs the contiguous work

@@ -41,10 +41,10 @@ __global__ __launch_bounds__(256) void small_gram_kernel(const MatDesc* __restri
                                                          int nmats, int buf) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   const int chunk = blk - prefix[mi];
   const int n_pad = d.n_pad;
-  const float* __restrict__ X = d.xf[buf] + static_cast<int64_t>(chunk) * SC;
+  const float* __restrict__ X = pick(d.xf, buf) + static_cast<int64_t>(chunk) * SC;
   __shared__ __attribute__((aligned(16))) float xs[SC][XS];  // [k][i]
   const int t = threadIdx.x;
   // Load X[0:64][chunk] transposed into xs.
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void small_poly_kernel(const MatDesc* __restri
                                                          const int32_t* __restrict__ prefix,
                                                          int nmats) {
   const int mi = find_mat(prefix, nmats, blockIdx.x);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   __shared__ float A[SM][SM + 1];
   const int t = threadIdx.x;
   const int nc = d.s_chunks;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void small_bx_kernel(const MatDesc* __restrict
                                                        int nmats, int buf) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
-  const MatDesc& d = descs[mi];
+  const MatDesc d = descs[mi];
   const int chunk = blk - prefix[mi];
   const int n_pad = d.n_pad;
   __shared__ __attribute__((aligned(16))) float P[SM * SM];
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(256) void small_bx_kernel(const MatDesc* __restrict
   for (int e = t; e < SM * SM; e += 256) P[e] = gld<float>(d.spoly + e);
   __syncthreads();
   const int64_t col = static_cast<int64_t>(chunk) * SC + t;
-  const float* __restrict__ X = d.xf[buf] + col;
-  float* __restrict__ Y = d.xf[buf ^ 1] + col;
+  const float* __restrict__ X = pick(d.xf, buf) + col;
+  float* __restrict__ Y = pick(d.xf, buf ^ 1) + col;
   float x[SM];
 #pragma unroll
   for (int k = 0; k < SM; ++k) x[k] = gld<float>(X + static_cast<int64_t>(k) * n_pad);

@@ -175,10 +175,12 @@ def test_single256_update_epilogue_fp32(mm):
 
 # Shapes of both update routes: the wide-tile BX kernels write W from their
 # last launch (fused), the others leave it to the separate update pass.  The
-# list covers both orientations, ragged Gram sides, and rows whose length is
-# not a multiple of 4 (element-wise W accesses).
+# list covers both orientations, ragged Gram sides, rows whose length is not
+# a multiple of 4 (element-wise W accesses), and 160-row BX tiles that start
+# at an odd multiple of 32 rows (m = 480, 800: epilogue blocks paired from
+# the second one).
 UPDATE_SHAPES = [(130, 1000), (1000, 132), (515, 1030), (1030, 515), (2048, 512),
-                 (128, 128), (300, 520), (520, 300), (33, 17)]
+                 (128, 128), (300, 520), (520, 300), (33, 17), (480, 960), (1000, 800)]
 
 
 @pytest.mark.parametrize("shape", UPDATE_SHAPES)
