@@ -238,18 +238,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
   for (int k = 0; k < 4; ++k) {
     const int jl = ty + 16 * k;
     if (j0 + jl >= n_pad || i0 + tx * 4 >= m_pad) continue;
-    __bf16 h[4], l[4];
+    float x[4];
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
       const int il = tx * 4 + c4;
-      const float x = sigma * (tr ? tile[jl][il] : tile[il][jl]);
-      h[c4] = static_cast<__bf16>(x);
-      l[c4] = static_cast<__bf16>(x - static_cast<float>(h[c4]));
+      x[c4] = sigma * (tr ? tile[jl][il] : tile[il][jl]);
     }
+    const uint32_t h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+    const uint2 hv = make_uint2(h0, h1);
+    const uint2 lv = make_uint2(pack_bf16(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
+                                pack_bf16(x[2] - bf_lo(h1), x[3] - bf_hi(h1)));
     const int64_t off = static_cast<int64_t>(j0 + jl) * d.m_pad + i0 + tx * 4;
-    uint2 hv, lv;
-    __builtin_memcpy(&hv, h, 8);
-    __builtin_memcpy(&lv, l, 8);
     gst(d.xt_hi[0] + off, hv);
     gst(d.xt_lo[0] + off, lv);
   }

@@ -100,15 +100,6 @@ __device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int 
   return lo;
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const __bf16 x = static_cast<__bf16>(a), y = static_cast<__bf16>(b);
-  uint16_t ux, uy;
-  __builtin_memcpy(&ux, &x, 2);
-  __builtin_memcpy(&uy, &y, 2);
-  return static_cast<uint32_t>(ux) | (static_cast<uint32_t>(uy) << 16);
-}
 
 // Waits until at most `newer` later steps of this wave's loads are in flight
 // (`per` loads per step, a compile-time count for each wave class).

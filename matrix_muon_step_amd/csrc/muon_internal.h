@@ -22,6 +22,20 @@ __device__ __forceinline__ void gst(void* p, T v) {
   __builtin_memcpy((__attribute__((address_space(1))) void*)p, &v, sizeof(T));
 }
 
+// bf16 halves of a 32-bit word as float32 (low half = element 0).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two float32 values rounded to bf16 (nearest, ties to even) in one word,
+// a in the low half: a single packed conversion on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
 // Matrix-core kernel configurations (tile rows x tile columns, MFMA shape):
 //   G256: 256 x 256, 32x32x16   (Gram, polynomial, BX)
 //   W160: 160 x 256, 32x32x16   (BX only; Gram side a multiple of 160)
