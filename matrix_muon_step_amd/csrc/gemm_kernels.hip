@@ -292,6 +292,117 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
   mfma16<C>(a, b, acc);
 }
 
+// Epilogue of a symmetric product (Gram, polynomial) for one wave's sub-tile
+// (WM x WN, rows gi0 = wi0.., columns gj0 = wj0..), through the wave's LDS
+// slice so that every global access is 16 bytes per lane along a row:
+//   1. (polynomial) the input A at the mirror positions, A[gj][gi..], rows
+//      of the slice M[jl][il] (A is symmetric, so these are the values the
+//      accumulators need);
+//   2. the results in accumulator layout (column gj per lane, four
+//      consecutive rows gi) rounded to bf16 and written to M[jl][il..il+3]
+//      (for the polynomial in place of the A values they use);
+//   3. rows of M to the mirror half, P[gj][gi..];
+//   4. the same words, kept in registers, to a row-major slice S[il][jl]
+//      (same LDS), whose rows go to the direct half, P[gi][gj..].
+// On a diagonal tile (DIAG) both halves are written from the elements with
+// gi <= gj only, so the two triangles hold bit-identical values.
+template <class C, int MODE, bool DIAG>
+__device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi0, int wj0, int lane, __bf16* slice,
+                                             const f32x4_t (&acc)[C::BMB][C::BNB]) {
+  static_assert(C::EPI_ROWS == C::WM && C::WM == C::WN, "square wave tiles, staged whole");
+  constexpr int LD = C::EPI_LD;
+  constexpr int CPR = C::WM / 8;       // 16-byte chunks per slice row
+  constexpr int NCH = C::WN * CPR;     // chunks per sub-tile
+  constexpr int NIT = (NCH + 63) / 64;
+  const int l16 = lane & 15, lq = lane >> 4;
+  __bf16* rdst = (MODE == POLY) ? d.poly : d.gram;
+  if constexpr (MODE == POLY) {
+#pragma unroll
+    for (int t = 0; t < NIT; ++t) {
+      const int c = t * 64 + lane;
+      if (c < NCH) {
+        const int jl = c / CPR, ch = c - (c / CPR) * CPR;
+        *reinterpret_cast<uint4*>(slice + jl * LD + 8 * ch) =
+            gld<uint4>(d.gram + static_cast<int64_t>(wj0 + jl) * m_pad + wi0 + 8 * ch);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+  uint32_t w[C::BMB][C::BNB][2];
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j) {
+      uint2* mp = reinterpret_cast<uint2*>(slice + (16 * j + l16) * LD + 16 * i + 4 * lq);
+      float v[4];
+      if constexpr (MODE == POLY) {
+        const uint2 av = *mp;  // A[gj][gi..gi+3] == A[gi..gi+3][gj]
+        v[0] = fmaf(kCoefC, acc[i][j][0], kCoefB * bf_lo(av.x));
+        v[1] = fmaf(kCoefC, acc[i][j][1], kCoefB * bf_hi(av.x));
+        v[2] = fmaf(kCoefC, acc[i][j][2], kCoefB * bf_lo(av.y));
+        v[3] = fmaf(kCoefC, acc[i][j][3], kCoefB * bf_hi(av.y));
+      } else {
+        v[0] = acc[i][j][0]; v[1] = acc[i][j][1]; v[2] = acc[i][j][2]; v[3] = acc[i][j][3];
+      }
+      w[i][j][0] = pack_bf16(v[0], v[1]);
+      w[i][j][1] = pack_bf16(v[2], v[3]);
+      *mp = make_uint2(w[i][j][0], w[i][j][1]);
+    }
+  asm volatile("" ::: "memory");
+  // Mirror half: row gj of the slice holds P[gj][wi0 ..].
+#pragma unroll
+  for (int t = 0; t < NIT; ++t) {
+    const int c = t * 64 + lane;
+    if (c < NCH) {
+      const int jl = c / CPR, ch = c - (c / CPR) * CPR;
+      const int gj = wj0 + jl, gi = wi0 + 8 * ch;
+      const uint4 val = *reinterpret_cast<const uint4*>(slice + jl * LD + 8 * ch);
+      __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;
+      if (!DIAG || gi + 7 <= gj) {
+        gst(p, val);
+      } else if (gi <= gj) {
+        uint16_t hv[8];
+        __builtin_memcpy(hv, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gi + e <= gj) gst(p + e, hv[e]);
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+  // Direct half: the words again, row-major.
+#pragma unroll
+  for (int i = 0; i < C::BMB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BNB; ++j) {
+      const int rl = 16 * i + 4 * lq, cl = 16 * j + l16;
+      const uint16_t hb[4] = {static_cast<uint16_t>(w[i][j][0]), static_cast<uint16_t>(w[i][j][0] >> 16),
+                              static_cast<uint16_t>(w[i][j][1]), static_cast<uint16_t>(w[i][j][1] >> 16)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * LD + cl, &hb[r], 2);
+    }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < NIT; ++t) {
+    const int c = t * 64 + lane;
+    if (c < NCH) {
+      const int il = c / CPR, ch = c - (c / CPR) * CPR;
+      const int gi = wi0 + il, gj = wj0 + 8 * ch;
+      const uint4 val = *reinterpret_cast<const uint4*>(slice + il * LD + 8 * ch);
+      __bf16* p = rdst + static_cast<int64_t>(gi) * m_pad + gj;
+      if (!DIAG || gi <= gj) {
+        gst(p, val);
+      } else if (gi < gj + 8) {
+        uint16_t hv[8];
+        __builtin_memcpy(hv, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gi <= gj + e) gst(p + e, hv[e]);
+      }
+    }
+  }
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                               const int32_t* __restrict__ prefix,
@@ -433,130 +544,61 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
 
   // ---- epilogue.  16x16 accumulator layout: lane holds column (lane & 15),
   // register r holds row 4 * (lane >> 4) + r.  Each wave works alone on its
-  // sub-tile: transposed outputs from registers, the row-major copy through
-  // its private LDS slice, EPI_ROWS rows at a time.
-  const bool diag = (MODE != BXM) && (ti == tj);
+  // sub-tile through its private LDS slice.
   const int wi0 = ti * T + wr * C::WM;      // first global row of the wave's sub-tile
   const int wj0 = tj * T + wc * C::WN;      // first global column
   __bf16* slice = smem + wave * (C::EPIB / 2);
-  // Gram / polynomial tiles also get a row-major copy (the mirror half);
-  // the BX output is only needed as the X^T pair.
-  __bf16* rdst = (MODE == POLY) ? d.poly : d.gram;
-  const int64_t rld = m_pad;
-  constexpr int HALVES = C::WM / C::EPI_ROWS;
-  constexpr int HB = C::EPI_ROWS / 16;      // row blocks per half
-  // Global reads are issued a batch of PRE block rows at a time (they are
-  // independent and mostly come from HBM), then combined.
+  if constexpr (MODE != BXM) {
+    if (ti == tj)
+      sym_epilogue<C, MODE, true>(d, m_pad, wi0, wj0, lane, slice, acc);
+    else
+      sym_epilogue<C, MODE, false>(d, m_pad, wi0, wj0, lane, slice, acc);
+    return;
+  }
+  // BX: X' = a (X_hi + X_lo) + P X_hi, stored as the X^T pair straight from
+  // the accumulators (four consecutive Gram-side rows per lane are 8
+  // contiguous bytes of a row of X^T).  Global reads are issued a batch of
+  // PRE block rows at a time (they are independent and mostly come from
+  // HBM), then combined.
   constexpr int PRE = (16 / C::BNB) > 0 ? (16 / C::BNB) : 1;
 #pragma unroll
-  for (int h = 0; h < HALVES; ++h) {
+  for (int b0 = 0; b0 < C::BMB; b0 += PRE) {
+    uint2 in_a[PRE][C::BNB], in_b[PRE][C::BNB];
 #pragma unroll
-  for (int b0 = 0; b0 < HB; b0 += PRE) {
-    constexpr int NPRE = PRE;
-    uint2 in_a[NPRE][C::BNB], in_b[NPRE][C::BNB];
-    if (MODE != GRAM) {
-#pragma unroll
-      for (int ib = b0; ib < b0 + NPRE && ib < HB; ++ib) {
-#pragma unroll
-        for (int j = 0; j < C::BNB; ++j) {
-          const int gi = wi0 + (h * HB + ib) * 16 + lq * 4;
-          const int gj = wj0 + j * 16 + l16;
-          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-          if (MODE == BXM) {
-            in_a[ib - b0][j] = gld<uint2>(pick(d.xt_hi, buf) + off);
-            in_b[ib - b0][j] = gld<uint2>(pick(d.xt_lo, buf) + off);
-          } else {
-            in_a[ib - b0][j] = gld<uint2>(d.gram + off);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int ib = b0; ib < b0 + NPRE && ib < HB; ++ib) {
-      const int i = h * HB + ib;
+    for (int ib = b0; ib < b0 + PRE && ib < C::BMB; ++ib) {
 #pragma unroll
       for (int j = 0; j < C::BNB; ++j) {
-        const int gi = wi0 + i * 16 + lq * 4;
+        const int gi = wi0 + ib * 16 + lq * 4;
         const int gj = wj0 + j * 16 + l16;
+        const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+        in_a[ib - b0][j] = gld<uint2>(pick(d.xt_hi, buf) + off);
+        in_b[ib - b0][j] = gld<uint2>(pick(d.xt_lo, buf) + off);
+      }
+    }
+#pragma unroll
+    for (int ib = b0; ib < b0 + PRE && ib < C::BMB; ++ib) {
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j) {
+        const int gi = wi0 + ib * 16 + lq * 4;
+        const int gj = wj0 + j * 16 + l16;
+        const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
+        const uint2 hx = in_a[ib - b0][j];
+        const uint2 lx = in_b[ib - b0][j];
         float v[4];
-        uint32_t w0, w1;
-        if (MODE == BXM) {
-          const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-          const uint2 hx = in_a[ib - b0][j];
-          const uint2 lx = in_b[ib - b0][j];
-          v[0] = fmaf(kCoefA, bf_lo(hx.x) + bf_lo(lx.x), acc[i][j][0]);
-          v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), acc[i][j][1]);
-          v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), acc[i][j][2]);
-          v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), acc[i][j][3]);
-          w0 = pack_bf16(v[0], v[1]);
-          w1 = pack_bf16(v[2], v[3]);
-          const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
-          const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
-          gst(pick(d.xt_hi, buf ^ 1) + off, make_uint2(w0, w1));
-          gst(pick(d.xt_lo, buf ^ 1) + off, make_uint2(l0, l1));
-        } else {
-          if (MODE == POLY) {
-            // A is stored symmetric: A[gi..gi+3][gj] == A[gj][gi..gi+3].
-            const uint2 a = in_a[ib - b0][j];
-            v[0] = fmaf(kCoefC, acc[i][j][0], kCoefB * bf_lo(a.x));
-            v[1] = fmaf(kCoefC, acc[i][j][1], kCoefB * bf_hi(a.x));
-            v[2] = fmaf(kCoefC, acc[i][j][2], kCoefB * bf_lo(a.y));
-            v[3] = fmaf(kCoefC, acc[i][j][3], kCoefB * bf_hi(a.y));
-          } else {
-            v[0] = acc[i][j][0]; v[1] = acc[i][j][1]; v[2] = acc[i][j][2]; v[3] = acc[i][j][3];
-          }
-          w0 = pack_bf16(v[0], v[1]);
-          w1 = pack_bf16(v[2], v[3]);
-          __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;  // mirror position
-          if (!diag || gi + 3 <= gj) {
-            gst(p, make_uint2(w0, w1));
-          } else {
-            const uint32_t wv[2] = {w0, w1};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (gi + r <= gj) {
-                const uint16_t bits = static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16));
-                gst(p + r, bits);
-              }
-            }
-          }
-        }
-        // row-major copy of the high parts into the wave's slice
-        if (MODE != BXM) {
-          const int rl = ib * 16 + lq * 4;
-          const int cl = j * 16 + l16;
-          const uint16_t hb[4] = {static_cast<uint16_t>(w0), static_cast<uint16_t>(w0 >> 16),
-                                  static_cast<uint16_t>(w1), static_cast<uint16_t>(w1 >> 16)};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::EPI_LD + cl, &hb[r], 2);
-        }
+        v[0] = fmaf(kCoefA, bf_lo(hx.x) + bf_lo(lx.x), acc[ib][j][0]);
+        v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), acc[ib][j][1]);
+        v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), acc[ib][j][2]);
+        v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), acc[ib][j][3]);
+        const uint32_t w0 = pack_bf16(v[0], v[1]);
+        const uint32_t w1 = pack_bf16(v[2], v[3]);
+        const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
+        const uint32_t l1 = pack_bf16(v[2] - bf_lo(w1), v[3] - bf_hi(w1));
+        gst(pick(d.xt_hi, buf ^ 1) + off, make_uint2(w0, w1));
+        gst(pick(d.xt_lo, buf ^ 1) + off, make_uint2(l0, l1));
       }
     }
   }
-    // Slice rows -> global rows, 16 bytes at a time.  A wave's LDS
-    // operations complete in order; the compiler barrier keeps the
-    // cross-lane exchange through the slice in program order.
-    if (MODE == BXM) continue;
-    asm volatile("" ::: "memory");
-    constexpr int CPR = C::WN / 8;
-    for (int c = lane; c < C::EPI_ROWS * CPR; c += 64) {
-      const int rl = c / CPR;
-      const int cc = c - rl * CPR;
-      const int gi = wi0 + h * C::EPI_ROWS + rl;
-      const int gj = wj0 + cc * 8;
-      const uint4 val = *reinterpret_cast<const uint4*>(slice + rl * C::EPI_LD + cc * 8);
-      __bf16* p = rdst + static_cast<int64_t>(gi) * rld + gj;
-      if (!diag || gi <= gj) {
-        gst(p, val);
-      } else if (gi < gj + 8) {
-        uint16_t hv[8];
-        __builtin_memcpy(hv, &val, 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gi <= gj + e) gst(p + e, hv[e]);
-      }
-    }
-  }
+  (void)slice;
 }
 
 // Tile configurations: edge T and wave grid.
