@@ -80,7 +80,7 @@ struct G32 {
   static constexpr int NSTAGE = NSTAGE_;                  // ring of LDS stages
   static constexpr int SLICE_LD = WN + 8;                 // Gram/poly epilogue slice row stride (bf16)
   static constexpr int TP = 68;                           // BX epilogue tile pitch (floats), see bx_epilogue
-  static constexpr int SLICEB_SYM = 32 * SLICE_LD * 2;
+  static constexpr int SLICEB_SYM = 64 * SLICE_LD * 2;
   static constexpr int SLICEB_BX = WN * TP * 4;
   static constexpr int SLICEB = SLICEB_SYM > SLICEB_BX ? SLICEB_SYM : SLICEB_BX;  // bytes per wave
   static constexpr int LDSB = (NSTAGE * STAGEB > SLICEB * NW) ? NSTAGE * STAGEB : SLICEB * NW;
@@ -589,6 +589,117 @@ __device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, in
   bx_pass<C, MODE, 64, 4, 32, 0, true>(d, buf, m_pad, gm, wj0, lane, Tm, xm, 4 * H, 4 * H, da, none, 0, 0);
 }
 
+// Epilogue of a symmetric product (Gram, polynomial) for one wave's sub-tile
+// (WM Gram-side rows wi0.., WN = 64 columns wj0..), two 32-row blocks (one
+// 128-byte line of columns of the mirror half) at a time, through the
+// wave's LDS slice so that every global access is 16 bytes per lane along
+// a row:
+//   1. (polynomial) the input A at the mirror positions, A[gj][gi..], as
+//      rows of the slice M[jl][il] (A is symmetric: these are the values
+//      the accumulators need);
+//   2. the results in accumulator layout (column gj per lane, runs of four
+//      rows gi) rounded to bf16 and written to M[jl][il..il+3] (for the
+//      polynomial in place of the A values they use);
+//   3. rows of M to the mirror half, P[gj][gi..] (8 lanes per 128 bytes);
+//   4. the same words, kept in registers, to a row-major slice S[il][jl]
+//      (same LDS), whose rows go to the direct half, P[gi][gj..].
+// On a diagonal tile (DIAG) both halves are written from the elements with
+// gi <= gj only, so the two triangles hold bit-identical values.
+template <class C, int MODE, bool DIAG>
+__device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi0, int wj0, int lane, __bf16* slice,
+                                             const f32x16_t (&acc)[C::BMB][C::BNB]) {
+  static_assert(C::BMB % 2 == 0 && C::WN == 64, "block pairs of 64 rows, 64-column wave tiles");
+  constexpr int LD = C::SLICE_LD;
+  constexpr int NIT = 64 * 8 / 64;     // 16-byte chunks per lane of a 64 x 64 slice
+  __bf16* rdst = (MODE == POLY) ? d.poly : d.gram;
+  const int col = lane & 31;
+  const int rq = 4 * (lane >> 5);
+#pragma unroll
+  for (int pr = 0; pr < C::BMB / 2; ++pr) {
+    const int gi0 = wi0 + 64 * pr;
+    if constexpr (MODE == POLY) {
+#pragma unroll
+      for (int t = 0; t < NIT; ++t) {
+        const int jl = t * 8 + (lane >> 3), ch = lane & 7;
+        *reinterpret_cast<uint4*>(slice + jl * LD + 8 * ch) =
+            gld<uint4>(d.gram + static_cast<int64_t>(wj0 + jl) * m_pad + gi0 + 8 * ch);
+      }
+      asm volatile("" ::: "memory");
+    }
+    uint32_t w[2][C::BNB][4][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint2* mp = reinterpret_cast<uint2*>(slice + (32 * j + col) * LD + 32 * h + 8 * g + rq);
+          const f32x16_t& a = acc[2 * pr + h][j];
+          float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          if constexpr (MODE == POLY) {
+            const uint2 av = *mp;  // A[gj][gi..gi+3] == A[gi..gi+3][gj]
+            v[0] = fmaf(kCoefC, v[0], kCoefB * bf_lo(av.x));
+            v[1] = fmaf(kCoefC, v[1], kCoefB * bf_hi(av.x));
+            v[2] = fmaf(kCoefC, v[2], kCoefB * bf_lo(av.y));
+            v[3] = fmaf(kCoefC, v[3], kCoefB * bf_hi(av.y));
+          }
+          w[h][j][g][0] = pack_bf16(v[0], v[1]);
+          w[h][j][g][1] = pack_bf16(v[2], v[3]);
+          *mp = make_uint2(w[h][j][g][0], w[h][j][g][1]);
+        }
+    asm volatile("" ::: "memory");
+    // Mirror half: row gj of the slice holds P[gj][gi0 .. gi0 + 63].
+#pragma unroll
+    for (int t = 0; t < NIT; ++t) {
+      const int jl = t * 8 + (lane >> 3), ch = lane & 7;
+      const int gj = wj0 + jl, gi = gi0 + 8 * ch;
+      const uint4 val = *reinterpret_cast<const uint4*>(slice + jl * LD + 8 * ch);
+      __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;
+      if (!DIAG || gi + 7 <= gj) {
+        gst(p, val);
+      } else if (gi <= gj) {
+        uint16_t hv[8];
+        __builtin_memcpy(hv, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gi + e <= gj) gst(p + e, hv[e]);
+      }
+    }
+    asm volatile("" ::: "memory");
+    // Direct half: the same words, row-major.
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < C::BNB; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int rl = 32 * h + 8 * g + rq, cl = 32 * j + col;
+          const uint16_t hb[4] = {static_cast<uint16_t>(w[h][j][g][0]), static_cast<uint16_t>(w[h][j][g][0] >> 16),
+                                  static_cast<uint16_t>(w[h][j][g][1]), static_cast<uint16_t>(w[h][j][g][1] >> 16)};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * LD + cl, &hb[r], 2);
+        }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < NIT; ++t) {
+      const int il = t * 8 + (lane >> 3), ch = lane & 7;
+      const int gi = gi0 + il, gj = wj0 + 8 * ch;
+      const uint4 val = *reinterpret_cast<const uint4*>(slice + il * LD + 8 * ch);
+      __bf16* p = rdst + static_cast<int64_t>(gi) * m_pad + gj;
+      if (!DIAG || gi <= gj) {
+        gst(p, val);
+      } else if (gi < gj + 8) {
+        uint16_t hv[8];
+        __builtin_memcpy(hv, &val, 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gi <= gj + e) gst(p + e, hv[e]);
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     const MatDesc* __restrict__ descs, const int32_t* __restrict__ prefix, int nmats, XcdSplit split, int buf) {
@@ -759,95 +870,12 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     if constexpr (MODE == BXD) diag_flush(da, d.diag_part + local * C::NW + wave, lane);
     return;
   }
-  const bool diag = ti == tj;
-  __bf16* slice = reinterpret_cast<__bf16*>(smem) + wave * (C::SLICEB / 2);
-  __bf16* rdst = (MODE == POLY) ? d.poly : d.gram;
-  const int64_t rld = m_pad;
-  const int col = lane & 31;
-  const int rq = 4 * (lane >> 5);
-
-  // Epilogue inputs of one block row (A, for the polynomial), double
-  // buffered so the reads of row i+1 are in flight while row i is finished.
-  uint2 in_a[2][C::BNB][4];
-  auto load_row = [&](int i, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < C::BNB; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int gi = wi0 + i * 32 + 8 * g + rq;
-        const int gj = wj0 + j * 32 + col;
-        const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-        if (MODE == POLY) in_a[slot][j][g] = gld<uint2>(d.gram + off);  // A symmetric
-      }
-  };
-  if (MODE != GRAM) load_row(0, 0);
-#pragma unroll
-  for (int i = 0; i < C::BMB; ++i) {
-    const int slot = i & 1;
-    if (MODE != GRAM && i + 1 < C::BMB) load_row(i + 1, slot ^ 1);
-#pragma unroll
-    for (int j = 0; j < C::BNB; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int gi = wi0 + i * 32 + 8 * g + rq;
-        const int gj = wj0 + j * 32 + col;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * g + r];
-        uint32_t w0 = 0, w1 = 0;
-        {
-          if (MODE == POLY) {
-            const uint2 a = in_a[slot][j][g];
-            v[0] = fmaf(kCoefC, v[0], kCoefB * bf_lo(a.x));
-            v[1] = fmaf(kCoefC, v[1], kCoefB * bf_hi(a.x));
-            v[2] = fmaf(kCoefC, v[2], kCoefB * bf_lo(a.y));
-            v[3] = fmaf(kCoefC, v[3], kCoefB * bf_hi(a.y));
-          }
-          w0 = pack_bf16(v[0], v[1]);
-          w1 = pack_bf16(v[2], v[3]);
-          __bf16* p = rdst + static_cast<int64_t>(gj) * m_pad + gi;  // mirror position
-          if (!diag || gi + 3 <= gj) {
-            gst(p, make_uint2(w0, w1));
-          } else {
-            const uint32_t wv[2] = {w0, w1};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (gi + r <= gj) gst(p + r, static_cast<uint16_t>(wv[r >> 1] >> ((r & 1) * 16)));
-            }
-          }
-        }
-        // row-major copy of the high parts into the wave's 32-row slice
-        const int rl = 8 * g + rq;
-        const int cl = j * 32 + col;
-        const uint16_t hb[4] = {static_cast<uint16_t>(w0), static_cast<uint16_t>(w0 >> 16),
-                                static_cast<uint16_t>(w1), static_cast<uint16_t>(w1 >> 16)};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) __builtin_memcpy(slice + (rl + r) * C::SLICE_LD + cl, &hb[r], 2);
-      }
-    }
-    // Slice (32 rows x WN) -> global rows, 16 bytes at a time.  A wave's
-    // LDS operations complete in order; the compiler barrier keeps the
-    // cross-lane exchange through the slice in program order.
-    asm volatile("" ::: "memory");
-    constexpr int CPR = C::WN / 8;
-#pragma unroll
-    for (int c = lane; c < 32 * CPR; c += 64) {
-      const int rl = c / CPR;
-      const int cc = c - rl * CPR;
-      const int gi = wi0 + i * 32 + rl;
-      const int gj = wj0 + cc * 8;
-      const uint4 val = *reinterpret_cast<const uint4*>(slice + rl * C::SLICE_LD + cc * 8);
-      __bf16* p = rdst + static_cast<int64_t>(gi) * rld + gj;
-      if (!diag || gi <= gj) {
-        gst(p, val);
-      } else if (gi < gj + 8) {
-        uint16_t hv[8];
-        __builtin_memcpy(hv, &val, 16);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gi <= gj + e) gst(p + e, hv[e]);
-      }
-    }
+  if constexpr (MODE == GRAM || MODE == POLY) {
+    __bf16* slice = reinterpret_cast<__bf16*>(smem) + wave * (C::SLICEB / 2);
+    if (ti == tj)
+      sym_epilogue<C, MODE, true>(d, m_pad, wi0, wj0, lane, slice, acc);
+    else
+      sym_epilogue<C, MODE, false>(d, m_pad, wi0, wj0, lane, slice, acc);
   }
 }
 
