@@ -301,7 +301,11 @@ def main():
     traffic = load_traffic(TRAFFIC_SOURCES, w.name)
     n_el = w.n_params
     g_bytes = 2 if w.g_dtype == "bf16" else 4
-    mom_bytes = n_el * (g_bytes + 8)          # read G, B; write B
+    # read G, B; write B; and, where the normalisation is folded into the
+    # first iteration (Gram side > 64, ns_steps > 0), the padded bf16 pair
+    plans = mm.muon_plan_query(shapes, ns_steps=args.ns_steps)[1]
+    pair_bytes = sum(4 * p["m_pad"] * p["n_pad"] for p in plans if p["tile"] and args.ns_steps > 0)
+    mom_bytes = n_el * (g_bytes + 8) + pair_bytes
     upd_bytes = n_el * (8 + 4)                # read W + X pair, write W
     ew = {
         "momentum_gbps": mom_bytes / (stage_ms["momentum"] * 1e-3) / 1e9 if stage_ms["momentum"] else None,

@@ -31,80 +31,121 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// X^T pair of one 64x64 tile of X held in LDS (tile[r][c] = the tile's
+// element of M at row r, column c of M's own orientation), each value
+// multiplied by `scale`; padding is written as zeros.  A row of X^T (one
+// long-side index) holds the tile's 64 short-side values: 128 bytes of each
+// array.
+__device__ __forceinline__ void write_pair_tile(const MatDesc& d, const float (&tile)[kEwTile][kEwTile + 1], int i0,
+                                                int j0, float scale, bool tr) {
+  const int tx = threadIdx.x & 15;
+  const int ty = threadIdx.x >> 4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int jl = ty + 16 * k;
+    if (j0 + jl >= d.n_pad || i0 + tx * 4 >= d.m_pad) continue;
+    float x[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int il = tx * 4 + c4;
+      x[c4] = scale * (tr ? tile[jl][il] : tile[il][jl]);
+    }
+    const uint32_t h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+    const uint2 hv = make_uint2(h0, h1);
+    const uint2 lv = make_uint2(pack_bf16(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
+                                pack_bf16(x[2] - bf_lo(h1), x[3] - bf_hi(h1)));
+    const int64_t off = static_cast<int64_t>(j0 + jl) * d.m_pad + i0 + tx * 4;
+    gst(d.xt_hi[0] + off, hv);
+    gst(d.xt_lo[0] + off, lv);
+  }
+}
+
 // ---------------------------------------------------------------- momentum
-// B <- mu * B + G;  M = B (or G + mu * B);  partials[block] = sum of M^2 over
-// the block's 4096 elements.  Orthogonalise-only mode: M is read from G.
-// With diagnostics, mom_bad[block] = 1 if one of the block's M is NaN or
-// infinite.
-__global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __restrict__ descs,
-                                                            const int32_t* __restrict__ prefix,
-                                                            int nmats, float mu) {
+// One 64x64 tile of X (the short-side-major view of M, padded) per
+// work-group: B <- mu * B + G and M = B (or G + mu * B) for the tile's
+// elements of M, their sum of squares (partials[tile]) and, with
+// diagnostics, whether one is NaN or infinite (mom_bad[tile]).  For a
+// matrix whose normalisation is folded into the first iteration (kFold),
+// the tile also writes the bf16 pair of the unnormalised M as X^T.
+// Orthogonalise-only mode: M is read from G and nothing else is written.
+__global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict__ descs,
+                                                       const int32_t* __restrict__ prefix, int nmats, float mu) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
   const MatDesc d = descs[mi];
   const int local = blk - prefix[mi];
+  const int tpr = (d.n_pad + kEwTile - 1) / kEwTile;
+  const int i0 = (local / tpr) * kEwTile;  // X rows (short side)
+  const int j0 = (local % tpr) * kEwTile;  // X cols (long side)
   const int flags = d.flags;
-  const int64_t total = d.rows * d.cols;
-  const int64_t base = static_cast<int64_t>(local) * kMomChunk;
-  const int64_t end = (base + kMomChunk < total) ? base + kMomChunk : total;
+  const bool tr = flags & kTransposed;
   const bool ortho = flags & kOrthoOnly;
   const bool gbf = flags & kGBf16;
   const bool nest = flags & kNesterov;
-  float* __restrict__ B = d.B;
+  const bool fold = flags & kFold;
+  const int64_t rows = d.rows, cols = d.cols;
+  const int64_t r0 = tr ? j0 : i0;  // region of M (its own orientation)
+  const int64_t c0 = tr ? i0 : j0;
+  const bool vec = (cols & 3) == 0;  // rows of M start 16-byte aligned
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  const int tx = threadIdx.x & 15;   // column group of 4
+  const int ty = threadIdx.x >> 4;   // 0..15
   float acc = 0.f;
   uint32_t bad = 0;
 #pragma unroll
-  for (int it = 0; it < kMomChunk / 1024; ++it) {
-    const int64_t e = base + (static_cast<int64_t>(it) * 256 + threadIdx.x) * 4;
-    if (e >= end) break;
-    float g[4], b[4];
-    const int cnt = (end - e >= 4) ? 4 : static_cast<int>(end - e);
-    if (cnt == 4) {
-      if (gbf) {
-        const uint2 gv = gld<uint2>(static_cast<const uint16_t*>(d.G) + e);
-        g[0] = __uint_as_float(gv.x << 16);
-        g[1] = __uint_as_float(gv.x & 0xffff0000u);
-        g[2] = __uint_as_float(gv.y << 16);
-        g[3] = __uint_as_float(gv.y & 0xffff0000u);
+  for (int k = 0; k < 4; ++k) {
+    const int rl = ty + 16 * k;
+    const int64_t r = r0 + rl;
+    const int64_t c = c0 + tx * 4;
+    float mv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows && c < cols) {
+      const int64_t e = r * cols + c;
+      const int cnt = (cols - c >= 4) ? 4 : static_cast<int>(cols - c);
+      float g[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+      if (vec && cnt == 4) {
+        if (gbf) {
+          const uint2 gv = gld<uint2>(static_cast<const uint16_t*>(d.G) + e);
+          g[0] = bf_lo(gv.x); g[1] = bf_hi(gv.x); g[2] = bf_lo(gv.y); g[3] = bf_hi(gv.y);
+        } else {
+          const float4 gv = gld<float4>(static_cast<const float*>(d.G) + e);
+          g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+        }
+        if (!ortho) {
+          const float4 bv = gld<float4>(d.B + e);
+          b[0] = bv.x; b[1] = bv.y; b[2] = bv.z; b[3] = bv.w;
+        }
       } else {
-        const float4 gv = gld<float4>(static_cast<const float*>(d.G) + e);
-        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
-      }
-      if (!ortho) {
-        const float4 bv = gld<float4>(B + e);
-        b[0] = bv.x; b[1] = bv.y; b[2] = bv.z; b[3] = bv.w;
-      }
-    } else {
-      for (int k = 0; k < 4; ++k) {
-        g[k] = 0.f; b[k] = 0.f;
-        if (k < cnt) {
-          g[k] = gbf ? bf16_bits_to_float(gld<uint16_t>(static_cast<const uint16_t*>(d.G) + e + k))
-                     : gld<float>(static_cast<const float*>(d.G) + e + k);
-          if (!ortho) b[k] = gld<float>(B + e + k);
+        for (int q = 0; q < cnt; ++q) {
+          g[q] = gbf ? bf16_bits_to_float(gld<uint16_t>(static_cast<const uint16_t*>(d.G) + e + q))
+                     : gld<float>(static_cast<const float*>(d.G) + e + q);
+          if (!ortho) b[q] = gld<float>(d.B + e + q);
         }
       }
-    }
-    float mval[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (ortho) {
-        mval[k] = g[k];
-      } else {
-        b[k] = fmaf(mu, b[k], g[k]);
-        mval[k] = nest ? fmaf(mu, b[k], g[k]) : b[k];
+      for (int q = 0; q < 4; ++q) {
+        if (ortho) {
+          mv[q] = g[q];
+        } else {
+          b[q] = fmaf(mu, b[q], g[q]);
+          mv[q] = nest ? fmaf(mu, b[q], g[q]) : b[q];
+        }
       }
-    }
-    if (!ortho) {
-      if (cnt == 4) {
-        gst(B + e, make_float4(b[0], b[1], b[2], b[3]));
-      } else {
-        for (int k = 0; k < cnt; ++k) gst(B + e + k, b[k]);
+      if (!ortho) {
+        if (vec && cnt == 4) {
+          gst(d.B + e, make_float4(b[0], b[1], b[2], b[3]));
+        } else {
+          for (int q = 0; q < cnt; ++q) gst(d.B + e + q, b[q]);
+        }
       }
+      // Elements past the last column stay zero (the loads above left g, b
+      // zero there).
+      for (int q = cnt; q < 4; ++q) mv[q] = 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc = fmaf(mval[k], mval[k], acc);
-      bad |= (__float_as_uint(mval[k]) & 0x7f800000u) == 0x7f800000u;
+    for (int q = 0; q < 4; ++q) {
+      acc = fmaf(mv[q], mv[q], acc);
+      bad |= (__float_as_uint(mv[q]) & 0x7f800000u) == 0x7f800000u;
+      tile[rl][tx * 4 + q] = mv[q];
     }
   }
   __shared__ float red[4];
@@ -118,12 +159,18 @@ __global__ __launch_bounds__(256) void momentum_norm_kernel(const MatDesc* __res
     __syncthreads();
   }
   if (threadIdx.x == 0) gst(d.partials + local, ((red[0] + red[1]) + red[2]) + red[3]);
+  if (fold) write_pair_tile(d, tile, i0, j0, 1.f, tr);
 }
 
 // ---------------------------------------------------------------- norm
-// One work-group per matrix: fixed-order float64 sum of the block partials,
-// then sigma = 1 / (sqrt(sum) + eps).  With diagnostics it also keeps
-// ||M||_F and the OR of the blocks' non-finite flags in mstat.
+// One work-group per matrix: fixed-order float64 sum of the tile partials,
+// then sigma = 1 / (sqrt(sum) + eps).  A folded matrix (kFold) keeps its
+// unnormalised pair when ||M||_F lies in [2^-50, 2^50] and the first
+// iteration multiplies by sigma (first_scale = sigma); outside that range
+// (where the unnormalised Gram product could lose range in float32) or for
+// a matrix that is not folded, the prep pass writes sigma * M instead
+// (prep = 1, first_scale = 1).  With diagnostics it also keeps ||M||_F and
+// the OR of the tiles' non-finite flags in mstat.
 __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ descs, float eps) {
   const MatDesc d = descs[blockIdx.x];
   const int nb = d.mom_blocks;
@@ -146,7 +193,11 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
   }
   if (threadIdx.x == 0) {
     const double nrm = sqrt(red[0]);
-    gst(d.sigma, static_cast<float>(1.0 / (nrm + static_cast<double>(eps))));
+    const float sigma = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
+    const bool keep = (d.flags & kFold) && nrm >= 0x1p-50 && nrm <= 0x1p50;
+    gst(d.sigma, sigma);
+    gst(d.sigma + kSigFirst, keep ? sigma : 1.f);
+    gst(d.sigma + kSigPrep, __int_as_float(keep ? 0 : 1));
     if (diag) {
       gst(d.mstat, static_cast<float>(nrm));
       gst(d.mstat + 1, __int_as_float(any_bad ? 1 : 0));
@@ -156,101 +207,88 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
 
 // ---------------------------------------------------------------- prep
 // X = sigma * M in the short-side-major padded layout (transposed when
-// rows > cols), split into bf16 high part and bf16 residual.  Padding is
-// written as zeros.  One 64x64 tile of X per work-group.
+// rows > cols), split into bf16 high part and bf16 residual (or float32 for
+// the small-Gram path); padding is written as zeros.  Only for the matrices
+// the norm pass marked (prep = 1): the work-groups walk the matrices in
+// order and share each marked matrix's 64x64 tiles, so a call whose
+// matrices all keep their folded pair costs one pass over the flags.
 __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ descs,
-                                                   const int32_t* __restrict__ prefix, int nmats,
-                                                   float mu) {
-  const int blk = blockIdx.x;
-  const int mi = find_mat(prefix, nmats, blk);
-  const MatDesc d = descs[mi];
-  const int local = blk - prefix[mi];
-  // The padded extents are multiples of 32 but not always of 64: the last
-  // tile row / column is partial and every write below is masked to them
-  // (4-element groups never straddle a padded edge).
-  const int tpr = (d.n_pad + kEwTile - 1) / kEwTile;
-  const int i0 = (local / tpr) * kEwTile;  // X rows (short side)
-  const int j0 = (local % tpr) * kEwTile;  // X cols (long side)
-  const int m_pad = d.m_pad, n_pad = d.n_pad;
-  const int flags = d.flags;
-  const bool tr = flags & kTransposed;
-  const bool ortho = flags & kOrthoOnly;
-  const bool gbf = flags & kGBf16;
-  const bool nest = flags & kNesterov;
-  const int64_t rows = d.rows, cols = d.cols;
-  // Region of M (original orientation) that feeds this X tile.
-  const int64_t r0 = tr ? j0 : i0;
-  const int64_t c0 = tr ? i0 : j0;
-  const float sigma = gld<float>(d.sigma);
+                                                   const int32_t* __restrict__ prefix, int nmats, float mu) {
   __shared__ float tile[kEwTile][kEwTile + 1];
   const int tx = threadIdx.x & 15;   // column group of 4
   const int ty = threadIdx.x >> 4;   // 0..15
+  // Common case first: no matrix marked (one parallel pass over the flags).
+  int any = 0;
+  for (int mi = threadIdx.x; mi < nmats; mi += 256) any |= __float_as_int(gld<float>(descs[mi].sigma + kSigPrep));
+  if (!__syncthreads_or(any)) return;
+  for (int mi = 0; mi < nmats; ++mi) {
+    if (__float_as_int(gld<float>(descs[mi].sigma + kSigPrep)) == 0) continue;
+    const MatDesc d = descs[mi];
+    const int ntiles = prefix[mi + 1] - prefix[mi];
+    const int tpr = (d.n_pad + kEwTile - 1) / kEwTile;
+    const int flags = d.flags;
+    const bool tr = flags & kTransposed;
+    const bool ortho = flags & kOrthoOnly;
+    const bool gbf = flags & kGBf16;
+    const bool nest = flags & kNesterov;
+    const int64_t rows = d.rows, cols = d.cols;
+    const float sigma = gld<float>(d.sigma);
+    for (int local = blockIdx.x; local < ntiles; local += gridDim.x) {
+      const int i0 = (local / tpr) * kEwTile;
+      const int j0 = (local % tpr) * kEwTile;
+      const int64_t r0 = tr ? j0 : i0;
+      const int64_t c0 = tr ? i0 : j0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int rl = ty + 16 * k;
-    const int64_t r = r0 + rl;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows) {
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int64_t c = c0 + tx * 4 + c4;
-        if (c < cols) {
-          const int64_t e = r * cols + c;
-          float mval;
-          if (ortho) {
-            mval = gld<float>(static_cast<const float*>(d.G) + e);
-          } else {
-            const float bval = gld<float>(d.B + e);
-            if (nest) {
-              const float g = gbf ? bf16_bits_to_float(gld<uint16_t>(static_cast<const uint16_t*>(d.G) + e))
-                                  : gld<float>(static_cast<const float*>(d.G) + e);
-              mval = fmaf(mu, bval, g);
-            } else {
-              mval = bval;
+      for (int k = 0; k < 4; ++k) {
+        const int rl = ty + 16 * k;
+        const int64_t r = r0 + rl;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < rows) {
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const int64_t c = c0 + tx * 4 + c4;
+            if (c < cols) {
+              const int64_t e = r * cols + c;
+              float mval;
+              if (ortho) {
+                mval = gld<float>(static_cast<const float*>(d.G) + e);
+              } else {
+                const float bval = gld<float>(d.B + e);
+                if (nest) {
+                  const float g = gbf ? bf16_bits_to_float(gld<uint16_t>(static_cast<const uint16_t*>(d.G) + e))
+                                      : gld<float>(static_cast<const float*>(d.G) + e);
+                  mval = fmaf(mu, bval, g);
+                } else {
+                  mval = bval;
+                }
+              }
+              v[c4] = mval;
             }
           }
-          v[c4] = mval;
         }
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) tile[rl][tx * 4 + c4] = v[c4];
       }
-    }
+      __syncthreads();
+      if (flags & kSmall) {
+        // Float32 iterate for the small-Gram path.
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) tile[rl][tx * 4 + c4] = v[c4];
-  }
-  __syncthreads();
-  if (flags & kSmall) {
-    // Float32 iterate for the small-Gram path.
+        for (int k = 0; k < 4; ++k) {
+          const int il = ty + 16 * k;
+          if (i0 + il >= d.m_pad || j0 + tx * 4 >= d.n_pad) continue;
+          float v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int il = ty + 16 * k;
-      if (i0 + il >= m_pad || j0 + tx * 4 >= n_pad) continue;
-      float v[4];
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int jl = tx * 4 + c4;
-        v[c4] = sigma * (tr ? tile[jl][il] : tile[il][jl]);
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const int jl = tx * 4 + c4;
+            v[c4] = sigma * (tr ? tile[jl][il] : tile[il][jl]);
+          }
+          const int64_t off = static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4;
+          gst(d.xf[0] + off, make_float4(v[0], v[1], v[2], v[3]));
+        }
+      } else {
+        write_pair_tile(d, tile, i0, j0, sigma, tr);
       }
-      const int64_t off = static_cast<int64_t>(i0 + il) * d.n_pad + j0 + tx * 4;
-      gst(d.xf[0] + off, make_float4(v[0], v[1], v[2], v[3]));
+      __syncthreads();  // the tile is rewritten by the next iteration
     }
-    return;
-  }
-  // X^T as the bf16 pair: row j of X^T holds column j of X.
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int jl = ty + 16 * k;
-    if (j0 + jl >= n_pad || i0 + tx * 4 >= m_pad) continue;
-    float x[4];
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const int il = tx * 4 + c4;
-      x[c4] = sigma * (tr ? tile[jl][il] : tile[il][jl]);
-    }
-    const uint32_t h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
-    const uint2 hv = make_uint2(h0, h1);
-    const uint2 lv = make_uint2(pack_bf16(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
-                                pack_bf16(x[2] - bf_lo(h1), x[3] - bf_hi(h1)));
-    const int64_t off = static_cast<int64_t>(j0 + jl) * d.m_pad + i0 + tx * 4;
-    gst(d.xt_hi[0] + off, hv);
-    gst(d.xt_lo[0] + off, lv);
   }
 }
 
@@ -384,7 +422,7 @@ __global__ __launch_bounds__(256) void diag_kernel(const MatDesc* __restrict__ d
 
 hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
                            hipStream_t s) {
-  hipLaunchKernelGGL(momentum_norm_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, mu);
+  hipLaunchKernelGGL(momentum_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, mu);
   return hipGetLastError();
 }
 
@@ -395,7 +433,10 @@ hipError_t launch_norm(const MatDesc* d, int nmats, float eps, hipStream_t s) {
 
 hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
                        hipStream_t s) {
-  hipLaunchKernelGGL(prep_kernel, dim3(total), dim3(256), 0, s, d, prefix, nmats, mu);
+  // Enough work-groups to fill the chip when every matrix needs the pass;
+  // each walks all matrices' flags.
+  const int grid = total < 4096 ? total : 4096;
+  hipLaunchKernelGGL(prep_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, d, prefix, nmats, mu);
   return hipGetLastError();
 }
 

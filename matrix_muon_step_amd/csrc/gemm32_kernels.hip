@@ -397,7 +397,7 @@ __device__ __forceinline__ void upd1(float* wp, float o, float ls, float lwd, bo
 template <class C, int MODE, int W, int NG, int W2, int NG2, bool MERGED>
 __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
                                         float* T, const XIn<NG>& x, int p0, int q0, DiagAcc& da,
-                                        XIn<(NG2 > 0 ? NG2 : 1)>& nx, int gi0n, int p0n) {
+                                        XIn<(NG2 > 0 ? NG2 : 1)>& nx, int gi0n, int p0n, float s1) {
   constexpr bool DG = MODE == BXD;
   const bool tr = d.flags & kTransposed;
   const bool ortho = d.flags & kOrthoOnly;
@@ -425,6 +425,10 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
     for (int q = 0; q < 4; ++q) {
       v[2 * q] = fmaf(kCoefA, bf_lo(hw[q]) + bf_lo(lw[q]), v[2 * q]);
       v[2 * q + 1] = fmaf(kCoefA, bf_hi(hw[q]) + bf_hi(lw[q]), v[2 * q + 1]);
+    }
+    if (s1 != 1.f) {  // first iteration on the unnormalised pair
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= s1;
     }
     const int gj = wj0 + jl;
     const int gi = gi0 + il;
@@ -523,7 +527,7 @@ __device__ __forceinline__ void bx_stage_unit(int lane, const f32x16_t (&acc)[C:
 template <class C, int MODE, int PH, int K>
 __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
                                          const f32x16_t (&acc)[C::BMB][C::BNB],
-                                         const XIn<Units<C, PH>::width(K) / 8>& cur, DiagAcc& da) {
+                                         const XIn<Units<C, PH>::width(K) / 8>& cur, DiagAcc& da, float s1) {
   using U = Units<C, PH>;
   constexpr int W = U::width(K);
   const int gi0 = wi0 + 32 * U::start(K);
@@ -531,12 +535,12 @@ __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, i
     constexpr int W2 = U::width(K + 1);
     XIn<W2 / 8> nxt;
     bx_pass<C, MODE, W, W / 8, W2, W2 / 8, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, nxt,
-                                                  wi0 + 32 * U::start(K + 1), 0);
+                                                  wi0 + 32 * U::start(K + 1), 0, s1);
     bx_stage_unit<C, PH, K + 1>(lane, acc, T);
-    bx_units<C, MODE, PH, K + 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da);
+    bx_units<C, MODE, PH, K + 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da, s1);
   } else {
     XIn<1> none;
-    bx_pass<C, MODE, W, W / 8, 32, 0, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, none, 0, 0);
+    bx_pass<C, MODE, W, W / 8, 32, 0, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, none, 0, 0, s1);
   }
 }
 
@@ -545,14 +549,14 @@ __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, i
 // requested, then the units run in turn.
 template <class C, int MODE, int PH>
 __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
-                                            const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da) {
+                                            const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da, float s1) {
   using U = Units<C, PH>;
   constexpr int W = U::width(0);
   bx_stage_unit<C, PH, 0>(lane, acc, T);
   XIn<W / 8> x0;
 #pragma unroll
   for (int q = 0; q < W / 8; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
-  bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da);
+  bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da, s1);
 }
 
 // The epilogue of a wave pair that splits a tile's Gram-side rows at an odd
@@ -567,7 +571,7 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
 template <class C, int MODE, int H>
 __device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane,
                                                    float* T, float* Tm, const f32x16_t (&acc)[C::BMB][C::BNB],
-                                                   DiagAcc& da) {
+                                                   DiagAcc& da, float s1) {
   static_assert(C::BMB == 5, "merged epilogue: two pairs and one shared block per wave");
   constexpr int I0 = H, I1 = H + 2, MB = H ? 0 : 4;
   const int g0 = wi0 + 32 * I0, g1 = wi0 + 32 * I1;
@@ -577,16 +581,16 @@ __device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, in
   XIn<8> x0, x1;
 #pragma unroll
   for (int q = 0; q < 8; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
-  bx_pass<C, MODE, 64, 8, 64, 8, false>(d, buf, m_pad, g0, wj0, lane, T, x0, 0, 0, da, x1, g1, 0);
+  bx_pass<C, MODE, 64, 8, 64, 8, false>(d, buf, m_pad, g0, wj0, lane, T, x0, 0, 0, da, x1, g1, 0, s1);
   bx_stage_acc<C>(lane, acc[I1], T);
   bx_stage_acc<C>(lane, acc[I1 + 1], T + 32);
   XIn<4> xm;
-  bx_pass<C, MODE, 64, 8, 64, 4, false>(d, buf, m_pad, g1, wj0, lane, T, x1, 0, 0, da, xm, gm, 4 * H);
+  bx_pass<C, MODE, 64, 8, 64, 4, false>(d, buf, m_pad, g1, wj0, lane, T, x1, 0, 0, da, xm, gm, 4 * H, s1);
   __syncthreads();
   bx_stage_acc<C>(lane, acc[MB], Tm + 32 * H);
   __syncthreads();
   XIn<1> none;
-  bx_pass<C, MODE, 64, 4, 32, 0, true>(d, buf, m_pad, gm, wj0, lane, Tm, xm, 4 * H, 4 * H, da, none, 0, 0);
+  bx_pass<C, MODE, 64, 4, 32, 0, true>(d, buf, m_pad, gm, wj0, lane, Tm, xm, 4 * H, 4 * H, da, none, 0, 0, s1);
 }
 
 // Epilogue of a symmetric product (Gram, polynomial) for one wave's sub-tile
@@ -607,7 +611,7 @@ __device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, in
 // gi <= gj only, so the two triangles hold bit-identical values.
 template <class C, int MODE, bool DIAG>
 __device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi0, int wj0, int lane, __bf16* slice,
-                                             const f32x16_t (&acc)[C::BMB][C::BNB]) {
+                                             const f32x16_t (&acc)[C::BMB][C::BNB], float gscale) {
   static_assert(C::BMB % 2 == 0 && C::WN == 64, "block pairs of 64 rows, 64-column wave tiles");
   constexpr int LD = C::SLICE_LD;
   constexpr int NIT = 64 * 8 / 64;     // 16-byte chunks per lane of a 64 x 64 slice
@@ -636,6 +640,12 @@ __device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi
           uint2* mp = reinterpret_cast<uint2*>(slice + (32 * j + col) * LD + 32 * h + 8 * g + rq);
           const f32x16_t& a = acc[2 * pr + h][j];
           float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          if constexpr (MODE == GRAM) {
+            // The first iteration's operand is the unnormalised pair
+            // (gscale = sigma^2), later ones 1.
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] *= gscale;
+          }
           if constexpr (MODE == POLY) {
             const uint2 av = *mp;  // A[gj][gi..gi+3] == A[gi..gi+3][gj]
             v[0] = fmaf(kCoefC, v[0], kCoefB * bf_lo(av.x));
@@ -702,7 +712,8 @@ __device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
-    const MatDesc* __restrict__ descs, const int32_t* __restrict__ prefix, int nmats, XcdSplit split, int buf) {
+    const MatDesc* __restrict__ descs, const int32_t* __restrict__ prefix, int nmats, XcdSplit split, int buf,
+    int first) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDSB];
 
   // XCD-aware work: XCD (block id % 8) walks its own cost-balanced
@@ -847,6 +858,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   // The epilogue reads the descriptor through the table: a copy (see
   // MatDesc) measured 1% slower here.
   const MatDesc& d = dr;
+  // First iteration: the iterate is the unnormalised pair of M; its Gram
+  // product is scaled by s1^2 and the BX result by s1 (s1 = sigma, or 1
+  // where the prep pass already normalised).
+  const float s1 = first ? gld<float>(d.sigma + kSigFirst) : 1.f;
 
   // ---- epilogue (wave-local).
   const int wi0 = ti * C::BM + wr * C::WM;   // first global row of the wave's sub-tile
@@ -858,24 +873,25 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       // The two waves of a column share the line at row WM - 32 of the tile.
       float* Tm = reinterpret_cast<float*>(smem) + wc * (C::SLICEB / 4);
       if (wr == 0)
-        bx_epilogue_merged<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da);
+        bx_epilogue_merged<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
       else
-        bx_epilogue_merged<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da);
+        bx_epilogue_merged<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
     } else if (((wi0 >> 5) & 1) == 0) {
       // Wave-uniform: whether the wave's first block starts a 64-row line.
-      bx_epilogue<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, da);
+      bx_epilogue<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, da, s1);
     } else {
-      bx_epilogue<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, da);
+      bx_epilogue<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, da, s1);
     }
     if constexpr (MODE == BXD) diag_flush(da, d.diag_part + local * C::NW + wave, lane);
     return;
   }
   if constexpr (MODE == GRAM || MODE == POLY) {
     __bf16* slice = reinterpret_cast<__bf16*>(smem) + wave * (C::SLICEB / 2);
+    const float gscale = (MODE == GRAM && first) ? s1 * s1 : 1.f;
     if (ti == tj)
-      sym_epilogue<C, MODE, true>(d, m_pad, wi0, wj0, lane, slice, acc);
+      sym_epilogue<C, MODE, true>(d, m_pad, wi0, wj0, lane, slice, acc, gscale);
     else
-      sym_epilogue<C, MODE, false>(d, m_pad, wi0, wj0, lane, slice, acc);
+      sym_epilogue<C, MODE, false>(d, m_pad, wi0, wj0, lane, slice, acc, gscale);
   }
 }
 
@@ -884,30 +900,32 @@ using W160 = G32<160, 256, 1, 4, 3>;
 using W320 = G32<320, 256, 2, 4, 4>;
 
 template <class C, int MODE>
-hipError_t launch(const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp, int buf, hipStream_t s) {
+hipError_t launch(const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp, int buf, int first,
+                  hipStream_t s) {
   if (sp.max_len <= 0) return hipSuccess;
-  hipLaunchKernelGGL((ns_gemm32_kernel<C, MODE>), dim3(8 * sp.max_len), dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+  hipLaunchKernelGGL((ns_gemm32_kernel<C, MODE>), dim3(8 * sp.max_len), dim3(C::kThreads), 0, s, d, prefix, nmats, sp,
+                     buf, first);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
-                            const XcdSplit& split, int buf, hipStream_t s) {
+                            const XcdSplit& split, int buf, int first, hipStream_t s) {
   if (cfg == kCfgG256) {
-    if (mode == GRAM) return launch<G256, GRAM>(d, prefix, nmats, split, buf, s);
-    if (mode == POLY) return launch<G256, POLY>(d, prefix, nmats, split, buf, s);
-    if (mode == BXM) return launch<G256, BXM>(d, prefix, nmats, split, buf, s);
-    if (mode == BXL) return launch<G256, BXL>(d, prefix, nmats, split, buf, s);
-    if (mode == BXD) return launch<G256, BXD>(d, prefix, nmats, split, buf, s);
+    if (mode == GRAM) return launch<G256, GRAM>(d, prefix, nmats, split, buf, first, s);
+    if (mode == POLY) return launch<G256, POLY>(d, prefix, nmats, split, buf, first, s);
+    if (mode == BXM) return launch<G256, BXM>(d, prefix, nmats, split, buf, first, s);
+    if (mode == BXL) return launch<G256, BXL>(d, prefix, nmats, split, buf, first, s);
+    if (mode == BXD) return launch<G256, BXD>(d, prefix, nmats, split, buf, first, s);
     return hipErrorInvalidValue;
   }
-  if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, s);
-  if (cfg == kCfgW160 && mode == BXL) return launch<W160, BXL>(d, prefix, nmats, split, buf, s);
-  if (cfg == kCfgW160 && mode == BXD) return launch<W160, BXD>(d, prefix, nmats, split, buf, s);
-  if (cfg == kCfgW320 && mode == BXM) return launch<W320, BXM>(d, prefix, nmats, split, buf, s);
-  if (cfg == kCfgW320 && mode == BXL) return launch<W320, BXL>(d, prefix, nmats, split, buf, s);
-  if (cfg == kCfgW320 && mode == BXD) return launch<W320, BXD>(d, prefix, nmats, split, buf, s);
+  if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, first, s);
+  if (cfg == kCfgW160 && mode == BXL) return launch<W160, BXL>(d, prefix, nmats, split, buf, first, s);
+  if (cfg == kCfgW160 && mode == BXD) return launch<W160, BXD>(d, prefix, nmats, split, buf, first, s);
+  if (cfg == kCfgW320 && mode == BXM) return launch<W320, BXM>(d, prefix, nmats, split, buf, first, s);
+  if (cfg == kCfgW320 && mode == BXL) return launch<W320, BXL>(d, prefix, nmats, split, buf, first, s);
+  if (cfg == kCfgW320 && mode == BXD) return launch<W320, BXD>(d, prefix, nmats, split, buf, first, s);
   return hipErrorInvalidValue;
 }
 

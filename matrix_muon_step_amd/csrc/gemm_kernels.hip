@@ -308,7 +308,7 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
 // gi <= gj only, so the two triangles hold bit-identical values.
 template <class C, int MODE, bool DIAG>
 __device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi0, int wj0, int lane, __bf16* slice,
-                                             const f32x4_t (&acc)[C::BMB][C::BNB]) {
+                                             const f32x4_t (&acc)[C::BMB][C::BNB], float gscale) {
   static_assert(C::EPI_ROWS == C::WM && C::WM == C::WN, "square wave tiles, staged whole");
   constexpr int LD = C::EPI_LD;
   constexpr int CPR = C::WM / 8;       // 16-byte chunks per slice row
@@ -342,7 +342,10 @@ __device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi
         v[2] = fmaf(kCoefC, acc[i][j][2], kCoefB * bf_lo(av.y));
         v[3] = fmaf(kCoefC, acc[i][j][3], kCoefB * bf_hi(av.y));
       } else {
-        v[0] = acc[i][j][0]; v[1] = acc[i][j][1]; v[2] = acc[i][j][2]; v[3] = acc[i][j][3];
+        // Gram: the first iteration's operand is the unnormalised pair
+        // (gscale = sigma^2), later ones 1.
+        v[0] = acc[i][j][0] * gscale; v[1] = acc[i][j][1] * gscale;
+        v[2] = acc[i][j][2] * gscale; v[3] = acc[i][j][3] * gscale;
       }
       w[i][j][0] = pack_bf16(v[0], v[1]);
       w[i][j][1] = pack_bf16(v[2], v[3]);
@@ -406,7 +409,7 @@ __device__ __forceinline__ void sym_epilogue(const MatDesc& d, int m_pad, int wi
 template <class C, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const MatDesc* __restrict__ descs,
                                                               const int32_t* __restrict__ prefix,
-                                                              int nmats, XcdSplit split, int buf) {
+                                                              int nmats, XcdSplit split, int buf, int first) {
   constexpr int T = C::T;
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[C::LDSB];
   __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
@@ -548,11 +551,16 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   const int wi0 = ti * T + wr * C::WM;      // first global row of the wave's sub-tile
   const int wj0 = tj * T + wc * C::WN;      // first global column
   __bf16* slice = smem + wave * (C::EPIB / 2);
+  // First iteration: the iterate is the unnormalised pair of M; its Gram
+  // product is scaled by s1^2 and the BX result by s1 (s1 = sigma, or 1
+  // where the prep pass already normalised).
+  const float s1 = first ? gld<float>(d.sigma + kSigFirst) : 1.f;
   if constexpr (MODE != BXM) {
+    const float gscale = (MODE == GRAM) ? s1 * s1 : 1.f;
     if (ti == tj)
-      sym_epilogue<C, MODE, true>(d, m_pad, wi0, wj0, lane, slice, acc);
+      sym_epilogue<C, MODE, true>(d, m_pad, wi0, wj0, lane, slice, acc, gscale);
     else
-      sym_epilogue<C, MODE, false>(d, m_pad, wi0, wj0, lane, slice, acc);
+      sym_epilogue<C, MODE, false>(d, m_pad, wi0, wj0, lane, slice, acc, gscale);
     return;
   }
   // BX: X' = a (X_hi + X_lo) + P X_hi, stored as the X^T pair straight from
@@ -589,6 +597,10 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
         v[1] = fmaf(kCoefA, bf_hi(hx.x) + bf_hi(lx.x), acc[ib][j][1]);
         v[2] = fmaf(kCoefA, bf_lo(hx.y) + bf_lo(lx.y), acc[ib][j][2]);
         v[3] = fmaf(kCoefA, bf_hi(hx.y) + bf_hi(lx.y), acc[ib][j][3]);
+        if (s1 != 1.f) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] *= s1;
+        }
         const uint32_t w0 = pack_bf16(v[0], v[1]);
         const uint32_t w1 = pack_bf16(v[2], v[3]);
         const uint32_t l0 = pack_bf16(v[0] - bf_lo(w0), v[1] - bf_hi(w0));
@@ -607,15 +619,15 @@ using C128 = Cfg<128, 2, 2, 4>;
 
 template <class C>
 hipError_t launch_mode(int mode, const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp,
-                       int buf, hipStream_t s) {
+                       int buf, int first, hipStream_t s) {
   if (sp.max_len <= 0) return hipSuccess;
   const dim3 grid(8 * sp.max_len);
   if (mode == GRAM)
-    hipLaunchKernelGGL((ns_gemm_kernel<C, GRAM>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+    hipLaunchKernelGGL((ns_gemm_kernel<C, GRAM>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf, first);
   else if (mode == POLY)
-    hipLaunchKernelGGL((ns_gemm_kernel<C, POLY>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+    hipLaunchKernelGGL((ns_gemm_kernel<C, POLY>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf, first);
   else
-    hipLaunchKernelGGL((ns_gemm_kernel<C, BXM>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf);
+    hipLaunchKernelGGL((ns_gemm_kernel<C, BXM>), grid, dim3(C::kThreads), 0, s, d, prefix, nmats, sp, buf, first);
   return hipGetLastError();
 }
 
@@ -624,9 +636,9 @@ hipError_t launch_mode(int mode, const MatDesc* d, const int32_t* prefix, int nm
 
 
 hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
-                          const XcdSplit& split, int buf, hipStream_t s) {
-  if (cfg == kCfgT160) return launch_mode<C160>(mode, d, prefix, nmats, split, buf, s);
-  if (cfg == kCfgT128) return launch_mode<C128>(mode, d, prefix, nmats, split, buf, s);
+                          const XcdSplit& split, int buf, int first, hipStream_t s) {
+  if (cfg == kCfgT160) return launch_mode<C160>(mode, d, prefix, nmats, split, buf, first, s);
+  if (cfg == kCfgT128) return launch_mode<C128>(mode, d, prefix, nmats, split, buf, first, s);
   return hipErrorInvalidValue;
 }
 

@@ -203,17 +203,19 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.bx_group = small ? 0 : bx_group(cfg);
     // The wide-tile BX kernels apply the update from their last launch.
     const bool fused = !small && ns_steps > 0 && cfg_wide(cfg.bx);
-    d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0) | (fused ? kFusedUpd : 0);
+    // The normalisation is folded into the first iteration where there is
+    // one and the iterate is the bf16 pair.
+    const bool fold = !small && ns_steps > 0;
+    d.flags = it.flags | (tr ? kTransposed : 0) | (small ? kSmall : 0) | (fused ? kFusedUpd : 0) |
+              (fold ? kFold : 0);
     d.lr_scale = it.lr_scale;
     d.lr_wd = it.lr_wd;
     d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
-    const int64_t elems = it.rows * it.cols;
-    d.mom_blocks = static_cast<int32_t>((elems + kMomChunk - 1) / kMomChunk);
-    total_partials += d.mom_blocks;
-
     int64_t work[kNumTables] = {};
-    work[kTabMom] = d.mom_blocks;
     work[kTabPrep] = ((d.m_pad + kEwTile - 1) / kEwTile) * ((d.n_pad + kEwTile - 1) / kEwTile);
+    work[kTabMom] = work[kTabPrep];  // one momentum work-group per 64x64 tile of padded X
+    d.mom_blocks = static_cast<int32_t>(work[kTabMom]);
+    total_partials += d.mom_blocks;
     work[kTabUpd] = fused ? 0 : ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
     if (small) {
       work[kTabSmallGram] = d.s_chunks;
@@ -239,7 +241,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
   const size_t partial_off = off;
   off += align_up(sizeof(float) * total_partials);
   const size_t sigma_off = off;
-  off += align_up(sizeof(float) * n);
+  off += align_up(sizeof(float) * 4 * n);
   const size_t bad_off = off;
   off += align_up(sizeof(int32_t) * total_partials);
   const size_t mstat_off = off;
@@ -252,7 +254,7 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.partials = reinterpret_cast<float*>(partial_off + sizeof(float) * pcur);
     d.mom_bad = reinterpret_cast<int32_t*>(bad_off + sizeof(int32_t) * pcur);
     pcur += d.mom_blocks;
-    d.sigma = reinterpret_cast<float*>(sigma_off + sizeof(float) * i);
+    d.sigma = reinterpret_cast<float*>(sigma_off + sizeof(float) * 4 * i);
     d.mstat = reinterpret_cast<float*>(mstat_off + sizeof(float) * 2 * i);
     d.diag_part = reinterpret_cast<DiagPart*>(slot_off + sizeof(DiagPart) * scur);
     scur += d.diag_slots;
@@ -535,8 +537,8 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
         for (int r = 0; r * len < full.max_len; ++r) {
           const XcdSplit sp = split_round(full, r, len);
           e = run_stage(kmode >= 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
-            return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, s)
-                        : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, s);
+            return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s)
+                        : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s);
           });
           if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
         }

@@ -52,8 +52,6 @@ constexpr int kCfgWaves[kNumCfg] = {8, 4, 4, 4, 8};            // waves per work
 constexpr bool cfg_wide(int c) { return c == kCfgG256 || c == kCfgW160 || c == kCfgW320; }
 // Tile edge of the layout kernels (normalise/transpose, update).
 constexpr int kEwTile = 64;
-// Elements per work-group of the momentum/norm kernel.
-constexpr int kMomChunk = 4096;
 // Matrices whose Gram side m is at most this take the float32 path: with so
 // few singular values the bf16 operand rounding does not average out, and
 // the Gram work is small enough for plain float32 arithmetic.
@@ -69,7 +67,13 @@ enum GFlags : int32_t {
   kSmall = 16,      // m <= kSmallGram: float32 iterate and Gram path
   kFusedUpd = 32,   // the last BX launch applies the update (no update_kernel work)
   kDiag = 64,       // collect the per-matrix diagnostics of this call
+  kFold = 128,      // the momentum pass writes the unnormalised pair; the
+                    // first iteration applies 1 / (||M||_F + eps)
 };
+
+// Per-matrix scalars after the norm pass (MatDesc::sigma[]).
+constexpr int kSigFirst = 1;  // scale the first iteration applies (sigma, or 1)
+constexpr int kSigPrep = 2;   // int bits: 1 = the prep pass writes sigma * M
 
 // Per-wave partial sums of the diagnostics, written by the kernel that
 // writes W (fused last BX or update pass); reduced in a fixed order.
@@ -124,15 +128,15 @@ struct MatDesc {
   float* xf[2];      // float32 iterate (small path), kSmallGram x n_pad
   float* sgram;      // small path: per-chunk partial Gram matrices
   float* spoly;      // small path: P, kSmallGram x kSmallGram float32
-  float* partials;   // per-block sums of squares of M
-  float* sigma;      // 1 / (||M||_F + eps)
+  float* partials;   // per-tile sums of squares of M
+  float* sigma;      // [0] 1 / (||M||_F + eps), [kSigFirst], [kSigPrep]
   int32_t* mom_bad;  // diagnostics: per momentum block, 1 if M holds a non-finite value
   float* mstat;      // diagnostics: [0] = ||M||_F, [1] = non-finite flag of M (int bits)
   DiagPart* diag_part;  // diagnostics: per-wave partials of the W-writing kernel
   int64_t rows, cols;
   int32_t m, n, m_pad, n_pad;
   int32_t flags;
-  int32_t mom_blocks;  // work-groups of the momentum kernel for this matrix
+  int32_t mom_blocks;  // work-groups (64x64 tiles of padded X) of the momentum kernel
   float lr_scale;      // lr * scale, formed in float32 on the host
   float lr_wd;         // lr * weight_decay (float32), 0 in orthogonalise-only mode
   int32_t s_chunks;    // small path: column chunks (n_pad / kSmallChunk)
@@ -178,10 +182,12 @@ hipError_t launch_diag(const MatDesc* d, int nmats, void* out, hipStream_t s);
 // also 3 = last BX with the update, 4 = the same with diagnostics) for the
 // matrices whose configuration for that stage is `cfg` (16x16 kernels:
 // T160, T128; 32x32 kernels: G256, W160).
+// `first`: the first iteration, whose Gram product is scaled by
+// sigma[kSigFirst]^2 and whose BX result by sigma[kSigFirst].
 hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
-                          const XcdSplit& split, int buf, hipStream_t s);
+                          const XcdSplit& split, int buf, int first, hipStream_t s);
 hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
-                            const XcdSplit& split, int buf, hipStream_t s);
+                            const XcdSplit& split, int buf, int first, hipStream_t s);
 hipError_t launch_small_gram(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
                              hipStream_t s);
 hipError_t launch_small_poly(const MatDesc* d, const int32_t* prefix, int nmats, int total,

@@ -279,6 +279,25 @@ def test_bf16_gradients_small(mm):
     check_step_results(*run_workload(mm, w), w.lr)
 
 
+@pytest.mark.parametrize("scale", [1e-18, 1e-12, 1.0, 1e10, 1e16])
+@pytest.mark.parametrize("shape", [(300, 520), (520, 300)])
+def test_gradient_scale_folded_and_normalised_paths(mm, shape, scale):
+    """The first iteration takes the unnormalised pair when ||M||_F lies in
+    [2^-50, 2^50] (scales 1e-12 .. 1e10 here, eps dominating the
+    normaliser at 1e-12) and the separately normalised one outside (1e-18,
+    1e16); both must match the oracle."""
+    log_case(f"gradient scale {scale:g} {shape}")
+    r, c = shape
+    G = (scale * synth.numpy_gradient(r, c, 8, 0.1, "f32", [74, r, c, 0]).astype(np.float64)).astype(np.float32)
+    W0 = np.zeros((r, c), np.float32)
+    Wd, Gd, Bd = dev(W0), dev(G), torch.zeros(r, c, dtype=torch.float32, device="cuda")
+    mm.muon_step([(Wd, Gd, Bd, 1.0)], mu=0.9, lr=0.5, ns_steps=5)
+    torch.cuda.synchronize()
+    Wref, _, _ = orc.muon_step(W0, G, np.zeros((r, c)), 0.9, 0.5)
+    assert np.isfinite(Wd.cpu().numpy()).all()
+    assert relfro(Wd.cpu().numpy(), Wref) <= NS_TOL
+
+
 def test_zero_gradient_leaves_weights(mm):
     log_case("zero gradient")
     Wd = dev(np.arange(12 * 20, dtype=np.float32).reshape(12, 20) * 1e-3)
