@@ -376,6 +376,19 @@ __device__ __forceinline__ void upd4(float* wp, float4 o, float ls, float lwd, b
   }
   gst(wp, nw);
 }
+// upd4 with the old W values already loaded (w).
+template <bool DG>
+__device__ __forceinline__ void upd4w(float* wp, float4 o, float4 w, float ls, float lwd, DiagAcc& da) {
+  const float4 nw = make_float4(fmaf(-ls, o.x, fmaf(-lwd, w.x, w.x)), fmaf(-ls, o.y, fmaf(-lwd, w.y, w.y)),
+                                fmaf(-ls, o.z, fmaf(-lwd, w.z, w.z)), fmaf(-ls, o.w, fmaf(-lwd, w.w, w.w)));
+  if constexpr (DG) {
+    diag_add(da, o.x, w.x, nw.x);
+    diag_add(da, o.y, w.y, nw.y);
+    diag_add(da, o.z, w.z, nw.z);
+    diag_add(da, o.w, w.w, nw.w);
+  }
+  gst(wp, nw);
+}
 template <bool DG>
 __device__ __forceinline__ void upd1(float* wp, float o, float ls, float lwd, bool ortho, DiagAcc& da) {
   if (ortho) {
@@ -448,9 +461,10 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
         float* wp = d.W + static_cast<int64_t>(gj) * d.cols + gi;
         if (gi + 7 < d.m && w16) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-            upd4<DG>(wp + 4 * h, make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]), ls, lwd,
-                     ortho, da);
+          for (int h = 0; h < 2; ++h) {
+            const float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+            upd4<DG>(wp + 4 * h, o, ls, lwd, ortho, da);
+          }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -471,28 +485,50 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
   // wrote back (uniform over the work-group: one matrix per tile).
   if constexpr (MERGED) __syncthreads();
   asm volatile("" ::: "memory");
-  // X-major pass
+  // X-major pass (non-transposed matrix, last iteration: W[gi][gj .. gj+7]),
+  // WB row groups at a time: their rows of W are all requested before the
+  // first of them is written (WB = 1 with diagnostics, whose sums take the
+  // registers).
+  constexpr int WB = DG ? 1 : 2;
+  static_assert(NG % WB == 0, "X-major pass in batches of WB row groups");
 #pragma unroll
-  for (int q = 0; q < NG; ++q) {
-    const int il = (q0 + q) * 8 + (lane & 7);
-    const int jl = (lane >> 3) * 8;
-    float v[8];
+  for (int qb = 0; qb < NG; qb += WB) {
+    float4 wv[WB][2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = T[(jl + e) * C::TP + il];
-    const int gi = gi0 + il;
-    const int gj = wj0 + jl;
-    if (gi < d.m) {
-      // non-transposed matrix, last iteration: W[gi][gj .. gj+7]
-      float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
-      if (gj + 7 < d.n && w16) {
+    for (int qq = 0; qq < WB; ++qq) {
+      const int il = (q0 + qb + qq) * 8 + (lane & 7);
+      const int gi = gi0 + il, gj = wj0 + (lane >> 3) * 8;
+      if (!ortho && gi < d.m && gj + 7 < d.n && w16) {
+        const float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
+        wv[qq][0] = gld<float4>(wp);
+        wv[qq][1] = gld<float4>(wp + 4);
+      }
+    }
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          upd4<DG>(wp + 4 * h, make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]), ls, lwd,
-                   ortho, da);
-      } else {
+    for (int qq = 0; qq < WB; ++qq) {
+      const int il = (q0 + qb + qq) * 8 + (lane & 7);
+      const int jl = (lane >> 3) * 8;
+      float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (gj + e < d.n) upd1<DG>(wp + e, v[e], ls, lwd, ortho, da);
+      for (int e = 0; e < 8; ++e) v[e] = T[(jl + e) * C::TP + il];
+      const int gi = gi0 + il;
+      const int gj = wj0 + jl;
+      if (gi < d.m) {
+        float* wp = d.W + static_cast<int64_t>(gi) * d.cols + gj;
+        if (gj + 7 < d.n && w16) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float4 o = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+            if (ortho)
+              gst(wp + 4 * h, o);
+            else
+              upd4w<DG>(wp + 4 * h, o, wv[qq][h], ls, lwd, da);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gj + e < d.n) upd1<DG>(wp + e, v[e], ls, lwd, ortho, da);
+        }
       }
     }
   }
