@@ -171,7 +171,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
 // a matrix that is not folded, the prep pass writes sigma * M instead
 // (prep = 1, first_scale = 1).  With diagnostics it also keeps ||M||_F and
 // the OR of the tiles' non-finite flags in mstat.
-__global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ descs, float eps) {
+__global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ descs, float eps,
+                                                   int32_t* __restrict__ prep_count) {
   const MatDesc d = descs[blockIdx.x];
   const int nb = d.mom_blocks;
   double s = 0.0;
@@ -198,6 +199,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
     gst(d.sigma, sigma);
     gst(d.sigma + kSigFirst, keep ? sigma : 1.f);
     gst(d.sigma + kSigPrep, __int_as_float(keep ? 0 : 1));
+    if (!keep) atomicAdd(prep_count, 1);  // the call's count of marked matrices (zeroed by the upload)
     if (diag) {
       gst(d.mstat, static_cast<float>(nrm));
       gst(d.mstat + 1, __int_as_float(any_bad ? 1 : 0));
@@ -209,22 +211,23 @@ __global__ __launch_bounds__(256) void norm_kernel(const MatDesc* __restrict__ d
 // X = sigma * M in the short-side-major padded layout (transposed when
 // rows > cols), split into bf16 high part and bf16 residual (or float32 for
 // the small-Gram path); padding is written as zeros.  Only for the matrices
-// the norm pass marked (prep = 1): the work-groups walk the matrices in
-// order and share each marked matrix's 64x64 tiles, so a call whose
-// matrices all keep their folded pair costs one pass over the flags.
+// the norm pass marked (prep = 1): when none is marked (the count the norm
+// pass kept is zero) every work-group returns at once; otherwise the
+// work-groups stride over the 64x64 tiles of all matrices and skip the
+// tiles of unmarked ones.
 __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ descs,
-                                                   const int32_t* __restrict__ prefix, int nmats, float mu) {
+                                                   const int32_t* __restrict__ prefix, int nmats, float mu,
+                                                   const int32_t* __restrict__ prep_count) {
   __shared__ float tile[kEwTile][kEwTile + 1];
   const int tx = threadIdx.x & 15;   // column group of 4
   const int ty = threadIdx.x >> 4;   // 0..15
-  // Common case first: no matrix marked (one parallel pass over the flags).
-  int any = 0;
-  for (int mi = threadIdx.x; mi < nmats; mi += 256) any |= __float_as_int(gld<float>(descs[mi].sigma + kSigPrep));
-  if (!__syncthreads_or(any)) return;
-  for (int mi = 0; mi < nmats; ++mi) {
+  if (gld<int32_t>(prep_count) == 0) return;
+  const int total = prefix[nmats];
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int mi = find_mat(prefix, nmats, t);
     if (__float_as_int(gld<float>(descs[mi].sigma + kSigPrep)) == 0) continue;
     const MatDesc d = descs[mi];
-    const int ntiles = prefix[mi + 1] - prefix[mi];
+    const int local = t - prefix[mi];
     const int tpr = (d.n_pad + kEwTile - 1) / kEwTile;
     const int flags = d.flags;
     const bool tr = flags & kTransposed;
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const MatDesc* __restrict__ d
     const bool nest = flags & kNesterov;
     const int64_t rows = d.rows, cols = d.cols;
     const float sigma = gld<float>(d.sigma);
-    for (int local = blockIdx.x; local < ntiles; local += gridDim.x) {
+    {
       const int i0 = (local / tpr) * kEwTile;
       const int j0 = (local % tpr) * kEwTile;
       const int64_t r0 = tr ? j0 : i0;
@@ -426,17 +429,16 @@ hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, i
   return hipGetLastError();
 }
 
-hipError_t launch_norm(const MatDesc* d, int nmats, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(norm_kernel, dim3(nmats), dim3(256), 0, s, d, eps);
+hipError_t launch_norm(const MatDesc* d, int nmats, float eps, int32_t* prep_count, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(nmats), dim3(256), 0, s, d, eps, prep_count);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
-                       hipStream_t s) {
-  // Enough work-groups to fill the chip when every matrix needs the pass;
-  // each walks all matrices' flags.
+                       const int32_t* prep_count, hipStream_t s) {
+  // Enough work-groups to fill the chip when every matrix needs the pass.
   const int grid = total < 4096 ? total : 4096;
-  hipLaunchKernelGGL(prep_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, d, prefix, nmats, mu);
+  hipLaunchKernelGGL(prep_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, d, prefix, nmats, mu, prep_count);
   return hipGetLastError();
 }
 

@@ -169,7 +169,9 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
 
   size_t off = 0;
   off += align_up(sizeof(MatDesc) * n);
-  off += align_up(sizeof(int32_t) * kNumTables * (n + 1));
+  // prefix tables, then the call's count of matrices marked for the prep
+  // pass (uploaded as zero with the table)
+  off += align_up(sizeof(int32_t) * (kNumTables * (n + 1) + 1));
   plan.table_bytes = off;
 
   int64_t total_partials = 0;
@@ -515,9 +517,12 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   if (e != hipSuccess) return hip_fail(e, "descriptor upload");
   e = run_stage(MUON_STAGE_MOMENTUM, s, [&] { return launch_momentum(d_desc, ptab(kTabMom), n, ttot(kTabMom), mu, s); });
   if (e != hipSuccess) return hip_fail(e, "momentum launch");
-  e = run_stage(MUON_STAGE_NORM, s, [&] { return launch_norm(d_desc, n, eps, s); });
+  int32_t* d_prep_count = const_cast<int32_t*>(d_pre) + kNumTables * (n + 1);
+  e = run_stage(MUON_STAGE_NORM, s, [&] { return launch_norm(d_desc, n, eps, d_prep_count, s); });
   if (e != hipSuccess) return hip_fail(e, "norm launch");
-  e = run_stage(MUON_STAGE_PREP, s, [&] { return launch_prep(d_desc, ptab(kTabPrep), n, ttot(kTabPrep), mu, s); });
+  e = run_stage(MUON_STAGE_PREP, s, [&] {
+    return launch_prep(d_desc, ptab(kTabPrep), n, ttot(kTabPrep), mu, d_prep_count, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "prep launch");
   int buf = 0;
   static const int stage_of_mode[3] = {MUON_STAGE_GRAM, MUON_STAGE_POLY, MUON_STAGE_BX};

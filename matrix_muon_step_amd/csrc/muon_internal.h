@@ -170,9 +170,11 @@ struct XcdSplit {
 // range, which the device-side search skips.
 hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, int total,
                            float mu, hipStream_t s);
-hipError_t launch_norm(const MatDesc* d, int nmats, float eps, hipStream_t s);
+// prep_count: one int the norm pass increments per matrix it marks for the
+// prep pass (zero at the start of the call).
+hipError_t launch_norm(const MatDesc* d, int nmats, float eps, int32_t* prep_count, hipStream_t s);
 hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
-                       hipStream_t s);
+                       const int32_t* prep_count, hipStream_t s);
 hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
                          bool diag, hipStream_t s);
 // Final reduction of the diagnostics: one work-group per matrix writes out[i]

@@ -298,6 +298,31 @@ def test_gradient_scale_folded_and_normalised_paths(mm, shape, scale):
     assert relfro(Wd.cpu().numpy(), Wref) <= NS_TOL
 
 
+def test_many_small_matrices_grouped(mm):
+    """600 matrices in one call, mostly with a Gram side <= 64 (normalised by
+    the prep pass) and a few folded ones: every matrix against the oracle."""
+    log_case("600 mixed matrices, one call")
+    rng = np.random.default_rng(75)
+    shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 300))) for _ in range(590)]
+    shapes += [(int(rng.integers(65, 200)), int(rng.integers(65, 400))) for _ in range(10)]
+    host, mats = [], []
+    for i, (r, c) in enumerate(shapes):
+        if rng.random() < 0.5:
+            r, c = c, r
+        g = synth.numpy_gradient(r, c, 4, 0.1, "f32", [75, i, r, c])
+        host.append(g)
+        mats.append((dev(np.zeros((r, c), np.float32)), dev(g), torch.zeros(r, c, device="cuda"), 1.0))
+    mm.muon_step(mats, mu=0.9, lr=0.1, ns_steps=5)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for g, (Wd, _, _, _) in zip(host, mats):
+        ref, _, _ = orc.muon_step(np.zeros(g.shape), g, np.zeros(g.shape), 0.9, 0.1)
+        err = relfro(Wd.cpu().numpy(), ref)
+        worst = max(worst, err)
+        assert err <= NS_TOL, (g.shape, err)
+    print(f"  worst relFro {worst:.3e}")
+
+
 def test_zero_gradient_leaves_weights(mm):
     log_case("zero gradient")
     Wd = dev(np.arange(12 * 20, dtype=np.float32).reshape(12, 20) * 1e-3)
