@@ -24,9 +24,12 @@
  * iteration runs on bf16 matrix cores with float32 accumulation; A and P are
  * stored as bf16; the iterate X is carried as a pair of bf16 values (high
  * part and rounding residual) so that the linear term a*X keeps ~16
- * significant bits.  For m <= 64 (few singular values, where bf16 operand
- * rounding does not average out and the work is small) the iteration runs
- * in float32 throughout.
+ * significant bits.  The pair first holds M itself and the first
+ * iteration applies 1 / (||M||_F + eps) in its float32 epilogues (the Gram
+ * product scaled by its square), unless ||M||_F lies outside [2^-50, 2^50],
+ * where the pair holds the normalised M instead.  For m <= 64 (few singular
+ * values, where bf16 operand rounding does not average out and the work is
+ * small) the iteration runs in float32 throughout.
  *
  * Memory: every pointer passed to the step calls is a DEVICE pointer on the
  * current HIP device, except the descriptor arrays themselves (mats, hp and
@@ -212,9 +215,13 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
  * per stage to `ms` and the launch counts to `launches` (arrays of
  * MUON_STAGE_COUNT entries, caller-owned host memory), and clears them. */
 typedef enum muon_stage {
-  MUON_STAGE_MOMENTUM = 0, /* momentum + Frobenius partial sums        */
+  MUON_STAGE_MOMENTUM = 0, /* momentum, Frobenius partial sums and the */
+                           /* unnormalised bf16 pair (first iteration  */
+                           /* applies the normalisation)               */
   MUON_STAGE_NORM = 1,     /* per-matrix norm reduction                */
-  MUON_STAGE_PREP = 2,     /* normalise, transpose, split to bf16 pair */
+  MUON_STAGE_PREP = 2,     /* normalised iterate, only for matrices    */
+                           /* that cannot fold it (m <= 64, ns_steps 0,*/
+                           /* ||M||_F outside [2^-50, 2^50])           */
   MUON_STAGE_GRAM = 3,     /* A = X X^T (upper tiles + mirror)         */
   MUON_STAGE_POLY = 4,     /* P = b A + c A A (upper tiles + mirror)   */
   MUON_STAGE_BX = 5,       /* X = a X + P X                            */
