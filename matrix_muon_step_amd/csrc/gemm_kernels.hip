@@ -292,6 +292,38 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
   mfma16<C>(a, b, acc);
 }
 
+// The main loop of a wave whose sub-tile lies wholly below the diagonal of a
+// diagonal tile of a symmetric product: it does its share of the stage
+// loads, waits and barriers exactly as main_loop16 does, but no fragment
+// reads and no products (nothing of its sub-tile is stored), which leaves
+// its SIMD to the other work-group on the CU.
+template <class C, int PER>
+__device__ __forceinline__ void load_loop16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                            const int (&g_off)[C::QMAX], int kmul, int nk,
+                                            LAS unsigned char* lds, int wave) {
+#pragma unroll
+  for (int st = 0; st < C::NSTAGE; ++st)
+    if (st < nk) issue16<C>(Aop, Bop, g_off, wave, st * C::BK * kmul, lds + st * C::STAGEB);
+  {
+    const int newer = nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1;
+    if (newer >= 3) MUON_WAIT_VM(3 * PER);
+    else if (newer == 2) MUON_WAIT_VM(2 * PER);
+    else if (newer == 1) MUON_WAIT_VM(PER);
+    else MUON_WAIT_VM(0);
+  }
+  __builtin_amdgcn_s_barrier();
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int newer = (kt < nk - C::NSTAGE) ? C::NSTAGE - 2 : nk - 2 - kt;
+    if (newer >= 2) MUON_WAIT_VM(2 * PER);
+    else if (newer == 1) MUON_WAIT_VM(PER);
+    else MUON_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int fut = kt + C::NSTAGE;
+    if (fut < nk) issue16<C>(Aop, Bop, g_off, wave, fut * C::BK * kmul, lds + (kt % C::NSTAGE) * C::STAGEB);
+  }
+}
+
 // Epilogue of a symmetric product (Gram, polynomial) for one wave's sub-tile
 // (WM x WN, rows gi0 = wi0.., columns gj0 = wj0..), through the wave's LDS
 // slice so that every global access is 16 bytes per lane along a row:
@@ -541,9 +573,18 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
 
   const int nk = K / C::BK;
   LAS unsigned char* lds = (LAS unsigned char*)smem_raw;
-  if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
-  else main_loop16<C, 2 * (C::QMAX - 1), TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+  // On a diagonal tile of a symmetric product, a wave whose sub-tile lies
+  // wholly below the diagonal only loads (its results are never stored).
+  const bool below = (MODE != BXM) && ti == tj && wr * C::WM >= (wc + 1) * C::WN;
+  if (below) {
+    if (nq == C::QMAX) load_loop16<C, 2 * C::QMAX>(Aop, Bop, g_off, kmul, nk, lds, wave);
+    else load_loop16<C, 2 * (C::QMAX - 1)>(Aop, Bop, g_off, kmul, nk, lds, wave);
+  } else {
+    if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    else main_loop16<C, 2 * (C::QMAX - 1), TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+  }
   __syncthreads();
+  if (below) return;
 
   // ---- epilogue.  16x16 accumulator layout: lane holds column (lane & 15),
   // register r holds row 4 * (lane >> 4) + r.  Each wave works alone on its
