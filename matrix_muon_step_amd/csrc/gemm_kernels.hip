@@ -178,14 +178,16 @@ __device__ __forceinline__ bf16x8_t frag16(const LAS unsigned char* p, const LAS
   }
 }
 
-template <class C>
+// TRI: the wave's sub-tile sits on the diagonal of a symmetric product; the
+// 16x16 blocks below the diagonal (i > j) are never stored and skipped.
+template <class C, bool TRI>
 __device__ __forceinline__ void mfma16(const bf16x8_t (&a)[C::BMB], const bf16x8_t (&b)[C::BNB],
                                        f32x4_t (&acc)[C::BMB][C::BNB]) {
 #pragma unroll
   for (int i = 0; i < C::BMB; ++i)
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (!TRI || j >= i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
 // The products of one step with the next step's fragments read in place:
@@ -196,7 +198,27 @@ __device__ __forceinline__ void mfma16(const bf16x8_t (&a)[C::BMB], const bf16x8
 // `dst` (the slot just released) and `src` (the next stage) always differ;
 // __restrict__ lets the compiler order the LDS reads against the in-flight
 // direct-to-LDS loads without a blanket wait.
-template <class C, bool TR>
+// Scheduling groups of mfma_and_read16 (counts must be constants): rows
+// 0..BMB-2 as (row of products, A re-read); the last row as (product,
+// B re-read) pairs.  With TRI a row i holds BNB - i products.
+template <int I, int BMB, int BNB, int RPF, bool TRI>
+__device__ __forceinline__ void sched_rows16() {
+  if constexpr (I < BMB - 1) {
+    __builtin_amdgcn_sched_group_barrier(0x008, TRI ? BNB - I : BNB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
+    sched_rows16<I + 1, BMB, BNB, RPF, TRI>();
+  }
+}
+template <int J, int BMB, int BNB, int RPF, bool TRI>
+__device__ __forceinline__ void sched_last16() {
+  if constexpr (J < BNB) {
+    if constexpr (!TRI || J >= BMB - 1) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
+    sched_last16<J + 1, BMB, BNB, RPF, TRI>();
+  }
+}
+
+template <class C, bool TR, bool TRI>
 __device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                                 const int (&g_off)[C::QMAX], int wave, int koff, bool queue,
                                                 LAS unsigned char* __restrict__ dst,
@@ -209,29 +231,21 @@ __device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, 
   for (int i = 0; i < C::BMB - 1; ++i) {
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (!TRI || j >= i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     a[i] = frag16<C, TR>(src + f.a[i], src + f.a1[i]);
   }
   constexpr int L = C::BMB - 1;
 #pragma unroll
   for (int j = 0; j < C::BNB; ++j) {
-    acc[L][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[L], b[j], acc[L][j], 0, 0, 0);
+    if (!TRI || j >= L) acc[L][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[L], b[j], acc[L][j], 0, 0, 0);
     b[j] = frag16<C, TR>(src + f.b[j], src + f.b1[j]);
   }
   a[L] = frag16<C, TR>(src + f.a[L], src + f.a1[L]);
   // Keep that order: a row of products, then the re-read of its A fragment;
   // in the last row one product, then one B re-read.
   constexpr int RPF = TR ? 2 : 1;  // LDS reads per fragment
-#pragma unroll
-  for (int i = 0; i < C::BMB - 1; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, C::BNB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < C::BNB; ++j) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
-  }
+  sched_rows16<0, C::BMB, C::BNB, RPF, TRI>();
+  sched_last16<0, C::BMB, C::BNB, RPF, TRI>();
   __builtin_amdgcn_sched_group_barrier(0x100, RPF, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -241,7 +255,7 @@ __device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, 
 // of stage kt, barrier (stage kt+1 visible to all, stage kt free), refill
 // stage kt with step kt+NSTAGE, multiply while reading step kt+1's
 // fragments.
-template <class C, int PER, bool TR>
+template <class C, int PER, bool TR, bool TRI>
 __device__ __forceinline__ void step16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                        const int (&g_off)[C::QMAX], int kmul, int nk, int kt, int newer,
                                        LAS unsigned char* lds, int wave, const Frag16<C>& f,
@@ -254,14 +268,14 @@ __device__ __forceinline__ void step16(const __bf16* __restrict__ Aop, const __b
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   const int fut = kt + C::NSTAGE;
-  mfma_and_read16<C, TR>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk, lds + (kt % C::NSTAGE) * C::STAGEB,
+  mfma_and_read16<C, TR, TRI>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk, lds + (kt % C::NSTAGE) * C::STAGEB,
                          lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, f, a, b, acc);
 }
 
 // Main loop: the prologue fills every ring slot; steady steps keep
 // NSTAGE-2 later steps in flight with immediate wait counts; draining steps
 // stop refilling; the last step only multiplies.
-template <class C, int PER, bool TR>
+template <class C, int PER, bool TR, bool TRI>
 __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                             const int (&g_off)[C::QMAX], int kmul, int nk,
                                             LAS unsigned char* lds, int wave, const Frag16<C>& f,
@@ -286,10 +300,10 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
   for (int j = 0; j < C::BNB; ++j) b[j] = frag16<C, TR>(lds + f.b[j], lds + f.b1[j]);
   int kt = 0;
   for (; kt < nk - C::NSTAGE; ++kt)
-    step16<C, PER, TR>(Aop, Bop, g_off, kmul, nk, kt, C::NSTAGE - 2, lds, wave, f, a, b, acc);
+    step16<C, PER, TR, TRI>(Aop, Bop, g_off, kmul, nk, kt, C::NSTAGE - 2, lds, wave, f, a, b, acc);
   for (; kt + 1 < nk; ++kt)
-    step16<C, PER, TR>(Aop, Bop, g_off, kmul, nk, kt, nk - 2 - kt, lds, wave, f, a, b, acc);
-  mfma16<C>(a, b, acc);
+    step16<C, PER, TR, TRI>(Aop, Bop, g_off, kmul, nk, kt, nk - 2 - kt, lds, wave, f, a, b, acc);
+  mfma16<C, TRI>(a, b, acc);
 }
 
 // The main loop of a wave whose sub-tile lies wholly below the diagonal of a
@@ -579,9 +593,15 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   if (below) {
     if (nq == C::QMAX) load_loop16<C, 2 * C::QMAX>(Aop, Bop, g_off, kmul, nk, lds, wave);
     else load_loop16<C, 2 * (C::QMAX - 1)>(Aop, Bop, g_off, kmul, nk, lds, wave);
+  } else if (MODE != BXM && ti == tj && wr * C::WM == wc * C::WN) {
+    // A sub-tile on the diagonal: only its blocks with i <= j are stored.
+    if constexpr (C::WM == C::WN) {
+      if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+      else main_loop16<C, 2 * (C::QMAX - 1), TR, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    }
   } else {
-    if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
-    else main_loop16<C, 2 * (C::QMAX - 1), TR>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR, false>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    else main_loop16<C, 2 * (C::QMAX - 1), TR, false>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
   }
   __syncthreads();
   if (below) return;
