@@ -557,6 +557,14 @@ __device__ __forceinline__ void bx_stage_unit(int lane, const f32x16_t (&acc)[C:
   if constexpr (U::pair(K)) bx_stage_acc<C>(lane, acc[U::start(K) + 1], T + 32);
 }
 
+// Row groups of the first unit requested before the barrier that ends the
+// main loop (their latency overlaps the last products and the barrier);
+// the rest after its accumulators are staged.
+#ifndef MUON_BX_EARLY
+#define MUON_BX_EARLY 4
+#endif
+constexpr int kEarly = MUON_BX_EARLY;
+
 // Unit K is staged in T and its inputs are requested (or in flight): its
 // passes run while the next unit's inputs are requested, then the next
 // unit's accumulators go to T (after this unit's last read of T).
@@ -588,10 +596,14 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
                                             const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da, float s1) {
   using U = Units<C, PH>;
   constexpr int W = U::width(0);
-  bx_stage_unit<C, PH, 0>(lane, acc, T);
   XIn<W / 8> x0;
+  constexpr int E = kEarly < W / 8 ? kEarly : W / 8;
 #pragma unroll
-  for (int q = 0; q < W / 8; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
+  for (int q = 0; q < E; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
+  __syncthreads();  // every wave is done with the ring that T overlaps
+  bx_stage_unit<C, PH, 0>(lane, acc, T);
+#pragma unroll
+  for (int q = E; q < W / 8; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
   bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da, s1);
 }
 
@@ -612,11 +624,14 @@ __device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, in
   constexpr int I0 = H, I1 = H + 2, MB = H ? 0 : 4;
   const int g0 = wi0 + 32 * I0, g1 = wi0 + 32 * I1;
   const int gm = wi0 + 32 * MB - 32 * H;  // first column of the shared line
-  bx_stage_acc<C>(lane, acc[I0], T);
-  bx_stage_acc<C>(lane, acc[I0 + 1], T + 32);
   XIn<8> x0, x1;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
+  for (int q = 0; q < kEarly; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
+  __syncthreads();  // every wave is done with the ring that T overlaps
+  bx_stage_acc<C>(lane, acc[I0], T);
+  bx_stage_acc<C>(lane, acc[I0 + 1], T + 32);
+#pragma unroll
+  for (int q = kEarly; q < 8; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
   bx_pass<C, MODE, 64, 8, 64, 8, false>(d, buf, m_pad, g0, wj0, lane, T, x0, 0, 0, da, x1, g1, 0, s1);
   bx_stage_acc<C>(lane, acc[I1], T);
   bx_stage_acc<C>(lane, acc[I1 + 1], T + 32);
@@ -890,7 +905,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   if (per == PER_FULL) main_loop<C, PER_FULL, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   else main_loop<C, PER_FULL - 2, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-  __syncthreads();
+  // The epilogue's LDS tiles overlap the ring: a barrier first (the BX
+  // epilogues take it themselves, after requesting their first inputs).
+  if constexpr (MODE < BXM) __syncthreads();
   // The epilogue reads the descriptor through the table: a copy (see
   // MatDesc) measured 1% slower here.
   const MatDesc& d = dr;
