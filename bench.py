@@ -162,6 +162,27 @@ def cpu_baseline(w, budget_s=20.0):
             "seconds_measured": round(t_used, 3)}
 
 
+def copy_ceiling_gbps(dev, stream, nbytes=2**30, reps=5):
+    """Measured HBM ceiling for the bandwidth-bound kernels: a plain device
+    copy of nbytes (read + write), HIP events on the launch stream."""
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +331,7 @@ def main():
     ew = {
         "momentum_gbps": mom_bytes / (stage_ms["momentum"] * 1e-3) / 1e9 if stage_ms["momentum"] else None,
         "update_gbps": upd_bytes / (stage_ms["update"] * 1e-3) / 1e9 if stage_ms["update"] else None,
+        "copy_ceiling_gbps": copy_ceiling_gbps(dev, stream),
     }
 
     out = {
