@@ -51,11 +51,22 @@ def ns_flops(shapes, kind):
     return tot
 
 
+def _code_only(text):
+    """Source text without comments, blank lines or indentation changes:
+    what the compiler sees, so a comment edit does not void a record."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = (" ".join(ln.split()) for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash(names):
     h = hashlib.sha256()
     for nm in names:
-        with open(os.path.join(ROOT, "matrix_muon_step_amd", "csrc", nm), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "matrix_muon_step_amd", "csrc", nm), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,38 +9,42 @@
 //
 //   G256 : 256 x 256 output tile, 8 waves as 2 x 4, wave tile 128 x 64.
 //          Gram, polynomial (upper tiles) and BX.
-//   W160 : 160 x 256 output tile (160 rows on the Gram side m, 256 columns on
-//          the long side n), 4 waves as 1 x 4, wave tile 160 x 64.  BX only,
-//          for Gram sides that are multiples of 160 but not of 256.
+//   W320 : 320 x 256 output tile (320 rows on the Gram side m, 256 columns on
+//          the long side n), 8 waves as 2 x 4, wave tile 160 x 64.  BX only,
+//          for Gram sides that are multiples of 320 (m = 1600).
+//   W160 : 160 x 256 output tile, 4 waves as 1 x 4, wave tile 160 x 64.  BX
+//          only, for Gram sides that are multiples of 160 but not of 256 or
+//          320.
 //
 // A 32x32x16 MFMA does twice the work of a 16x16x32 one per instruction
 // and keeps the matrix pipe full from two waves per SIMD; wave tiles of
 // 128 x 64 / 160 x 64 read 12 / 14 KB of LDS fragments per 32-deep k-step
 // for 16 / 20 MFMAs.
 //
-// Main loop: a ring of three LDS stages (32 k each) is filled by
-// direct-to-LDS 16-byte loads issued two steps ahead.  Fragment reads are
-// ordinary LDS loads inside a step function whose stage pointers are
-// __restrict__ (the stage being filled and the stage being read are always
-// different ring slots), which lets the compiler order the reads against
-// the in-flight direct-to-LDS loads without a blanket wait.  Each wave
-// waits for its own loads (vmcnt) and a barrier publishes a stage.
-// Operand rows are 64 bytes in LDS with the four 16-byte k-chunks
-// XOR-swizzled by row ((r >> 1) ^ (r >> 2)): measured conflict-free on
-// gfx950 for the 32x32x16 and 16x16x32 fragment reads (the (r >> 1) ^
-// (r >> 3) form runs at half the LDS rate).  The swizzle repeats every 8
-// rows, so one base address per k16 half serves every fragment of a wave
-// (+2048 bytes per 32 rows).
+// Main loop: a ring of NSTAGE LDS stages (32 k each; 4 for G256 and W320,
+// 3 for W160) is filled by direct-to-LDS 16-byte loads: the slot a step
+// frees is refilled with the step NSTAGE later.  Fragment reads are ordinary LDS loads inside a step
+// function whose stage pointers are __restrict__ (the stage being filled
+// and the stage being read are always different ring slots), which lets
+// the compiler order the reads against the in-flight direct-to-LDS loads
+// without a blanket wait.  Each wave waits for its own loads (vmcnt) and a
+// barrier publishes a stage.  Operand rows are 64 bytes in LDS with the
+// four 16-byte k-chunks XOR-swizzled by row ((r >> 1) ^ (r >> 2)): measured
+// conflict-free on gfx950 for the 32x32x16 and 16x16x32 fragment reads (the
+// (r >> 1) ^ (r >> 3) form runs at half the LDS rate).  The swizzle repeats
+// every 8 rows, so one base address per k16 half serves every fragment of
+// a wave (+2048 bytes per 32 rows).
 //
 // Epilogues: a 32x32 accumulator holds, per lane, column (lane & 31) and
 // rows 8g + 4 (lane >> 5) + r (g, r = 0..3): four runs of four consecutive
-// rows.  Gram and polynomial tiles are stored transposed straight from
-// registers (8-byte writes, the mirror half) and row-major through a
-// private 32-row LDS slice per wave.  The BX epilogue (bx_epilogue) passes
+// rows.  Gram and polynomial tiles go through a private 64 x 64 LDS slice
+// per wave, which serves both the mirror half and the direct half of the
+// symmetric result (sym_epilogue).  The BX epilogue (bx_epilogue) passes
 // the float32 results through a wave-private LDS tile so that the X^T pair
-// and W are read and written 16 bytes per lane along contiguous rows.  The last BX of a step (mode BXL) applies the
-// parameter update of the synthesis note's section 4, W <- W - lr*scale*O,
-// from the float32 values directly; the iterate itself is not stored then.
+// and W are read and written 16 bytes per lane along contiguous rows.  The
+// last BX of a step (mode BXL) applies the parameter update of the
+// synthesis note's section 4, W <- W - lr*scale*O, from the float32 values
+// directly; the iterate itself is not stored then.
 #include "muon_internal.h"
 
 namespace muon {
