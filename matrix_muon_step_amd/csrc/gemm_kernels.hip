@@ -46,11 +46,14 @@
 // which keeps the operand panels of neighbouring tiles in that XCD's L2.
 //
 // Epilogue.  An MFMA accumulator holds four consecutive rows of one column,
-// so outputs stored transposed (xt_*, and the mirror half of a symmetric
-// tile) go straight from registers as 8-byte stores; the direct half of a
-// symmetric tile is staged through LDS one band of rows at a time and
-// written as 16-byte rows.  On diagonal tiles
-// each symmetric pair is written from the element with i <= j only.
+// so the BX outputs (rows of xt_*) go straight from registers as 8-byte
+// stores.  A symmetric tile goes through the wave's private LDS slice,
+// first in mirror layout (stored as the mirror half) and then row-major
+// (the direct half), 16 bytes per lane along rows (sym_epilogue).  On
+// diagonal tiles each symmetric pair is written from the element with
+// i <= j only, so both triangles hold the same bits, and the products that
+// would only feed elements below the diagonal are skipped (load_loop16,
+// mfma16 with TRI).
 #include "muon_internal.h"
 
 namespace muon {
