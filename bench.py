@@ -383,7 +383,11 @@ def main():
         "matrices_per_s": round(len(shapes) * 1000.0 / ms_per_step, 1),
         "stage_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
         "launches_per_step": launches,
-        "elementwise": {k: (round(v, 1) if v else None) for k, v in ew.items()},
+        "elementwise": dict(
+            {k: (round(v, 1) if v else None) for k, v in ew.items()},
+            momentum_frac_of_hbm_peak=round(ew["momentum_gbps"] / PEAK_HBM_GBPS, 4) if ew["momentum_gbps"] else None,
+            momentum_frac_of_copy_ceiling=(round(ew["momentum_gbps"] / ew["copy_ceiling_gbps"], 4)
+                                           if ew["momentum_gbps"] and ew["copy_ceiling_gbps"] else None)),
         "hbm_peak_gbps": PEAK_HBM_GBPS,
         "diagnostics": diag_info,
     }
