@@ -160,14 +160,21 @@ def torch_matrix(w: Workload, idx: int, step: int, device, generator=None) -> di
 
 
 # ---------------------------------------------------------------- special inputs
-def signed_partial_permutation(rows: int, cols: int, count: int, seed: Sequence[int]) -> np.ndarray:
-    """``count`` entries of +-1 at distinct positions, no two in one row or column."""
+def signed_partial_permutation_entries(rows: int, cols: int, count: int, seed: Sequence[int]):
+    """Row indices, column indices and signs of ``signed_partial_permutation``
+    (for building the matrix where it lives, e.g. on the GPU at large sizes)."""
     if count > min(rows, cols):
         raise ValueError("count exceeds min(rows, cols)")
     rng = np.random.default_rng(list(seed))
     r = rng.permutation(rows)[:count]
     c = rng.permutation(cols)[:count]
     s = rng.choice(np.array([-1.0, 1.0]), size=count)
+    return r, c, s
+
+
+def signed_partial_permutation(rows: int, cols: int, count: int, seed: Sequence[int]) -> np.ndarray:
+    """``count`` entries of +-1 at distinct positions, no two in one row or column."""
+    r, c, s = signed_partial_permutation_entries(rows, cols, count, seed)
     m = np.zeros((rows, cols), np.float32)
     m[r, c] = s
     return m

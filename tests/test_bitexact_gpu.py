@@ -76,6 +76,44 @@ def test_partial_permutation_five_steps(mm):
         assert mags[0] == scheme_scalar(2.0 ** -j, 5, fused=bool(pl["fused_update"]))
 
 
+# Maximum shapes the library accepts (MUON_MAX_GRAM x MUON_MAX_DIM, both
+# orientations) and the edges of the float32 small path at the maximum long
+# side.  The matrices are built on the GPU from the generator's entries.
+MAX_SHAPES = [(16384, 65536, 7), (65536, 16384, 7), (64, 65536, 3), (65, 65536, 3), (1, 65536, 0)]
+
+
+@pytest.mark.parametrize("shape", MAX_SHAPES)
+def test_partial_permutation_maximum_sizes(mm, shape):
+    """The partial-permutation check at the largest supported shapes: support
+    and signs exact, every nonzero magnitude bit-identical and equal to the
+    precision scheme's scalar value (float32 small path: within 1e-5 of
+    p^5(2^-j), its own rounding), no other element nonzero."""
+    r, c, j = shape
+    print(f"[case] partial permutation {r}x{c}, 4^{j} entries", flush=True)
+    ri, ci, si = synth.signed_partial_permutation_entries(r, c, 4 ** j, [62, r, c])
+    M = torch.zeros(r, c, dtype=torch.float32, device="cuda")
+    rt = torch.from_numpy(ri).cuda()
+    ct = torch.from_numpy(ci).cuda()
+    M[rt, ct] = torch.from_numpy(si.astype(np.float32)).cuda()
+    (O,) = mm.muon_orthogonalize([M], ns_steps=5, eps=0.0)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(O)) == 4 ** j
+    vals = O[rt, ct].cpu().numpy()
+    assert np.array_equal(np.sign(vals), si.astype(np.float32))
+    mags = np.abs(vals)
+    assert np.all(mags.view(np.uint32) == mags.view(np.uint32)[0])
+    _, plans = mm.muon_plan_query([(r, c)])
+    if plans[0]["tile"]:
+        assert mags[0] == scheme_scalar(2.0 ** -j, 5, fused=bool(plans[0]["fused_update"]))
+    else:
+        x = 2.0 ** -j
+        for _ in range(5):
+            x = 3.4445 * x - 4.7750 * x ** 3 + 2.0315 * x ** 5
+        assert abs(mags[0] - x) <= 1e-5 * x
+    del M, O
+    torch.cuda.empty_cache()
+
+
 def _bf16(x):
     return np.float32(torch.tensor(float(x), dtype=torch.float32).to(torch.bfloat16).float().item())
 
