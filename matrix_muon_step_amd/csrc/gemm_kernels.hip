@@ -151,8 +151,10 @@ struct Frag16 {
   int b1[C::BNB];
 };
 
-// Direct-to-LDS loads of one step into `dst` (both operands).
-template <class C>
+// Direct-to-LDS loads of one step into `dst` (both operands; SELF: the A
+// operand only, for a diagonal tile of a symmetric product, whose B operand
+// is the same panel and is read from the A half of the stage).
+template <class C, bool SELF>
 __device__ __forceinline__ void issue16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                         const int (&g_off)[C::QMAX], int wave, int koff,
                                         LAS unsigned char* __restrict__ dst) {
@@ -162,8 +164,9 @@ __device__ __forceinline__ void issue16(const __bf16* __restrict__ Aop, const __
     if (i < C::QMAX - 1 || q < C::QN) {
       __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + g_off[i] + koff), (LAS void*)(dst + q * 1024), 16,
                                        0, 0);
-      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + koff),
-                                       (LAS void*)(dst + C::OPB + q * 1024), 16, 0, 0);
+      if constexpr (!SELF)
+        __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + g_off[i] + koff),
+                                         (LAS void*)(dst + C::OPB + q * 1024), 16, 0, 0);
     }
   }
 }
@@ -221,14 +224,14 @@ __device__ __forceinline__ void sched_last16() {
   }
 }
 
-template <class C, bool TR, bool TRI>
+template <class C, bool TR, bool TRI, bool SELF>
 __device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                                 const int (&g_off)[C::QMAX], int wave, int koff, bool queue,
                                                 LAS unsigned char* __restrict__ dst,
                                                 const LAS unsigned char* __restrict__ src, const Frag16<C>& f,
                                                 bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB],
                                                 f32x4_t (&acc)[C::BMB][C::BNB]) {
-  if (queue) issue16<C>(Aop, Bop, g_off, wave, koff, dst);
+  if (queue) issue16<C, SELF>(Aop, Bop, g_off, wave, koff, dst);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < C::BMB - 1; ++i) {
@@ -258,7 +261,7 @@ __device__ __forceinline__ void mfma_and_read16(const __bf16* __restrict__ Aop, 
 // of stage kt, barrier (stage kt+1 visible to all, stage kt free), refill
 // stage kt with step kt+NSTAGE, multiply while reading step kt+1's
 // fragments.
-template <class C, int PER, bool TR, bool TRI>
+template <class C, int PER, bool TR, bool TRI, bool SELF>
 __device__ __forceinline__ void step16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                        const int (&g_off)[C::QMAX], int kmul, int nk, int kt, int newer,
                                        LAS unsigned char* lds, int wave, const Frag16<C>& f,
@@ -271,14 +274,14 @@ __device__ __forceinline__ void step16(const __bf16* __restrict__ Aop, const __b
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   const int fut = kt + C::NSTAGE;
-  mfma_and_read16<C, TR, TRI>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk, lds + (kt % C::NSTAGE) * C::STAGEB,
+  mfma_and_read16<C, TR, TRI, SELF>(Aop, Bop, g_off, wave, fut * C::BK * kmul, fut < nk, lds + (kt % C::NSTAGE) * C::STAGEB,
                          lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, f, a, b, acc);
 }
 
 // Main loop: the prologue fills every ring slot; steady steps keep
 // NSTAGE-2 later steps in flight with immediate wait counts; draining steps
 // stop refilling; the last step only multiplies.
-template <class C, int PER, bool TR, bool TRI>
+template <class C, int PER, bool TR, bool TRI, bool SELF>
 __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                             const int (&g_off)[C::QMAX], int kmul, int nk,
                                             LAS unsigned char* lds, int wave, const Frag16<C>& f,
@@ -286,7 +289,7 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
   static_assert(C::NSTAGE >= 3 && C::NSTAGE <= 4, "wait counts assume 3 or 4 stages");
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
-    if (st < nk) issue16<C>(Aop, Bop, g_off, wave, st * C::BK * kmul, lds + st * C::STAGEB);
+    if (st < nk) issue16<C, SELF>(Aop, Bop, g_off, wave, st * C::BK * kmul, lds + st * C::STAGEB);
   {
     const int newer = nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1;
     if (newer >= 3) MUON_WAIT_VM(3 * PER);
@@ -303,15 +306,16 @@ __device__ __forceinline__ void main_loop16(const __bf16* __restrict__ Aop, cons
   for (int j = 0; j < C::BNB; ++j) b[j] = frag16<C, TR>(lds + f.b[j], lds + f.b1[j]);
   int kt = 0;
   for (; kt < nk - C::NSTAGE; ++kt)
-    step16<C, PER, TR, TRI>(Aop, Bop, g_off, kmul, nk, kt, C::NSTAGE - 2, lds, wave, f, a, b, acc);
+    step16<C, PER, TR, TRI, SELF>(Aop, Bop, g_off, kmul, nk, kt, C::NSTAGE - 2, lds, wave, f, a, b, acc);
   for (; kt + 1 < nk; ++kt)
-    step16<C, PER, TR, TRI>(Aop, Bop, g_off, kmul, nk, kt, nk - 2 - kt, lds, wave, f, a, b, acc);
+    step16<C, PER, TR, TRI, SELF>(Aop, Bop, g_off, kmul, nk, kt, nk - 2 - kt, lds, wave, f, a, b, acc);
   mfma16<C, TRI>(a, b, acc);
 }
 
 // The main loop of a wave whose sub-tile lies wholly below the diagonal of a
 // diagonal tile of a symmetric product: it does its share of the stage
-// loads, waits and barriers exactly as main_loop16 does, but no fragment
+// loads (A half only, as every wave of a diagonal tile), waits and barriers
+// exactly as main_loop16 does, but no fragment
 // reads and no products (nothing of its sub-tile is stored), which leaves
 // its SIMD to the other work-group on the CU.
 template <class C, int PER>
@@ -320,7 +324,7 @@ __device__ __forceinline__ void load_loop16(const __bf16* __restrict__ Aop, cons
                                             LAS unsigned char* lds, int wave) {
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
-    if (st < nk) issue16<C>(Aop, Bop, g_off, wave, st * C::BK * kmul, lds + st * C::STAGEB);
+    if (st < nk) issue16<C, true>(Aop, Bop, g_off, wave, st * C::BK * kmul, lds + st * C::STAGEB);
   {
     const int newer = nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1;
     if (newer >= 3) MUON_WAIT_VM(3 * PER);
@@ -337,7 +341,7 @@ __device__ __forceinline__ void load_loop16(const __bf16* __restrict__ Aop, cons
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int fut = kt + C::NSTAGE;
-    if (fut < nk) issue16<C>(Aop, Bop, g_off, wave, fut * C::BK * kmul, lds + (kt % C::NSTAGE) * C::STAGEB);
+    if (fut < nk) issue16<C, true>(Aop, Bop, g_off, wave, fut * C::BK * kmul, lds + (kt % C::NSTAGE) * C::STAGEB);
   }
 }
 
@@ -592,19 +596,32 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
   LAS unsigned char* lds = (LAS unsigned char*)smem_raw;
   // On a diagonal tile of a symmetric product, a wave whose sub-tile lies
   // wholly below the diagonal only loads (its results are never stored).
-  const bool below = (MODE != BXM) && ti == tj && wr * C::WM >= (wc + 1) * C::WN;
+  // A diagonal tile of a symmetric product multiplies a panel by itself: its
+  // stages hold the panel once (A half) and the B fragments are read there.
+  const bool self = (MODE != BXM) && ti == tj;
+  if (self) {
+#pragma unroll
+    for (int jb = 0; jb < C::BNB; ++jb) {
+      fr.b[jb] -= C::OPB;
+      fr.b1[jb] -= C::OPB;
+    }
+  }
+  const bool below = self && wr * C::WM >= (wc + 1) * C::WN;
   if (below) {
-    if (nq == C::QMAX) load_loop16<C, 2 * C::QMAX>(Aop, Bop, g_off, kmul, nk, lds, wave);
-    else load_loop16<C, 2 * (C::QMAX - 1)>(Aop, Bop, g_off, kmul, nk, lds, wave);
-  } else if (MODE != BXM && ti == tj && wr * C::WM == wc * C::WN) {
+    if (nq == C::QMAX) load_loop16<C, C::QMAX>(Aop, Bop, g_off, kmul, nk, lds, wave);
+    else load_loop16<C, C::QMAX - 1>(Aop, Bop, g_off, kmul, nk, lds, wave);
+  } else if (self && wr * C::WM == wc * C::WN) {
     // A sub-tile on the diagonal: only its blocks with i <= j are stored.
     if constexpr (C::WM == C::WN) {
-      if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
-      else main_loop16<C, 2 * (C::QMAX - 1), TR, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+      if (nq == C::QMAX) main_loop16<C, C::QMAX, TR, true, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+      else main_loop16<C, C::QMAX - 1, TR, true, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
     }
+  } else if (self) {
+    if (nq == C::QMAX) main_loop16<C, C::QMAX, TR, false, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    else main_loop16<C, C::QMAX - 1, TR, false, true>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
   } else {
-    if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR, false>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
-    else main_loop16<C, 2 * (C::QMAX - 1), TR, false>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    if (nq == C::QMAX) main_loop16<C, 2 * C::QMAX, TR, false, false>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
+    else main_loop16<C, 2 * (C::QMAX - 1), TR, false, false>(Aop, Bop, g_off, kmul, nk, lds, wave, fr, acc);
   }
   __syncthreads();
   if (below) return;
