@@ -125,7 +125,10 @@ struct Slots {
   int kmul;
 };
 
-template <class C>
+// SELF: a diagonal tile of a symmetric product, whose B operand is the same
+// panel as its A operand: only the A half of the stage is loaded and the B
+// fragments are read from it.
+template <class C, bool SELF>
 __device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                             const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
                                             int wave) {
@@ -139,7 +142,7 @@ __device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, cons
 #pragma unroll
   for (int i = 0; i < C::QBMAX; ++i) {
     const int q = wave + i * C::NW;
-    if (i < C::QBMAX - 1 || q < C::QB)
+    if (!SELF && (i < C::QBMAX - 1 || q < C::QB))
       __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.boff[i] + k0 * sl.kmul),
                                        (LAS void*)(dst + C::OPA + q * 1024), 16, 0, 0);
   }
@@ -203,13 +206,13 @@ __device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf1
 // (`src`).  The two slots always differ; __restrict__ lets the compiler
 // order the LDS reads against the in-flight direct-to-LDS loads without a
 // blanket wait.
-template <class C, bool TR>
+template <class C, bool TR, bool SELF>
 __device__ __forceinline__ void refill_and_read(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                                 const Slots<C>& sl, int kfut, bool queue,
                                                 LAS unsigned char* __restrict__ dst,
                                                 const LAS unsigned char* __restrict__ src, int wave,
                                                 const Frag<C>& f, bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
-  if (queue) issue_loads<C>(Aop, Bop, sl, kfut, dst, wave);
+  if (queue) issue_loads<C, SELF>(Aop, Bop, sl, kfut, dst, wave);
   read_half<C, TR>(src, 0, f, a, b);
 }
 
@@ -239,13 +242,13 @@ __device__ __forceinline__ void interleave() {
 // PER (this wave's loads per step) is a template parameter and the steady
 // phase has a fixed number of steps in flight, so the loop body has no
 // branches and every wait count is an immediate.
-template <class C, int PER, bool TR>
+template <class C, int PER, bool TR, bool SELF>
 __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave,
                                           const Frag<C>& f, f32x16_t (&acc)[C::BMB][C::BNB]) {
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
-    if (st < nk) issue_loads<C>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
+    if (st < nk) issue_loads<C, SELF>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
   wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -263,7 +266,7 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    refill_and_read<C, TR>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur,
+    refill_and_read<C, TR, SELF>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur,
                            lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, wave, f, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_half<C>(fa1, fb1, acc);
@@ -906,9 +909,22 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int nk = K / 32;
   LAS unsigned char* lds = (LAS unsigned char*)smem;
   constexpr int PER_FULL = C::QAMAX + C::QBMAX;
-  if (per == PER_FULL) main_loop<C, PER_FULL, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-  else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-  else main_loop<C, PER_FULL - 2, TR>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+  // A diagonal tile of a symmetric product multiplies a panel by itself: its
+  // stages hold the panel once (A half) and the B fragments are read there.
+  const bool self = MODE < BXM && ti == tj;
+  if constexpr (MODE < BXM) {
+    if (self) {
+#pragma unroll
+      for (int j = 0; j < (C::BNB > 2 ? C::BNB : 2); ++j) fr.b[j] -= C::OPA;
+      if (na == C::QAMAX) main_loop<C, C::QAMAX, TR, true>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+      else main_loop<C, C::QAMAX - 1, TR, true>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    }
+  }
+  if (!self) {
+    if (per == PER_FULL) main_loop<C, PER_FULL, TR, false>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR, false>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    else main_loop<C, PER_FULL - 2, TR, false>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+  }
   // The epilogue's LDS tiles overlap the ring: a barrier first (the BX
   // epilogues take it themselves, after requesting their first inputs).
   if constexpr (MODE < BXM) __syncthreads();
