@@ -191,14 +191,36 @@ __device__ __forceinline__ void read_half(const LAS unsigned char* __restrict__ 
   }
 }
 
-template <class C>
+// DOFF >= 0: the wave's sub-tile straddles the diagonal of a diagonal tile
+// of a symmetric product, its column blocks starting DOFF blocks right of
+// its row blocks; block (i, j) lies wholly below the diagonal (never stored)
+// when i > j + DOFF, and its products are skipped.  DOFF < 0: every block.
+template <int DOFF>
+__device__ __forceinline__ constexpr bool tri_keep(int i, int j) {
+  return DOFF < 0 || i <= j + DOFF;
+}
+template <class C, int DOFF>
+__device__ __forceinline__ constexpr int tri_products() {
+  int n = 0;
+  for (int i = 0; i < C::BMB; ++i)
+    for (int j = 0; j < C::BNB; ++j) n += tri_keep<DOFF>(i, j) ? 1 : 0;
+  return n;
+}
+template <class C, int DOFF>
+__device__ __forceinline__ constexpr int tri_reads() {
+  int n = C::BNB;  // block column j is always used (with i = 0)
+  for (int i = 0; i < C::BMB; ++i) n += tri_keep<DOFF>(i, C::BNB - 1) ? 1 : 0;
+  return n;
+}
+
+template <class C, int DOFF>
 __device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf16x8_t (&b)[C::BNB],
                                           f32x16_t (&acc)[C::BMB][C::BNB]) {
 #pragma unroll
   for (int i = 0; i < C::BMB; ++i)
 #pragma unroll
     for (int j = 0; j < C::BNB; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if (tri_keep<DOFF>(i, j)) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
 // After the barrier of a step: queue a future step's loads into the ring
@@ -219,16 +241,18 @@ __device__ __forceinline__ void refill_and_read(const __bf16* __restrict__ Aop, 
 // Scheduling pattern for a block of first-half products and second-half
 // fragment reads: one LDS read after each product, so the reads stream out
 // while the matrix core works and the products never wait on them.
-template <class C>
+template <class C, int DOFF>
 __device__ __forceinline__ void interleave() {
-  constexpr int NR = C::BMB + C::BNB;      // fragment reads of a half
-  constexpr int NM = C::BMB * C::BNB;      // products of a half
+  constexpr int NR = tri_reads<C, DOFF>();     // fragment reads of a half
+  constexpr int NM = tri_products<C, DOFF>();  // products of a half
+  constexpr int NP = NR < NM ? NR : NM;
 #pragma unroll
-  for (int q = 0; q < NR; ++q) {
+  for (int q = 0; q < NP; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+  if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -242,7 +266,7 @@ __device__ __forceinline__ void interleave() {
 // PER (this wave's loads per step) is a template parameter and the steady
 // phase has a fixed number of steps in flight, so the loop body has no
 // branches and every wait count is an immediate.
-template <class C, int PER, bool TR, bool SELF>
+template <class C, int PER, bool TR, bool SELF, int DOFF>
 __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave,
                                           const Frag<C>& f, f32x16_t (&acc)[C::BMB][C::BNB]) {
@@ -259,9 +283,9 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
   // steps in flight.
   for (; kt < nk - C::NSTAGE; ++kt) {
     LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
-    mfma_half<C>(fa0, fb0, acc);
+    mfma_half<C, DOFF>(fa0, fb0, acc);
     read_half<C, TR>(cur, 1, f, fa1, fb1);
-    interleave<C>();
+    interleave<C, DOFF>();
     MUON_WAIT_VM((C::NSTAGE - 2) * PER);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();
@@ -269,27 +293,52 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
     refill_and_read<C, TR, SELF>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur,
                            lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, wave, f, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_half<C>(fa1, fb1, acc);
+    mfma_half<C, DOFF>(fa1, fb1, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   // Drain phase: no refills; the steps still in flight land one by one.
   for (; kt + 1 < nk; ++kt) {
     LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
-    mfma_half<C>(fa0, fb0, acc);
+    mfma_half<C, DOFF>(fa0, fb0, acc);
     read_half<C, TR>(cur, 1, f, fa1, fb1);
-    interleave<C>();
+    interleave<C, DOFF>();
     wait_newer<PER>(nk - 2 - kt);
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     read_half<C, TR>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, f, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_half<C>(fa1, fb1, acc);
+    mfma_half<C, DOFF>(fa1, fb1, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   read_half<C, TR>(lds + ((nk - 1) % C::NSTAGE) * C::STAGEB, 1, f, fa1, fb1);
-  mfma_half<C>(fa0, fb0, acc);
-  mfma_half<C>(fa1, fb1, acc);
+  mfma_half<C, DOFF>(fa0, fb0, acc);
+  mfma_half<C, DOFF>(fa1, fb1, acc);
+}
+
+// The main loop of a wave whose sub-tile lies wholly below the diagonal of a
+// diagonal tile of a symmetric product: its share of the stage loads (A
+// half only), waits and barriers exactly as main_loop, and nothing else.
+template <class C, int PER>
+__device__ __forceinline__ void load_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                          const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave) {
+#pragma unroll
+  for (int st = 0; st < C::NSTAGE; ++st)
+    if (st < nk) issue_loads<C, true>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
+  wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
+  __builtin_amdgcn_s_barrier();
+  int kt = 0;
+  for (; kt < nk - C::NSTAGE; ++kt) {
+    MUON_WAIT_VM((C::NSTAGE - 2) * PER);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_loads<C, true>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, lds + (kt % C::NSTAGE) * C::STAGEB, wave);
+  }
+  for (; kt + 1 < nk; ++kt) {
+    wait_newer<PER>(nk - 2 - kt);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
 }
 
 // ---------------------------------------------------------------- BX epilogue
@@ -830,7 +879,21 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave / C::NWN, wc = wave - wr * C::NWN;
+  int wr = wave / C::NWN, wc = wave - wr * C::NWN;
+  // Diagonal tile of a symmetric product (G256, 2 x 4 waves of 128 x 64):
+  // two sub-tiles lie wholly below the diagonal (nothing to compute), four
+  // straddle it (3 or 7 of their 8 blocks needed) and two lie above it.
+  // Waves w and w + 4 share a SIMD, so the sub-tiles are dealt to pair a
+  // full one with an empty one and a 7-block one with a 3-block one: every
+  // SIMD then has at most 10 of the 16 block products of a full tile.
+  if constexpr (MODE < BXM && C::NWM == 2 && C::NWN == 4 && C::BMB == 4 && C::BNB == 2) {
+    if (ti == tj) {
+      constexpr int kR[8] = {0, 0, 0, 1, 1, 1, 1, 0};
+      constexpr int kC[8] = {2, 3, 1, 3, 0, 1, 2, 0};
+      wr = kR[wave];
+      wc = kC[wave];
+    }
+  }
 
   Slots<C> sl;
   Frag<C> fr;
@@ -912,22 +975,42 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   // A diagonal tile of a symmetric product multiplies a panel by itself: its
   // stages hold the panel once (A half) and the B fragments are read there.
   const bool self = MODE < BXM && ti == tj;
+  // In a diagonal tile: sub-tiles wholly below the diagonal only load;
+  // sub-tiles straddling it skip their blocks below it (DOFF = offset of
+  // the column blocks from the row blocks, in 32-row blocks).
+  bool below = false;
   if constexpr (MODE < BXM) {
     if (self) {
 #pragma unroll
       for (int j = 0; j < (C::BNB > 2 ? C::BNB : 2); ++j) fr.b[j] -= C::OPA;
-      if (na == C::QAMAX) main_loop<C, C::QAMAX, TR, true>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-      else main_loop<C, C::QAMAX - 1, TR, true>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+      below = wr * C::WM >= (wc + 1) * C::WN;
+      const bool above = wr * C::WM + C::WM - 1 <= wc * C::WN;
+      const int doff = (wc * C::WN - wr * C::WM) / 32;
+      static_assert(C::QAMAX >= 2, "diagonal-tile loops assume two A loads per wave and step");
+      if (below) {
+        if (na == C::QAMAX) load_loop<C, C::QAMAX>(Aop, Bop, sl, nk, lds, wave);
+        else load_loop<C, C::QAMAX - 1>(Aop, Bop, sl, nk, lds, wave);
+      } else if (above || !(C::BMB == 4 && C::BNB == 2 && (doff == 0 || doff == 2))) {
+        if (na == C::QAMAX) main_loop<C, C::QAMAX, TR, true, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+        else main_loop<C, C::QAMAX - 1, TR, true, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+      } else if (doff == 0) {
+        if (na == C::QAMAX) main_loop<C, C::QAMAX, TR, true, 0>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+        else main_loop<C, C::QAMAX - 1, TR, true, 0>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+      } else {
+        if (na == C::QAMAX) main_loop<C, C::QAMAX, TR, true, 2>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+        else main_loop<C, C::QAMAX - 1, TR, true, 2>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+      }
     }
   }
   if (!self) {
-    if (per == PER_FULL) main_loop<C, PER_FULL, TR, false>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-    else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR, false>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-    else main_loop<C, PER_FULL - 2, TR, false>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    if (per == PER_FULL) main_loop<C, PER_FULL, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    else main_loop<C, PER_FULL - 2, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   }
   // The epilogue's LDS tiles overlap the ring: a barrier first (the BX
   // epilogues take it themselves, after requesting their first inputs).
   if constexpr (MODE < BXM) __syncthreads();
+  if (below) return;  // nothing of its sub-tile is stored
   // The epilogue reads the descriptor through the table: a copy (see
   // MatDesc) measured 1% slower here.
   const MatDesc& d = dr;
