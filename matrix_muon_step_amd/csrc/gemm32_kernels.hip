@@ -316,15 +316,16 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
   mfma_half<C, DOFF>(fa1, fb1, acc);
 }
 
-// The main loop of a wave whose sub-tile lies wholly below the diagonal of a
-// diagonal tile of a symmetric product: its share of the stage loads (A
-// half only), waits and barriers exactly as main_loop, and nothing else.
-template <class C, int PER>
+// The main loop of a wave with nothing to compute: its sub-tile lies wholly
+// below the diagonal of a diagonal tile of a symmetric product (SELF: A half
+// only), or wholly in the padding rows of a BX tile.  Its share of the stage
+// loads, waits and barriers exactly as main_loop, and nothing else.
+template <class C, int PER, bool SELF>
 __device__ __forceinline__ void load_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave) {
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
-    if (st < nk) issue_loads<C, true>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
+    if (st < nk) issue_loads<C, SELF>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
   wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
   __builtin_amdgcn_s_barrier();
   int kt = 0;
@@ -332,7 +333,7 @@ __device__ __forceinline__ void load_loop(const __bf16* __restrict__ Aop, const 
     MUON_WAIT_VM((C::NSTAGE - 2) * PER);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_loads<C, true>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, lds + (kt % C::NSTAGE) * C::STAGEB, wave);
+    issue_loads<C, SELF>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, lds + (kt % C::NSTAGE) * C::STAGEB, wave);
   }
   for (; kt + 1 < nk; ++kt) {
     wait_newer<PER>(nk - 2 - kt);
@@ -894,6 +895,29 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       wc = kC[wave];
     }
   }
+  // BX tile (W320) whose last wave columns lie wholly in padding rows of X^T
+  // (at or past k_gram, which no valid result reads): those waves only load.
+  // With one or two valid wave columns the sub-tiles are dealt so that the
+  // valid ones sit on different SIMDs (waves w and w + 4 share one); the
+  // wave of sub-tile (0, c) keeps index c, whose LDS tile the merged
+  // epilogue uses.
+  int bx_valid = C::NWN;
+  if constexpr (MODE >= BXM && C::NWM == 2 && C::NWN == 4 && C::WM % 64 == 32 && C::BM % 64 == 0) {
+    const int rem = dr.k_gram - tj * C::BN;
+    bx_valid = rem >= C::BN ? C::NWN : (rem + C::WN - 1) / C::WN;
+    if (bx_valid == 1) {
+      constexpr int kR[8] = {0, 1, 0, 0, 0, 1, 1, 1};
+      constexpr int kC[8] = {0, 0, 1, 2, 3, 1, 2, 3};
+      wr = kR[wave];
+      wc = kC[wave];
+    } else if (bx_valid == 2) {
+      constexpr int kR[8] = {0, 0, 1, 1, 0, 0, 1, 1};
+      constexpr int kC[8] = {0, 1, 0, 1, 2, 3, 2, 3};
+      wr = kR[wave];
+      wc = kC[wave];
+    }
+  }
+  const bool bx_pad = wc >= bx_valid;
 
   Slots<C> sl;
   Frag<C> fr;
@@ -988,8 +1012,8 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       const int doff = (wc * C::WN - wr * C::WM) / 32;
       static_assert(C::QAMAX >= 2, "diagonal-tile loops assume two A loads per wave and step");
       if (below) {
-        if (na == C::QAMAX) load_loop<C, C::QAMAX>(Aop, Bop, sl, nk, lds, wave);
-        else load_loop<C, C::QAMAX - 1>(Aop, Bop, sl, nk, lds, wave);
+        if (na == C::QAMAX) load_loop<C, C::QAMAX, true>(Aop, Bop, sl, nk, lds, wave);
+        else load_loop<C, C::QAMAX - 1, true>(Aop, Bop, sl, nk, lds, wave);
       } else if (above || !(C::BMB == 4 && C::BNB == 2 && (doff == 0 || doff == 2))) {
         if (na == C::QAMAX) main_loop<C, C::QAMAX, TR, true, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
         else main_loop<C, C::QAMAX - 1, TR, true, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
@@ -1002,7 +1026,11 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       }
     }
   }
-  if (!self) {
+  if (!self && bx_pad) {
+    if (per == PER_FULL) load_loop<C, PER_FULL, false>(Aop, Bop, sl, nk, lds, wave);
+    else if (per == PER_FULL - 1) load_loop<C, PER_FULL - 1, false>(Aop, Bop, sl, nk, lds, wave);
+    else load_loop<C, PER_FULL - 2, false>(Aop, Bop, sl, nk, lds, wave);
+  } else if (!self) {
     if (per == PER_FULL) main_loop<C, PER_FULL, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
     else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
     else main_loop<C, PER_FULL - 2, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
@@ -1028,7 +1056,15 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     if constexpr (C::NWM == 2 && C::WM % 64 == 32 && C::BM % 64 == 0) {
       // The two waves of a column share the line at row WM - 32 of the tile.
       float* Tm = reinterpret_cast<float*>(smem) + wc * (C::SLICEB / 4);
-      if (wr == 0)
+      if (bx_pad) {
+        // Nothing to store; the barriers of bx_epilogue_merged (the first,
+        // the two around the shared line, and the X-major pass's).
+        const bool need_xmajor = (MODE >= BXL) && !(d.flags & kTransposed);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        if (need_xmajor) __syncthreads();
+      } else if (wr == 0)
         bx_epilogue_merged<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
       else
         bx_epilogue_merged<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);

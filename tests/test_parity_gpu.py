@@ -335,9 +335,12 @@ def test_zero_gradient_leaves_weights(mm):
 
 
 def test_poisoned_workspace_gives_finite_results(mm):
-    """Workspace pre-filled with NaN bytes: every byte the path reads is written first."""
+    """Workspace pre-filled with NaN bytes: every byte the path reads is written
+    first.  The 320-row BX tiles of the last three shapes end in 1, 2 and 3
+    valid wave columns (the rest of the tile is padding that no result reads,
+    and its waves only load)."""
     log_case("poisoned workspace")
-    shapes = [(130, 260), (260, 130), (17, 33), (256, 256)]
+    shapes = [(130, 260), (260, 130), (17, 33), (256, 256), (320, 1600), (1650, 320), (640, 1700)]
     mats, host = [], []
     for i, (r, c) in enumerate(shapes):
         g = synth.numpy_gradient(r, c, 4, 0.1, "f32", [53, i, 0, 0])
