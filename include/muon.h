@@ -202,7 +202,9 @@ typedef struct muon_matrix_plan {
   int32_t fused_update; /* 1: the last BX launch writes W (or O) itself, from the  */
                         /* float32 accumulator; 0: a separate update pass reads   */
                         /* the final iterate pair (hi + lo)                       */
-  int32_t reserved;
+  int32_t xcd_edges;    /* bit s (s = 0 Gram, 1 polynomial, 2 BX) set when one of */
+                        /* the 8 XCDs starts its share of that grouped launch     */
+                        /* inside (or at the first tile of) this matrix's tiles   */
   int64_t x_offset;     /* byte offset of the iterate buffers in the workspace    */
 } muon_matrix_plan_t;
 
@@ -235,6 +237,17 @@ typedef enum muon_stage {
 
 muon_status_t muon_profile_enable(int32_t on);
 muon_status_t muon_profile_read(double* ms, int64_t* launches);
+
+/* Bandwidth yardstick for the HBM-bound stages (the measurement side of the
+ * boundary, not part of a step): copies `bytes` from src to dst (DEVICE
+ * memory, 16-byte aligned, bytes a multiple of 16, disjoint) with a plain
+ * streaming kernel that reads and writes every byte once, on `stream`.
+ * variant 0..MUON_COPY_PROBE_VARIANTS-1: bit 0 selects nontemporal loads and
+ * stores, bits 1-2 the grid (1024, 4096 or 16384 work-groups of 256 lanes,
+ * each lane with four 16-byte loads in flight).  A benchmark times the
+ * variants and takes the fastest as the measured copy ceiling. */
+#define MUON_COPY_PROBE_VARIANTS 6
+muon_status_t muon_copy_probe(const void* src, void* dst, size_t bytes, int32_t variant, void* stream);
 
 const char* muon_status_string(muon_status_t status);
 /* Message of the last error on the calling thread ("" if none). */

@@ -1,8 +1,9 @@
 """ctypes binding of libmuon (include/muon.h).  Argument marshalling only.
 
 Every function here has the name of the C entry point it calls.  Tensors are
-torch tensors on the current HIP device; torch supplies device memory and the
-current stream, nothing else.  There is no fallback: if libmuon.so is absent
+torch tensors on the current HIP device; torch supplies device memory and
+streams, nothing else.  Buffers the binding allocates for a call (workspace,
+outputs, the diagnostics array) are allocated on the stream the call runs on.  There is no fallback: if libmuon.so is absent
 the first call raises.
 """
 from __future__ import annotations
@@ -27,6 +28,7 @@ MUON_BF16 = 1
 MUON_MAX_NS_STEPS = 64
 MUON_MAX_DIM = 65536
 MUON_MAX_GRAM = 16384
+MUON_COPY_PROBE_VARIANTS = 6
 STAGES = ("momentum", "norm", "prep", "gram", "poly", "bx", "update", "upload", "bx_update", "diag")
 MUON_STAGE_COUNT = len(STAGES)
 
@@ -92,7 +94,7 @@ class muon_matrix_plan_t(ctypes.Structure):
         ("bx_tile_rows", ctypes.c_int32),
         ("bx_tile_cols", ctypes.c_int32),
         ("fused_update", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("xcd_edges", ctypes.c_int32),
         ("x_offset", ctypes.c_int64),
     ]
 
@@ -143,6 +145,9 @@ def lib() -> ctypes.CDLL:
                 L.muon_profile_enable.argtypes = [ctypes.c_int32]
                 L.muon_profile_read.restype = ctypes.c_int
                 L.muon_profile_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]
+                L.muon_copy_probe.restype = ctypes.c_int
+                L.muon_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                              ctypes.c_void_p]
                 L.muon_status_string.restype = ctypes.c_char_p
                 L.muon_status_string.argtypes = [ctypes.c_int]
                 L.muon_last_error.restype = ctypes.c_char_p
@@ -216,15 +221,22 @@ def _tensor_entries(matrices):
     return entries, (MUON_F32 if g_dtype is None else g_dtype)
 
 
-def _stream_handle(stream) -> int:
+def _torch_stream(stream):
+    """The torch stream object the call runs on: the current stream for
+    None, a torch stream as given, or an external HIP stream handle (int)."""
     import torch
 
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
 
 
 def _alloc_workspace(nbytes: int, device):
+    """Workspace on the current stream (callers enter the call's stream first,
+    so torch's caching allocator only hands the block to later work that is
+    ordered after the call's kernels)."""
     import torch
 
     if nbytes == 0:
@@ -233,6 +245,12 @@ def _alloc_workspace(nbytes: int, device):
     if ws.data_ptr() % 256:
         raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
     return ws
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
 
 # ---------------------------------------------------------------- entry points
@@ -251,7 +269,13 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
               workspace=None, stream=None, weight_decay=0.0) -> None:
     """One Muon step on a list of (W, G, B[, scale]) tensors; W, B updated in place.
 
-    weight_decay is the decoupled decay lambda: W <- W - lr * (lambda * W + scale * O)."""
+    weight_decay is the decoupled decay lambda: W <- W - lr * (lambda * W + scale * O).
+    stream: None (torch's current stream), a torch stream, or a HIP stream
+    handle (int).  The kernels run on that stream; the caller orders it after
+    the work that produced G (and W, B).  A workspace allocated here belongs
+    to that stream."""
+    import torch
+
     entries, gd = _tensor_entries(matrices)
     if not entries:
         return
@@ -260,10 +284,13 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
     need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
-    if workspace is None:
-        workspace = _alloc_workspace(need, matrices[0][0].device)
-    _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
-                           workspace.numel() * workspace.element_size(), ctypes.c_void_p(_stream_handle(stream))))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        if workspace is None:
+            workspace = _alloc_workspace(need, matrices[0][0].device)
+        ws_ptr, ws_len = _ws_args(workspace)
+        _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
+                               ctypes.c_void_p(st.cuda_stream)))
 
 
 def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
@@ -275,24 +302,25 @@ def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1
 
     entries, gd = _tensor_entries(matrices)
     n = len(entries)
-    if diag is None:
-        dev = matrices[0][0].device if n else torch.device("cuda")
-        diag = torch.zeros(max(1, n), 8, dtype=torch.int32, device=dev)
-    if not diag.is_cuda or diag.dtype != torch.int32 or not diag.is_contiguous() or diag.numel() < 8 * n:
-        raise ValueError("diag must be a contiguous int32 GPU tensor of at least n x 8 entries")
-    if not entries:
-        return diag
-    arr = raw_matrix_array(entries)
-    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
-    need = int(lib().muon_workspace_bytes(arr, n, ctypes.byref(hp)))
-    if need == 0:
-        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
-    if workspace is None:
-        workspace = _alloc_workspace(need, matrices[0][0].device)
-    _check(lib().muon_step_diag(arr, n, ctypes.byref(hp), ctypes.c_void_p(diag.data_ptr()),
-                                ctypes.c_void_p(workspace.data_ptr()),
-                                workspace.numel() * workspace.element_size(),
-                                ctypes.c_void_p(_stream_handle(stream))))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        if diag is None:
+            dev = matrices[0][0].device if n else torch.device("cuda")
+            diag = torch.zeros(max(1, n), 8, dtype=torch.int32, device=dev)
+        if not diag.is_cuda or diag.dtype != torch.int32 or not diag.is_contiguous() or diag.numel() < 8 * n:
+            raise ValueError("diag must be a contiguous int32 GPU tensor of at least n x 8 entries")
+        if not entries:
+            return diag
+        arr = raw_matrix_array(entries)
+        hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
+        need = int(lib().muon_workspace_bytes(arr, n, ctypes.byref(hp)))
+        if need == 0:
+            raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+        if workspace is None:
+            workspace = _alloc_workspace(need, matrices[0][0].device)
+        ws_ptr, ws_len = _ws_args(workspace)
+        _check(lib().muon_step_diag(arr, n, ctypes.byref(hp), ctypes.c_void_p(diag.data_ptr()), ws_ptr, ws_len,
+                                    ctypes.c_void_p(st.cuda_stream)))
     return diag
 
 
@@ -324,27 +352,28 @@ def muon_orthogonalize(Ms, Os=None, ns_steps=5, eps=1e-7, workspace=None, stream
     import torch
 
     Ms = list(Ms)
-    if Os is None:
-        Os = [torch.empty_like(M) for M in Ms]
     n = len(Ms)
     if n == 0:
         return []
-    for k, (M, O) in enumerate(zip(Ms, Os)):
-        if M.dtype != torch.float32 or O.dtype != torch.float32 or not M.is_cuda or not O.is_cuda:
-            raise ValueError(f"matrix {k}: M and O must be float32 GPU tensors")
-        if M.shape != O.shape or M.dim() != 2 or not M.is_contiguous() or not O.is_contiguous():
-            raise ValueError(f"matrix {k}: M and O must be contiguous 2-D tensors of one shape")
-    need = muon_orthogonalize_workspace_bytes([M.shape for M in Ms], ns_steps)
-    if workspace is None:
-        workspace = _alloc_workspace(need, Ms[0].device)
-    mp = (ctypes.c_void_p * n)(*[M.data_ptr() for M in Ms])
-    op = (ctypes.c_void_p * n)(*[O.data_ptr() for O in Os])
-    rows = (ctypes.c_int64 * n)(*[M.shape[0] for M in Ms])
-    cols = (ctypes.c_int64 * n)(*[M.shape[1] for M in Ms])
-    _check(lib().muon_orthogonalize(mp, op, rows, cols, n, int(ns_steps), float(eps),
-                                    ctypes.c_void_p(workspace.data_ptr()),
-                                    workspace.numel() * workspace.element_size(),
-                                    ctypes.c_void_p(_stream_handle(stream))))
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        if Os is None:
+            Os = [torch.empty_like(M) for M in Ms]
+        for k, (M, O) in enumerate(zip(Ms, Os)):
+            if M.dtype != torch.float32 or O.dtype != torch.float32 or not M.is_cuda or not O.is_cuda:
+                raise ValueError(f"matrix {k}: M and O must be float32 GPU tensors")
+            if M.shape != O.shape or M.dim() != 2 or not M.is_contiguous() or not O.is_contiguous():
+                raise ValueError(f"matrix {k}: M and O must be contiguous 2-D tensors of one shape")
+        need = muon_orthogonalize_workspace_bytes([M.shape for M in Ms], ns_steps)
+        if workspace is None:
+            workspace = _alloc_workspace(need, Ms[0].device)
+        mp = (ctypes.c_void_p * n)(*[M.data_ptr() for M in Ms])
+        op = (ctypes.c_void_p * n)(*[O.data_ptr() for O in Os])
+        rows = (ctypes.c_int64 * n)(*[M.shape[0] for M in Ms])
+        cols = (ctypes.c_int64 * n)(*[M.shape[1] for M in Ms])
+        ws_ptr, ws_len = _ws_args(workspace)
+        _check(lib().muon_orthogonalize(mp, op, rows, cols, n, int(ns_steps), float(eps), ws_ptr, ws_len,
+                                        ctypes.c_void_p(st.cuda_stream)))
     return Os
 
 
@@ -358,7 +387,7 @@ def muon_plan_query(shapes: Sequence[Tuple[int, int]], ns_steps=5, g_dtype=MUON_
     _check(lib().muon_plan_query(arr, n, ctypes.byref(hp), ctypes.byref(info), per))
     mats = [dict(transposed=p.transposed, m=p.m, n=p.n, m_pad=p.m_pad, n_pad=p.n_pad,
                  tile=p.tile, bx_tile_rows=p.bx_tile_rows, bx_tile_cols=p.bx_tile_cols, fp32_path=int(p.tile == 0),
-                 fused_update=p.fused_update, x_offset=p.x_offset) for p in list(per)[:n]]
+                 fused_update=p.fused_update, xcd_edges=p.xcd_edges, x_offset=p.x_offset) for p in list(per)[:n]]
     return {f: getattr(info, f) for f, _ in muon_plan_info_t._fields_ if f != "reserved"}, mats
 
 
@@ -372,3 +401,17 @@ def muon_profile_read():
     cnt = (ctypes.c_int64 * MUON_STAGE_COUNT)()
     _check(lib().muon_profile_read(ms, cnt))
     return {STAGES[k]: (ms[k], cnt[k]) for k in range(MUON_STAGE_COUNT)}
+
+
+def muon_copy_probe(src, dst, variant: int = 0, stream=None) -> None:
+    """Streaming device copy src -> dst (same byte size) with the library's
+    bandwidth yardstick kernel; the HBM ceiling of the bandwidth-bound stages."""
+    import torch
+
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not src.is_cuda or not dst.is_cuda:
+        raise ValueError("src and dst must be GPU tensors of the same byte size")
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        _check(lib().muon_copy_probe(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                                     int(variant), ctypes.c_void_p(st.cuda_stream)))

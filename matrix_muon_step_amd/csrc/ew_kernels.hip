@@ -12,14 +12,6 @@ namespace muon {
 
 namespace {
 
-__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
-  int lo = 0, hi = nmats - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -421,6 +413,36 @@ __global__ __launch_bounds__(256) void diag_kernel(const MatDesc* __restrict__ d
   }
 }
 
+// ---------------------------------------------------------------- copy probe
+// Streaming copy of n16 16-byte words, the yardstick of the bandwidth-bound
+// stages (one read and one write per byte, the momentum pass's mix).  Each
+// lane keeps U 16-byte loads in flight before storing them; the grid
+// strides over the buffer.  NT: nontemporal loads and stores (streamed
+// past the caches).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                         int64_t n16) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 256 * U;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 256 * U + threadIdx.x; base < n16; base += step) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + 256 * u;
+      if (i < n16) v[u] = NT ? __builtin_nontemporal_load(src + i) : gld<u32x4_t>(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + 256 * u;
+      if (i < n16) {
+        if (NT) __builtin_nontemporal_store(v[u], dst + i);
+        else gst(dst + i, v[u]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
@@ -453,6 +475,21 @@ hipError_t launch_update(const MatDesc* d, const int32_t* prefix, int nmats, int
 
 hipError_t launch_diag(const MatDesc* d, int nmats, void* out, hipStream_t s) {
   hipLaunchKernelGGL(diag_kernel, dim3(nmats), dim3(256), 0, s, d, static_cast<muon_diag_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, int variant, hipStream_t s) {
+  // variant: bit 0 = nontemporal; bits 1.. = grid (0: 1024, 1: 4096, 2: 16384 work-groups)
+  const int grids[3] = {1024, 4096, 16384};
+  const int gi = variant >> 1;
+  if (gi < 0 || gi > 2) return hipErrorInvalidValue;
+  const dim3 grid(grids[gi]);
+  const u32x4_t* a = static_cast<const u32x4_t*>(src);
+  u32x4_t* b = static_cast<u32x4_t*>(dst);
+  if (variant & 1)
+    hipLaunchKernelGGL((copy_probe_kernel<4, true>), grid, dim3(256), 0, s, a, b, n16);
+  else
+    hipLaunchKernelGGL((copy_probe_kernel<4, false>), grid, dim3(256), 0, s, a, b, n16);
   return hipGetLastError();
 }
 

@@ -57,11 +57,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 #define GAS __attribute__((address_space(1)))
 #define LAS __attribute__((address_space(3)))
-#define MUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
-constexpr float kCoefA = 3.4445f;
-constexpr float kCoefB = -4.7750f;
-constexpr float kCoefC = 2.0315f;
 
 // BXL: the last BX of a step; instead of storing the iterate it applies the
 // parameter update W -= lr * scale * O (or stores O in orthogonalise-only
@@ -93,16 +89,7 @@ struct G32 {
   static_assert(NW == 4 || NW == 8, "swizzle invariance of the load slots assumes 4 or 8 waves");
 };
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
-__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
-  int lo = 0, hi = nmats - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 
 // Waits until at most `newer` later steps of this wave's loads are in flight
@@ -617,10 +604,7 @@ __device__ __forceinline__ void bx_stage_unit(int lane, const f32x16_t (&acc)[C:
 // Row groups of the first unit requested before the barrier that ends the
 // main loop (their latency overlaps the last products and the barrier);
 // the rest after its accumulators are staged.
-#ifndef MUON_BX_EARLY
-#define MUON_BX_EARLY 4
-#endif
-constexpr int kEarly = MUON_BX_EARLY;
+constexpr int kEarly = 4;
 
 // Unit K is staged in T and its inputs are requested (or in flight): its
 // passes run while the next unit's inputs are requested, then the next

@@ -63,9 +63,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr float kCoefA = 3.4445f;
-constexpr float kCoefB = -4.7750f;
-constexpr float kCoefC = 2.0315f;
 
 enum Mode { GRAM = 0, POLY = 1, BXM = 2 };
 
@@ -99,26 +96,13 @@ struct Cfg {
   static_assert(T % 16 == 0, "tile edge must be a multiple of 16");
 };
 
-// Chunk position of k-chunk c (0..3) in LDS row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
-// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
-#define MUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
 #define GAS __attribute__((address_space(1)))
 #define LAS __attribute__((address_space(3)))
 
 
 
-__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
-  int lo = 0, hi = nmats - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 
 // Position of chunk c (8 columns) within k-row k of a transposed-operand

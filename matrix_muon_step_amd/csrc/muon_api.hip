@@ -105,30 +105,17 @@ int64_t upper_tiles(int64_t mp, int t) {
 // (upper tiles for the symmetric products) divided by each configuration's
 // relative sustained rate on gfx950, from measurements of these kernels:
 // 32x32 256-tiles 1.10, 320x256 BX tiles 1.04, 160x256 BX tiles 1.00,
-// 16x16 160-tiles 0.85, 128-tiles 0.70.  MUON_GEMM_CFG=g256|w160|t160|t128|w320
-// forces one combination (tuning).
+// 16x16 160-tiles 0.85, 128-tiles 0.70.  The choice depends on the shape
+// alone, so a matrix takes the same kernels (and gives the same bits)
+// whatever else a call holds.
 MatCfg choose_cfg(int64_t m, int64_t n) {
-  struct Cand { const char* name; int sym, bx; };
+  struct Cand { int sym, bx; };
   static const Cand cands[] = {
-      {"g256", kCfgG256, kCfgG256}, {"w160", kCfgT160, kCfgW160},
-      {"t160", kCfgT160, kCfgT160}, {"t128", kCfgT128, kCfgT128}, {"w320", kCfgT160, kCfgW320}};
-  constexpr int kCands = sizeof(cands) / sizeof(cands[0]);
+      {kCfgG256, kCfgG256}, {kCfgT160, kCfgW160}, {kCfgT160, kCfgT160}, {kCfgT128, kCfgT128}, {kCfgT160, kCfgW320}};
   static const double rate[kNumCfg] = {1.10, 1.00, 0.85, 0.70, 1.04};
-  static const int forced = [] {
-    const char* e = getenv("MUON_GEMM_CFG");
-    if (!e) return -1;
-    for (int i = 0; i < kCands; ++i)
-      if (strcmp(e, cands[i].name) == 0) return i;
-    return -1;
-  }();
-  // A forced combination applies only where it fits the matrix.
-  int only = -1;
-  if (forced >= 0 && round_up(m, kCfgRows[cands[forced].sym]) % kCfgRows[cands[forced].bx] == 0) only = forced;
   MatCfg best{};
   double best_cost = 0.0;
-  for (int i = 0; i < kCands; ++i) {
-    if (only >= 0 && i != only) continue;
-    const Cand& c = cands[i];
+  for (const Cand& c : cands) {
     const int64_t mp = round_up(m, kCfgRows[c.sym]);
     if (mp % kCfgRows[c.bx] != 0) continue;
     const int64_t np = round_up(n, kCfgCols[c.bx]);
@@ -145,16 +132,10 @@ MatCfg choose_cfg(int64_t m, int64_t n) {
   return best;
 }
 
-// Gram-side tile rows per group of the BX tile order (wide-tile kernels).
-int bx_group(const MatCfg& cfg) {
-  const int tpc = static_cast<int>(cfg.m_pad / kCfgRows[cfg.bx]);
-  static const int forced = [] {
-    const char* e = getenv("MUON_BX_GROUP");
-    return e ? atoi(e) : 0;
-  }();
-  if (forced > 0) return forced < tpc ? forced : tpc;
-  return tpc;
-}
+// Gram-side tile rows per group of the BX tile order (wide-tile kernels):
+// all of them, so the tiles of one long-side column run together and share
+// their X^T panel in L2.
+int bx_group(const MatCfg& cfg) { return static_cast<int>(cfg.m_pad / kCfgRows[cfg.bx]); }
 
 // Validates shapes and scalars of every item and fills the plan (offsets
 // relative to a workspace base of 0).  Pointer checks happen separately.
@@ -466,23 +447,6 @@ XcdSplit make_split(const Plan& plan, int tab, int mode) {
   return sp;
 }
 
-// Round r of a split cut into rounds of at most `len` work items per XCD.
-XcdSplit split_round(const XcdSplit& sp, int r, int len) {
-  XcdSplit o;
-  o.max_len = 0;
-  for (int x = 0; x < 8; ++x) {
-    o.begin[x] = std::min(sp.end[x], sp.begin[x] + r * len);
-    o.end[x] = std::min(sp.end[x], o.begin[x] + len);
-    o.max_len = std::max(o.max_len, o.end[x] - o.begin[x]);
-  }
-  return o;
-}
-
-int env_int(const char* name) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : 0;
-}
-
 muon_status_t hip_fail(hipError_t e, const char* where) {
   return fail(MUON_ERR_HIP, std::string("muon: ") + where + ": " + hipGetErrorString(e));
 }
@@ -532,21 +496,15 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
       for (int c = 0; c < kNumCfg; ++c) {
         const int tab = mode == 2 ? tab_bx(c) : tab_sym(c);
         if (plan.tot[tab] == 0) continue;
-        const XcdSplit full = make_split(plan, tab, mode);
+        const XcdSplit sp = make_split(plan, tab, mode);
         const bool wide = cfg_wide(c);
         // 3: BX with the update applied; 4: the same with diagnostics
         const int kmode = (wide && last && mode == 2) ? (diag ? 4 : 3) : mode;
-        static const int round_len[3] = {env_int("MUON_ROUND_GRAM"), env_int("MUON_ROUND_POLY"),
-                                         env_int("MUON_ROUND_BX")};
-        const int len = round_len[mode] > 0 ? round_len[mode] : full.max_len;
-        for (int r = 0; r * len < full.max_len; ++r) {
-          const XcdSplit sp = split_round(full, r, len);
-          e = run_stage(kmode >= 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
-            return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s)
-                        : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s);
-          });
-          if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
-        }
+        e = run_stage(kmode >= 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
+          return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s)
+                      : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "matrix-core launch");
       }
     }
     if (plan.tot[kTabSmallGram] > 0) {
@@ -807,7 +765,24 @@ muon_status_t muon_plan_query(const muon_matrix_t* mats, int64_t n, const muon_h
       p.bx_tile_rows = (d.flags & kSmall) ? 0 : kCfgRows[d.bx_cfg];
       p.bx_tile_cols = (d.flags & kSmall) ? 0 : kCfgCols[d.bx_cfg];
       p.fused_update = (d.flags & kFusedUpd) ? 1 : 0;
+      p.xcd_edges = 0;
       p.x_offset = plan.x_offset[i];
+    }
+    // Matrices whose work range holds the start of an XCD's range in a
+    // matrix-core launch (the split of make_split, as execute uses it).
+    for (int c = 0; c < kNumCfg; ++c) {
+      for (int mode = 0; mode < 3; ++mode) {
+        const int tab = mode == 2 ? tab_bx(c) : tab_sym(c);
+        if (plan.tot[tab] == 0) continue;
+        const XcdSplit sp = make_split(plan, tab, mode);
+        const std::vector<int32_t>& pre = plan.pre[tab];
+        for (int x = 1; x < 8; ++x) {
+          const int32_t b = sp.begin[x];
+          if (b >= plan.tot[tab]) continue;
+          const int64_t i = std::upper_bound(pre.begin(), pre.begin() + n, b) - pre.begin() - 1;
+          per_matrix[i].xcd_edges |= 1 << mode;
+        }
+      }
     }
   }
   return MUON_OK;
@@ -846,6 +821,22 @@ muon_status_t muon_profile_read(double* ms, int64_t* launches) {
     g_prof_pool.push_back(p.b);
   }
   return st;
+}
+
+muon_status_t muon_copy_probe(const void* src, void* dst, size_t bytes, int32_t variant, void* stream) {
+  g_last_error.clear();
+  if (!src || !dst) return fail(MUON_ERR_INVALID_ARG, "muon: src or dst is NULL");
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) || (bytes & 15u))
+    return fail(MUON_ERR_ALIGN, "muon: copy probe needs 16-byte aligned buffers and a multiple of 16 bytes");
+  if (variant < 0 || variant >= MUON_COPY_PROBE_VARIANTS)
+    return fail(MUON_ERR_INVALID_ARG, "muon: copy probe variant outside 0..MUON_COPY_PROBE_VARIANTS-1");
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (bytes > 0 && a < b + bytes && b < a + bytes) return fail(MUON_ERR_ALIAS, "muon: copy probe buffers overlap");
+  if (bytes == 0) return MUON_OK;
+  const hipError_t e = launch_copy_probe(src, dst, static_cast<int64_t>(bytes / 16), variant,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy probe launch");
+  return MUON_OK;
 }
 
 const char* muon_status_string(muon_status_t status) {

@@ -36,6 +36,34 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return u;
 }
 
+// Coefficients of the quintic Newton-Schulz step X <- aX + b(XX^T)X +
+// c(XX^T)^2 X, as the Muon synthesis note (papers.chlience.com, section 4)
+// prints them; float32 constants on the GPU.
+constexpr float kCoefA = 3.4445f;
+constexpr float kCoefB = -4.7750f;
+constexpr float kCoefC = 2.0315f;
+
+// Matrix of a grouped launch that owns work item `blk`: the last i with
+// prefix[i] <= blk (prefix = exclusive prefix sums of work per matrix; a
+// matrix with no work has an empty range and is never returned).
+__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
+  int lo = 0, hi = nmats - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Position of 16-byte k-chunk c (0..3) in a 64-byte LDS operand row r of
+// the matrix-core kernels: chunks XOR-swizzled by ((r >> 1) ^ (r >> 2)),
+// conflict-free for the 32x32x16 and 16x16x32 fragment reads on gfx950.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
+
+// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
+#define MUON_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
 // Matrix-core kernel configurations (tile rows x tile columns, MFMA shape):
 //   G256: 256 x 256, 32x32x16   (Gram, polynomial, BX)
 //   W160: 160 x 256, 32x32x16   (BX only; Gram side a multiple of 160)
@@ -190,6 +218,9 @@ hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* pr
                           const XcdSplit& split, int buf, int first, hipStream_t s);
 hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
                             const XcdSplit& split, int buf, int first, hipStream_t s);
+// Streaming copy of n16 16-byte words (bandwidth yardstick); variant as
+// muon_copy_probe documents.
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, int variant, hipStream_t s);
 hipError_t launch_small_gram(const MatDesc* d, const int32_t* prefix, int nmats, int total, int buf,
                              hipStream_t s);
 hipError_t launch_small_poly(const MatDesc* d, const int32_t* prefix, int nmats, int total,

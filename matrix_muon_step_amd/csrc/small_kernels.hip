@@ -18,21 +18,10 @@ namespace muon {
 
 namespace {
 
-constexpr float kCoefA = 3.4445f;
-constexpr float kCoefB = -4.7750f;
-constexpr float kCoefC = 2.0315f;
 constexpr int SM = kSmallGram;     // 64
 constexpr int SC = kSmallChunk;    // 256
 constexpr int XS = SM + 4;         // LDS row stride of the transposed chunk
 
-__device__ __forceinline__ int find_mat(const int32_t* __restrict__ prefix, int nmats, int blk) {
-  int lo = 0, hi = nmats - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= blk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
 
 // Partial Gram of one 256-column chunk: G_c[i][j] = sum_k X[i][k] X[j][k].
 // Thread t owns the 4x4 block (rows 4*(t/16).., cols 4*(t%16)..).
