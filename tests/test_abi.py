@@ -237,3 +237,34 @@ def test_plan_limits():
     assert info["workspace_bytes"] > 0
     with pytest.raises(mm.MuonError):
         mm.muon_plan_query([(16385, 16385)])
+
+
+def test_copy_probe_errors():
+    L = mm.lib()
+    a, b = BASE * 2, BASE * 3
+    assert L.muon_copy_probe(None, b, 64, 0, None) == mm.MUON_ERR_INVALID_ARG
+    assert L.muon_copy_probe(a + 8, b, 64, 0, None) == mm.MUON_ERR_ALIGN
+    assert L.muon_copy_probe(a, b, 60, 0, None) == mm.MUON_ERR_ALIGN
+    assert L.muon_copy_probe(a, a + 32, 64, 0, None) == mm.MUON_ERR_ALIAS
+    assert L.muon_copy_probe(a, b, 64, -1, None) == mm.MUON_ERR_INVALID_ARG
+    assert L.muon_copy_probe(a, b, 64, bd.MUON_COPY_PROBE_VARIANTS, None) == mm.MUON_ERR_INVALID_ARG
+    assert L.muon_copy_probe(a, b, 0, 0, None) == mm.MUON_OK
+
+
+def test_plan_xcd_edges_uniform_layers():
+    """48 identical layers of 6 matrices: each of the 8 XCDs takes 6 whole
+    layers of every grouped launch, so the XCD shares start exactly at
+    matrices 36, 72, ..., 252, in the Gram, polynomial and BX launches."""
+    import synth
+    w = synth.WORKLOADS["gpt2_xl_1p5b"]
+    _, plans = mm.muon_plan_query([(s.rows, s.cols) for s in w.matrices])
+    edges = {i: p["xcd_edges"] for i, p in enumerate(plans) if p["xcd_edges"]}
+    assert edges == {36 * k: 7 for k in range(1, 8)}
+
+
+def test_plan_xcd_edges_single_matrix():
+    """One matrix with many tiles: every XCD share starts inside it."""
+    _, plans = mm.muon_plan_query([(2048, 7168)])
+    assert plans[0]["xcd_edges"] == 7
+    _, plans = mm.muon_plan_query([(40, 70)])   # float32 path: no matrix-core launch
+    assert plans[0]["xcd_edges"] == 0

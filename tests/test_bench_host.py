@@ -67,3 +67,9 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_info_fields():
+    info = bench.cpu_info()
+    assert set(info) == {"cpu_model", "host_cpus", "blas", "blas_threads"}
+    assert info["host_cpus"] == os.cpu_count()

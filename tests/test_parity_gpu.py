@@ -356,38 +356,3 @@ def test_poisoned_workspace_gives_finite_results(mm):
         assert np.isfinite(Wn).all()
         ref, _, _ = orc.muon_step(W0, g, np.zeros_like(g), 0.95, 0.02)
         assert relfro(Wn, ref) <= NS_TOL
-
-
-# ------------------------------------------------------------------ full-size workloads (sampled)
-def _full_size(mm, name, sample):
-    w = synth.WORKLOADS[name]
-    log_case(f"{name} full size, sampled matrices {sample}")
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(1234 + w.wid)
-    mats, keep = [], {}
-    for i in range(len(w.matrices)):
-        t = synth.torch_matrix(w, i, 0, "cuda", generator=gen)
-        if i in sample:
-            keep[i] = (t["W0"].cpu().numpy().copy(), t["G"].float().cpu().numpy().astype(np.float64))
-        mats.append((t["W0"], t["G"], t["B0"], w.scale))
-    mm.muon_step(mats, mu=w.mu, lr=w.lr, ns_steps=5)
-    torch.cuda.synchronize()
-    for i in sample:
-        W0, g64 = keep[i]
-        Wr, Br, _ = orc.muon_step(W0, g64, np.zeros_like(g64), w.mu, w.lr, w.scale, 5)
-        Wg = mats[i][0].cpu().numpy().astype(np.float64)
-        Bg = mats[i][2].cpu().numpy()
-        assert relfro(Bg, Br) <= FP32_TOL
-        err = relfro(Wg - W0, Wr - W0)
-        print(f"  matrix {i} {w.matrices[i].rows}x{w.matrices[i].cols}: direction relFro {err:.3e}", flush=True)
-        assert err <= NS_TOL
-    del mats
-    torch.cuda.empty_cache()
-
-
-def test_gpt2_xl_full_size_sampled(mm):
-    _full_size(mm, "gpt2_xl_1p5b", [0, 4, 5, 287])
-
-
-def test_moe_share_full_size_sampled(mm):
-    _full_size(mm, "moe_share", [0, 64, 128])
