@@ -90,7 +90,7 @@ BX_KERNEL_RE = {
     (320, 256): r"ns_gemm32_kernel<[^<]*G32<320, 256, 2, 4, 4>, 2>",
 }
 BX_KERNEL_NAME = {(160, 256): "W160", (256, 256): "G256", (320, 256): "W320"}
-CALIB_RE = r"sqrt"
+CALIB_RE = r"copy_probe_kernel"
 
 
 def read_counter_csv(path, counter):
@@ -110,8 +110,8 @@ def read_counter_csv(path, counter):
 def record_traffic(workload, fetch_csv, write_csv, calib_bytes):
     """HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc
     runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
-    same counter reads for a plain elementwise kernel that reads and writes
-    calib_bytes.  Writes profiles/traffic_<workload>.json."""
+    same counter reads for the library's plain copy kernel, which reads and
+    writes calib_bytes.  Writes profiles/traffic_<workload>.json."""
     import re
     import statistics
     import matrix_muon_step_amd as mm
@@ -126,6 +126,7 @@ def record_traffic(workload, fetch_csv, write_csv, calib_bytes):
         counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
         per = read_counter_csv(path, counter)
         cal = [v for k, vs in per.items() if re.search(CALIB_RE, k) for v in vs]
+        cal = cal[:1]  # the calibration copy is the first copy-kernel dispatch
         bx = [v for k, vs in per.items() if pat.search(k) for v in vs]
         assert cal and bx, (name, list(per))
         factor = calib_bytes / (max(cal) * 1024.0)
@@ -142,16 +143,34 @@ def record_traffic(workload, fetch_csv, write_csv, calib_bytes):
     print(json.dumps(rec))
 
 
+def cpu_info():
+    """Host CPU model, logical CPU count and the BLAS numpy runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = None, None
+    try:
+        import threadpoolctl
+        infos = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = f"{infos[0].get('internal_api')} {infos[0].get('version')}"
+            threads = max(int(i.get("num_threads", 1)) for i in infos)
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas": blas, "blas_threads": threads}
+
+
 def cpu_baseline(w, budget_s=20.0):
     """The oracle on the host cores, on a bounded sample of the workload's
     matrices (whole layers, in order), scaled to one full step."""
-    import numpy as np
     from oracle import muon_oracle
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    info = cpu_info()
     per_layer = 6 if len(w.matrices) % 6 == 0 else 1
     t_used = 0.0
     done = 0
@@ -166,32 +185,222 @@ def cpu_baseline(w, budget_s=20.0):
             params_done += w.matrices[i].rows * w.matrices[i].cols
         done = min(done + per_layer, len(w.matrices))
     step_s = t_used * (w.n_params / params_done)
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(info["blas_threads"] or 1), "kind": "oracle",
             "sample": f"first {done} of {len(w.matrices)} matrices ({params_done / 1e6:.1f}M of "
                       f"{w.n_params / 1e6:.1f}M params), one fp64 Muon step each, "
-                      f"{t_used:.1f} s, scaled by parameter count",
-            "seconds_measured": round(t_used, 3)}
+                      f"{t_used:.1f} s, scaled by parameter count (extrapolated)",
+            "seconds_measured": round(t_used, 3), **info}
 
 
-def copy_ceiling_gbps(dev, stream, nbytes=2**30, reps=5):
-    """Measured HBM ceiling for the bandwidth-bound kernels: a plain device
-    copy of nbytes (read + write), HIP events on the launch stream."""
+def copy_ceiling_gbps(dev, nbytes=2**30, reps=10):
+    """Measured HBM ceiling of the bandwidth-bound stages: the fastest variant
+    of the library's streaming copy kernel (read + write nbytes), HIP events
+    on the launch stream."""
     import torch
+    import matrix_muon_step_amd as mm
 
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    stream = torch.cuda.current_stream()
+    best = None
+    for v in range(mm.MUON_COPY_PROBE_VARIANTS):
+        mm.muon_copy_probe(src, dst, v)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            mm.muon_copy_probe(src, dst, v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gbps = 2.0 * nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        if best is None or gbps > best[0]:
+            best = (gbps, v)
+    ok = bool(torch.equal(src, dst))
     del src, dst
-    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+    if not ok:
+        raise RuntimeError("copy probe produced a wrong copy")
+    return best
+
+
+# Steps timed per workload in the default run (the headline uses --steps).
+DEFAULT_STEPS = {"single256": 200, "gpt2s_fc_10step": 100, "gpt2_small": 50, "gpt2_xl_1p5b": 20, "moe_share": 10}
+LATENCY_BOUND = ("single256", "gpt2s_fc_10step")
+
+
+def make_inputs(w, dev, gen):
+    import torch
+    mats = []
+    for i in range(len(w.matrices)):
+        t = synth.torch_matrix(w, i, 0, dev, generator=gen)
+        mats.append((t["W0"], t["G"], t["B0"], w.scale))
+    # gpt2s_fc_10step: consecutive steps of one matrix, each with a fresh gradient
+    grads = None
+    if w.steps > 1:
+        grads = [[synth.torch_matrix(w, i, t, dev, generator=gen)["G"] for i in range(len(w.matrices))]
+                 for t in range(w.steps)]
+    torch.cuda.synchronize()
+    return mats, grads
+
+
+def bench_workload(w, steps, warmup, ns_steps, dev, headline, diag_steps=0, copy_ceiling=None):
+    """Times `steps` muon_step calls of workload w (profiling off), then a
+    separate profiled pass for the per-stage breakdown and the dominant
+    kernel's launch time.  Returns the workload's record."""
+    import torch
+    import matrix_muon_step_amd as mm
+
+    shapes = [(s.rows, s.cols) for s in w.matrices]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240 + w.wid)
+    mats, grads = make_inputs(w, dev, gen)
+    ws_bytes = mm.muon_workspace_bytes(mats, mu=w.mu, lr=w.lr, ns_steps=ns_steps)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: {len(shapes)} matrices, {w.n_params / 1e9:.4f}B params, "
+        f"workspace {ws_bytes / 2**30:.2f} GiB")
+    k = [0]
+
+    def step():
+        cur = mats
+        if grads is not None:
+            g = grads[k[0] % len(grads)]
+            cur = [(W, g[i], B, s) for i, (W, _, B, s) in enumerate(mats)]
+        k[0] += 1
+        mm.muon_step(cur, mu=w.mu, lr=w.lr, ns_steps=ns_steps, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    log(f"[bench] {w.name}: timed {steps} steps, {ms_per_step:.4f} ms/step "
+        f"(host wall {wall / steps * 1e3:.4f} ms/step)")
+
+    # ---- profiled pass: HIP events around every launch, on the launch stream
+    psteps = max(1, min(steps, 5))
+    mm.muon_profile_read()
+    mm.muon_profile_enable(True)
+    p0 = torch.cuda.Event(enable_timing=True)
+    p1 = torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(psteps):
+        step()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    mm.muon_profile_enable(False)
+    prof = mm.muon_profile_read()
+    prof_ms = p0.elapsed_time(p1) / psteps
+    log(f"[bench] {w.name}: profiled {psteps} steps, {prof_ms:.4f} ms/step")
+
+    big = [s for s in shapes if min(s) > 64]
+    stage_ms = {kk: v[0] / psteps for kk, v in prof.items()}
+    fl = {kk: ns_flops(big, kk) * ns_steps for kk in ("gram", "poly", "bx")}
+    ns_ms = stage_ms["gram"] + stage_ms["poly"] + stage_ms["bx"] + stage_ms["bx_update"]
+    ns_alg = fl["gram"] + fl["poly"] + fl["bx"]
+    ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
+    dense_eq = sum(4.0 * min(s) ** 2 * max(s) + 2.0 * min(s) ** 3 for s in big) * ns_steps
+    bx_iters = (ns_steps - 1) * psteps
+    bx_avg_ms = prof["bx"][0] / bx_iters if bx_iters and prof["bx"][1] else None
+    bx_flops_per_launch = ns_flops(big, "bx")
+    bx_tflops = bx_flops_per_launch / (bx_avg_ms * 1e-3) / 1e12 if bx_avg_ms else None
+    plans = mm.muon_plan_query(shapes, ns_steps=ns_steps)[1]
+    g_bytes = 2 if w.g_dtype == "bf16" else 4
+    pair_bytes = sum(4 * p["m_pad"] * p["n_pad"] for p in plans if p["tile"] and ns_steps > 0)
+    mom_bytes = w.n_params * (g_bytes + 8) + pair_bytes
+    mom_gbps = mom_bytes / (stage_ms["momentum"] * 1e-3) / 1e9 if stage_ms["momentum"] else None
+    rec = {
+        "ms_per_step": round(ms_per_step, 4),
+        "steps_per_s": round(1000.0 / ms_per_step, 3),
+        "matrices_per_s": round(len(shapes) * 1000.0 / ms_per_step, 1),
+        "steps": steps,
+        "ns5_alg_tflop_per_step": round(ns_alg / 1e12, 4),
+        "ns5_tflops": round(ns_tflops, 2) if ns_tflops else None,
+        "ns5_frac_of_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
+        "ns5_ms_per_step": round(ns_ms, 4),
+        "step_tflops": round(ns_alg / (ms_per_step * 1e-3) / 1e12, 2),
+        "bx_kernel_tflops": round(bx_tflops, 2) if bx_tflops else None,
+        "bx_frac_of_bf16_peak": round(bx_tflops / PEAK_BF16_TFLOPS, 4) if bx_tflops else None,
+        "momentum_gbps": round(mom_gbps, 1) if mom_gbps else None,
+        "momentum_frac_of_hbm_peak": round(mom_gbps / PEAK_HBM_GBPS, 4) if mom_gbps else None,
+        "momentum_frac_of_copy_ceiling": (round(mom_gbps / copy_ceiling, 4)
+                                          if mom_gbps and copy_ceiling else None),
+        "profiled_ms_per_step": round(prof_ms, 4),
+        "profiling_overhead_ms": round(prof_ms - ms_per_step, 4),
+        "stage_ms_per_step": {kk: round(v, 4) for kk, v in stage_ms.items() if v},
+        "launches_per_step": {kk: v[1] / psteps for kk, v in prof.items() if v[1]},
+    }
+    if w.name in LATENCY_BOUND:
+        rec["bound"] = "launch latency"
+        rec["us_per_step"] = round(ms_per_step * 1e3, 2)
+        rec["note"] = ("about 20 short launches of a few tiles each per step: the time is launch "
+                       "latency, so the roofline fractions do not describe the kernels")
+    if not headline:
+        del mats, ws, grads
+        torch.cuda.empty_cache()
+        return rec
+
+    # ---- the same step with per-matrix diagnostics (reported apart)
+    if diag_steps > 0:
+        dbuf = torch.zeros(len(shapes), 8, dtype=torch.int32, device=dev)
+
+        def dstep():
+            mm.muon_step_diag(mats, mu=w.mu, lr=w.lr, ns_steps=ns_steps, workspace=ws, diag=dbuf)
+
+        dstep()
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(diag_steps):
+            dstep()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        d_ms = d0.elapsed_time(d1) / diag_steps
+        recs = mm.diag_records(dbuf, len(shapes))
+        urms = [r["update_rms"] for r in recs]
+        rec["diagnostics"] = {"steps": diag_steps, "ms_per_step": round(d_ms, 4),
+                              "overhead_ms": round(d_ms - ms_per_step, 4),
+                              "nonfinite_matrices": sum(1 for r in recs if r["nonfinite"]),
+                              "update_rms_min": min(urms), "update_rms_max": max(urms)}
+        log(f"[bench] with diagnostics: {d_ms:.3f} ms/step")
+    bx_cfgs = sorted({(p["bx_tile_rows"], p["bx_tile_cols"]) for p in plans if p["tile"]})
+    kname = "+".join(f"ns_gemm32_kernel<{BX_KERNEL_NAME[c]}, BX>" if c in BX_KERNEL_NAME
+                     else f"ns_gemm_kernel<T{c[0]}, BX>" for c in bx_cfgs)
+    rec["roofline"] = {
+        "kernel": f"{kname} (X' = a X + P X)",
+        "bound": "mfma",
+        "achieved": round(bx_tflops, 2) if bx_tflops else None,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(bx_tflops / PEAK_BF16_TFLOPS, 4) if bx_tflops else None,
+        "traffic": load_traffic(TRAFFIC_SOURCES, w.name),
+        "avg_launch_ms": round(bx_avg_ms, 4) if bx_avg_ms else None,
+        "launches_per_step": prof["bx"][1] / psteps,
+        "alg_flops_per_launch": bx_flops_per_launch,
+    }
+    rec["ns5"] = {
+        "alg_tflop_per_step": round(ns_alg / 1e12, 3),
+        "tflops": round(ns_tflops, 2) if ns_tflops else None,
+        "frac_of_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
+        "effective_dense_tflops": round(dense_eq / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
+        "ms_per_step": round(ns_ms, 4),
+    }
+    rec["config"] = {"workload": w.name, "matrices": len(shapes), "params": w.n_params,
+                     "shapes": sorted({f"{r}x{c}" for r, c in shapes}), "ns_steps": ns_steps,
+                     "mu": w.mu, "lr": w.lr, "g_dtype": w.g_dtype}
+    del mats, ws, grads
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -199,14 +408,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gpt2_xl_1p5b", choices=list(synth.ORDER))
+    ap.add_argument("--workload", default="gpt2_xl_1p5b", choices=list(synth.ORDER),
+                    help="the headline workload (value, roofline, cpu_baseline)")
+    ap.add_argument("--only", action="store_true", help="time the headline workload alone")
     ap.add_argument("--ns-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--diag-steps", type=int, default=5,
                     help="after the timed steps, time this many steps with the per-matrix "
                          "diagnostics (muon_step_diag) and report their cost; 0 = skip")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="also run one device copy of this many MiB (counter calibration)")
+                    help="also run one plain copy of this many MiB with the library's copy "
+                         "kernel (counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a run with "
@@ -230,170 +442,60 @@ def main():
         sys.exit(1)
     mm.lib()
     dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[args.workload]
-    shapes = [(s.rows, s.cols) for s in w.matrices]
-    log(f"[bench] workload {w.name}: {len(shapes)} matrices, {w.n_params / 1e9:.3f}B params")
-
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(20240 + w.wid)
-    mats = []
-    for i in range(len(shapes)):
-        t = synth.torch_matrix(w, i, 0, dev, generator=gen)
-        mats.append((t["W0"], t["G"], t["B0"], w.scale))
-    ws_bytes = mm.muon_workspace_bytes(mats, mu=w.mu, lr=w.lr, ns_steps=args.ns_steps)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
-    log(f"[bench] inputs resident; workspace {ws_bytes / 2**30:.2f} GiB")
 
     if args.copy_calibration_mib:
         nb = args.copy_calibration_mib * 2**20
         src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        torch.sqrt(src, out=dst)  # one elementwise kernel: reads nb bytes, writes nb bytes
+        mm.muon_copy_probe(src, dst, 0)  # reads nb bytes, writes nb bytes
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {nb} bytes read, {nb} bytes written")
         del src, dst
 
-    def step():
-        mm.muon_step(mats, mu=w.mu, lr=w.lr, ns_steps=args.ns_steps, workspace=ws)
-
-    for k in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"[bench] warmup {k + 1}/{args.warmup} done")
-
-    mm.muon_profile_read()  # discard anything pending
-    mm.muon_profile_enable(True)
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for k in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    mm.muon_profile_enable(False)
-    prof = mm.muon_profile_read()
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
-
-    # ---- the same step with per-matrix diagnostics (reported apart; the
-    # metric above is the plain step)
-    diag_info = None
-    if args.diag_steps > 0:
-        dbuf = torch.zeros(len(shapes), 8, dtype=torch.int32, device=dev)
-
-        def dstep():
-            mm.muon_step_diag(mats, mu=w.mu, lr=w.lr, ns_steps=args.ns_steps, workspace=ws, diag=dbuf)
-
-        dstep()
-        torch.cuda.synchronize()
-        d0 = torch.cuda.Event(enable_timing=True)
-        d1 = torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for k in range(args.diag_steps):
-            dstep()
-        d1.record(stream)
-        torch.cuda.synchronize()
-        d_ms = d0.elapsed_time(d1) / args.diag_steps
-        recs = mm.diag_records(dbuf, len(shapes))
-        urms = [r["update_rms"] for r in recs]
-        diag_info = {"steps": args.diag_steps, "ms_per_step": round(d_ms, 4),
-                     "overhead_ms": round(d_ms - ms_per_step, 4),
-                     "nonfinite_matrices": sum(1 for r in recs if r["nonfinite"]),
-                     "update_rms_min": min(urms), "update_rms_max": max(urms)}
-        log(f"[bench] with diagnostics: {d_ms:.3f} ms/step")
-
-    # ---- per-stage figures (HIP events around every launch, same stream)
-    big = [s for s in shapes if min(s) > 64]
-    stage_ms = {k: v[0] / args.steps for k, v in prof.items()}
-    launches = {k: v[1] / args.steps for k, v in prof.items()}
-    fl = {k: ns_flops(big, k) * args.ns_steps for k in ("gram", "poly", "bx")}
-    ns_ms = stage_ms["gram"] + stage_ms["poly"] + stage_ms["bx"] + stage_ms["bx_update"]
-    ns_alg = fl["gram"] + fl["poly"] + fl["bx"]
-    ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else None
-    dense_eq = sum(4.0 * min(s) ** 2 * max(s) + 2.0 * min(s) ** 3 for s in big) * args.ns_steps
-    # Dominant kernel: the BX + aX product of the first ns_steps - 1
-    # iterations (the last one also applies the update and is timed apart).
-    # One launch per iteration covers every matrix when they share a tile
-    # configuration (all workloads here do); the figure is per iteration.
-    bx_iters = (args.ns_steps - 1) * args.steps
-    bx_launches = prof["bx"][1]
-    bx_avg_ms = prof["bx"][0] / bx_iters if bx_iters and bx_launches else None
-    bx_flops_per_launch = ns_flops(big, "bx")
-    bx_tflops = bx_flops_per_launch / (bx_avg_ms * 1e-3) / 1e12 if bx_avg_ms else None
-    bx_cfgs = sorted({(p["bx_tile_rows"], p["bx_tile_cols"]) for p in mm.muon_plan_query(shapes)[1] if p["tile"]})
-    kname = "+".join(f"ns_gemm32_kernel<{BX_KERNEL_NAME[c]}, BX>" if c in BX_KERNEL_NAME
-                     else f"ns_gemm_kernel<T{c[0]}, BX>" for c in bx_cfgs)
-    traffic = load_traffic(TRAFFIC_SOURCES, w.name)
-    n_el = w.n_params
-    g_bytes = 2 if w.g_dtype == "bf16" else 4
-    # read G, B; write B; and, where the normalisation is folded into the
-    # first iteration (Gram side > 64, ns_steps > 0), the padded bf16 pair
-    plans = mm.muon_plan_query(shapes, ns_steps=args.ns_steps)[1]
-    pair_bytes = sum(4 * p["m_pad"] * p["n_pad"] for p in plans if p["tile"] and args.ns_steps > 0)
-    mom_bytes = n_el * (g_bytes + 8) + pair_bytes
-    upd_bytes = n_el * (8 + 4)                # read W + X pair, write W
-    ew = {
-        "momentum_gbps": mom_bytes / (stage_ms["momentum"] * 1e-3) / 1e9 if stage_ms["momentum"] else None,
-        "update_gbps": upd_bytes / (stage_ms["update"] * 1e-3) / 1e9 if stage_ms["update"] else None,
-        "copy_ceiling_gbps": copy_ceiling_gbps(dev, stream),
-    }
-
+    ceiling, ceiling_variant = copy_ceiling_gbps(dev)
+    log(f"[bench] copy ceiling {ceiling:.0f} GB/s (variant {ceiling_variant})")
+    names = [args.workload] if args.only else [n for n in synth.ORDER]
+    records = {}
+    for name in names:
+        w = synth.WORKLOADS[name]
+        head = name == args.workload
+        steps = args.steps if head else DEFAULT_STEPS[name]
+        records[name] = bench_workload(w, steps, args.warmup, args.ns_steps, dev, head,
+                                       diag_steps=args.diag_steps if head else 0, copy_ceiling=ceiling)
+    h = records[args.workload]
+    w = synth.WORKLOADS[args.workload]
     out = {
         "metric": METRIC,
-        "value": round(1000.0 / ms_per_step, 4),
+        "value": h["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (low-rank plus noise gradients drawn on the GPU, random-init fp32 weights)",
-        "config": {"workload": w.name, "matrices": len(shapes), "params": n_el,
-                   "shapes": sorted({f"{r}x{c}" for r, c in shapes}), "ns_steps": args.ns_steps,
-                   "mu": w.mu, "lr": w.lr, "g_dtype": w.g_dtype},
-        "roofline": {
-            "kernel": f"{kname} (X' = a X + P X)",
-            "bound": "mfma",
-            "achieved": round(bx_tflops, 2) if bx_tflops else None,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(bx_tflops / PEAK_BF16_TFLOPS, 4) if bx_tflops else None,
-            "traffic": traffic,
-            "avg_launch_ms": round(bx_avg_ms, 4) if bx_avg_ms else None,
-            "launches_per_step": bx_launches / args.steps,
-            "alg_flops_per_launch": bx_flops_per_launch,
+        "config": h.pop("config"),
+        "roofline": h.pop("roofline"),
+        "ns5": h.pop("ns5"),
+        "matrices_per_s": h["matrices_per_s"],
+        "stage_ms_per_step": h["stage_ms_per_step"],
+        "launches_per_step": h["launches_per_step"],
+        "profiled_ms_per_step": h["profiled_ms_per_step"],
+        "elementwise": {
+            "momentum_gbps": h["momentum_gbps"],
+            "copy_ceiling_gbps": round(ceiling, 1),
+            "copy_ceiling_kernel": f"muon_copy_probe variant {ceiling_variant}",
+            "momentum_frac_of_hbm_peak": h["momentum_frac_of_hbm_peak"],
+            "momentum_frac_of_copy_ceiling": h["momentum_frac_of_copy_ceiling"],
         },
-        "ns5": {
-            "alg_tflop_per_step": round(ns_alg / 1e12, 3),
-            "tflops": round(ns_tflops, 2) if ns_tflops else None,
-            "frac_of_bf16_peak": round(ns_tflops / PEAK_BF16_TFLOPS, 4) if ns_tflops else None,
-            "effective_dense_tflops": round(dense_eq / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
-            "ms_per_step": round(ns_ms, 4),
-        },
-        "matrices_per_s": round(len(shapes) * 1000.0 / ms_per_step, 1),
-        "stage_ms_per_step": {k: round(v, 4) for k, v in stage_ms.items()},
-        "launches_per_step": launches,
-        "elementwise": dict(
-            {k: (round(v, 1) if v else None) for k, v in ew.items()},
-            momentum_frac_of_hbm_peak=round(ew["momentum_gbps"] / PEAK_HBM_GBPS, 4) if ew["momentum_gbps"] else None,
-            momentum_frac_of_copy_ceiling=(round(ew["momentum_gbps"] / ew["copy_ceiling_gbps"], 4)
-                                           if ew["momentum_gbps"] and ew["copy_ceiling_gbps"] else None)),
         "hbm_peak_gbps": PEAK_HBM_GBPS,
-        "diagnostics": diag_info,
+        "diagnostics": h.pop("diagnostics", None),
+        "workloads": records,
     }
-
-    del mats, ws
-    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w)
