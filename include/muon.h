@@ -132,6 +132,24 @@ size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n, const muon_hpa
 muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* muon_step for callers that cannot allocate device memory (serving loops
+ * and harnesses that forbid hipMalloc): the same kernels and the same bits
+ * as muon_step, with the workspace in a static device array of the library
+ * instead of a caller's buffer.  The array holds MUON_STATIC_WORKSPACE_BYTES
+ * (64 MiB) on every GPU the library runs on, from the first use on that GPU
+ * until the process ends; a call whose workspace (muon_workspace_bytes)
+ * exceeds it returns MUON_ERR_WORKSPACE before anything is enqueued.  The
+ * call allocates nothing: no device memory and no pinned host memory (its
+ * descriptor table is copied from the call's own host memory, which the
+ * copy has consumed when the call returns; so this entry point is not for
+ * stream capture).  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (every byte a call reads it writes first):
+ * calls that overlap on one GPU (other threads, other streams) race and
+ * must be ordered by the caller.  The address of the array is looked up once
+ * per device, with that device current. */
+#define MUON_STATIC_WORKSPACE_BYTES (64u * 1024u * 1024u)
+muon_status_t muon_step_static(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* stream);
+
 /* Per-matrix diagnostics of one step: the layer-wise quantities that the
  * practice checklist of the synthesis note asks a Muon run to record
  * (item 4 of its local-discussion part: update RMS per matrix shape,

@@ -29,6 +29,7 @@ MUON_MAX_NS_STEPS = 64
 MUON_MAX_DIM = 65536
 MUON_MAX_GRAM = 16384
 MUON_COPY_PROBE_VARIANTS = 6
+MUON_STATIC_WORKSPACE_BYTES = 64 * 1024 * 1024
 STAGES = ("momentum", "norm", "prep", "gram", "poly", "bx", "update", "upload", "bx_update", "diag")
 MUON_STAGE_COUNT = len(STAGES)
 
@@ -126,6 +127,8 @@ def lib() -> ctypes.CDLL:
                 L.muon_step.restype = ctypes.c_int
                 L.muon_step.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                L.muon_step_static.restype = ctypes.c_int
+                L.muon_step_static.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t), ctypes.c_void_p]
                 L.muon_step_diag.restype = ctypes.c_int
                 L.muon_step_diag.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -291,6 +294,21 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
         ws_ptr, ws_len = _ws_args(workspace)
         _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
                                ctypes.c_void_p(st.cuda_stream)))
+
+
+def muon_step_static(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7, stream=None,
+                     weight_decay=0.0) -> None:
+    """muon_step with the library's static device workspace: allocates
+    nothing (no torch allocation, no hipMalloc).  Raises MuonError
+    (MUON_ERR_WORKSPACE) when the call needs more than
+    MUON_STATIC_WORKSPACE_BYTES of workspace."""
+    entries, gd = _tensor_entries(matrices)
+    if not entries:
+        return
+    arr = raw_matrix_array(entries)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
+    st = _torch_stream(stream)
+    _check(lib().muon_step_static(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(st.cuda_stream)))
 
 
 def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,

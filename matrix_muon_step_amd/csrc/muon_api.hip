@@ -15,6 +15,13 @@
 
 using namespace muon;
 
+// Workspace of muon_step_static: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  In host code the
+// array's name is only a host-side stand-in; its device address on the
+// current device comes from hipGetSymbolAddress, taken once per device and
+// kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[MUON_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -455,8 +462,11 @@ muon_status_t hip_fail(hipError_t e, const char* where) {
 // workspace, then every stage is one grouped launch over all matrices.
 // With `diag_out` (a device muon_diag_t array) the W-writing kernels also
 // sum the diagnostics and a last launch reduces them.
+// `pageable`: copy the table straight from this call's host memory (the
+// copy has consumed it when hipMemcpyAsync returns) instead of through the
+// pinned staging ring, which allocates pinned memory on first use.
 muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStream_t s,
-                      void* diag_out = nullptr) {
+                      void* diag_out = nullptr, bool pageable = false) {
   const int n = static_cast<int>(plan.descs.size());
   const uintptr_t base = reinterpret_cast<uintptr_t>(workspace);
   bind_workspace(plan, base);
@@ -477,7 +487,10 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   auto ttot = [&](int k) { return static_cast<int>(plan.tot[k]); };
 
   hipError_t e;
-  e = run_stage(MUON_STAGE_UPLOAD, s, [&] { return upload_table(table.data(), table.size(), workspace, s); });
+  e = run_stage(MUON_STAGE_UPLOAD, s, [&] {
+    return pageable ? hipMemcpyAsync(workspace, table.data(), table.size(), hipMemcpyHostToDevice, s)
+                    : upload_table(table.data(), table.size(), workspace, s);
+  });
   if (e != hipSuccess) return hip_fail(e, "descriptor upload");
   e = run_stage(MUON_STAGE_MOMENTUM, s, [&] { return launch_momentum(d_desc, ptab(kTabMom), n, ttot(kTabMom), mu, s); });
   if (e != hipSuccess) return hip_fail(e, "momentum launch");
@@ -599,6 +612,31 @@ void fill_ptrs(Plan& plan, const std::vector<Item>& items) {
   }
 }
 
+// ---------------------------------------------------------------- static workspace
+// Device address of `scratch` per device (looked up once per device).
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void*>> g_scratch_ptr;  // (device, address of scratch there)
+
+muon_status_t static_workspace(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (const auto& p : g_scratch_ptr)
+    if (p.first == dev) {
+      *out = p.second;
+      return MUON_OK;
+    }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static workspace");
+  if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign)
+    return fail(MUON_ERR_HIP, "muon: the static workspace has no 256-byte aligned device address");
+  g_scratch_ptr.emplace_back(dev, ptr);
+  *out = ptr;
+  return MUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -613,8 +651,11 @@ size_t muon_workspace_bytes(const muon_matrix_t* mats, int64_t n, const muon_hpa
   return plan.total_bytes;
 }
 
+// use_static: the workspace is the library's static device array (after the
+// plan is checked to fit it); `workspace` and `workspace_bytes` are ignored.
 static muon_status_t step_impl(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
-                               muon_diag_t* diag, void* workspace, size_t workspace_bytes, void* stream) {
+                               muon_diag_t* diag, void* workspace, size_t workspace_bytes, void* stream,
+                               bool use_static = false) {
   std::vector<Item> items;
   muon_status_t st = items_from_step(mats, n, hp, true, items);
   if (st != MUON_OK) return st;
@@ -622,6 +663,15 @@ static muon_status_t step_impl(const muon_matrix_t* mats, int64_t n, const muon_
   Plan plan;
   st = make_plan(items, hp->ns_steps, plan);
   if (st != MUON_OK) return st;
+  if (use_static) {
+    if (plan.total_bytes > MUON_STATIC_WORKSPACE_BYTES)
+      return fail(MUON_ERR_WORKSPACE, "muon: this call needs " + std::to_string(plan.total_bytes) +
+                                          " bytes of workspace; the static workspace holds " +
+                                          std::to_string(static_cast<size_t>(MUON_STATIC_WORKSPACE_BYTES)));
+    st = static_workspace(&workspace);
+    if (st != MUON_OK) return st;
+    workspace_bytes = MUON_STATIC_WORKSPACE_BYTES;
+  }
   st = check_workspace(plan, workspace, workspace_bytes);
   if (st != MUON_OK) return st;
   std::vector<Range> rs;
@@ -638,13 +688,18 @@ static muon_status_t step_impl(const muon_matrix_t* mats, int64_t n, const muon_
   st = check_aliasing(rs);
   if (st != MUON_OK) return st;
   fill_ptrs(plan, items);
-  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream), diag);
+  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream), diag, use_static);
 }
 
 muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
                         void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   return step_impl(mats, n, hp, nullptr, workspace, workspace_bytes, stream);
+}
+
+muon_status_t muon_step_static(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* stream) {
+  g_last_error.clear();
+  return step_impl(mats, n, hp, nullptr, nullptr, 0, stream, true);
 }
 
 muon_status_t muon_step_diag(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,

@@ -268,3 +268,27 @@ def test_plan_xcd_edges_single_matrix():
     assert plans[0]["xcd_edges"] == 7
     _, plans = mm.muon_plan_query([(40, 70)])   # float32 path: no matrix-core launch
     assert plans[0]["xcd_edges"] == 0
+
+
+def test_step_static_rejects_before_any_gpu_call():
+    """muon_step_static validates and sizes the call on the host: arguments
+    errors and a workspace beyond the static array come back without a GPU
+    (this container has none) and without touching the device."""
+    L = mm.lib()
+    hp = bd.hparams()
+    assert L.muon_step_static(None, 0, ctypes.byref(hp), None) == mm.MUON_OK
+    arr = bd.raw_matrix_array([good(0, 4096, 4096)])
+    assert L.muon_step_static(arr, 1, ctypes.byref(hp), None) == mm.MUON_ERR_WORKSPACE
+    msg = mm.muon_last_error()
+    assert "static workspace holds" in msg and str(bd.MUON_STATIC_WORKSPACE_BYTES) in msg
+    arr = bd.raw_matrix_array([(0, BASE * 2, BASE * 3, 64, 64, 1.0)])
+    assert L.muon_step_static(arr, 1, ctypes.byref(hp), None) == mm.MUON_ERR_INVALID_ARG
+    bad_hp = bd.hparams(ns_steps=-1)
+    arr = bd.raw_matrix_array([good(0)])
+    assert L.muon_step_static(arr, 1, ctypes.byref(bad_hp), None) == mm.MUON_ERR_INVALID_ARG
+
+
+def test_static_workspace_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "muon.h")).read()
+    m = re.search(r"#define MUON_STATIC_WORKSPACE_BYTES \((\d+)u \* 1024u \* 1024u\)", src)
+    assert m and int(m.group(1)) * 2**20 == bd.MUON_STATIC_WORKSPACE_BYTES
