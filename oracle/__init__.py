@@ -10,4 +10,5 @@ from .muon_oracle import (  # noqa: F401
     newton_schulz,
     apply_update,
     muon_step,
+    qk_clip,
 )

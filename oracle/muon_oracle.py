@@ -40,7 +40,8 @@ mathematics rather than to itself: the SVD closed form of the iteration,
 transpose equivariance, singular vectors, the polynomial band, rank-one,
 partial-permutation and zero special cases, the momentum closed form and
 the update's linearity; the diagnostics by rank-one and scaled-orthogonal
-closed forms, the decay-only step and the non-finite cases.
+closed forms, the decay-only step and the non-finite cases; QK-Clip by the
+max logit it leaves on every head of random attention projections.
 """
 from __future__ import annotations
 
@@ -157,3 +158,27 @@ def muon_step_diag(W: np.ndarray, G: np.ndarray, B: np.ndarray, mu: float, lr: f
     O = newton_schulz(M, ns_steps, eps)
     W_new = apply_update(W, O, lr, scale, weight_decay)
     return W_new, B_new, O, diagnostics(W, W_new, M, O)
+
+
+def qk_clip(W: np.ndarray, head_dim: int, max_logits, tau: float) -> np.ndarray:
+    """QK-Clip of the Kimi K2 result (results section, result 3, of the
+    synthesis note): after the Muon step, the query and key projection
+    weights of every attention head whose max logit exceeds a threshold are
+    rescaled to bring that logit back.  The page gives neither the rule
+    nor the threshold; the reading taken (design notes, R18):
+
+    * ``W`` is a query or key projection in the (out, in) layout, rows
+      ``h * head_dim .. (h + 1) * head_dim`` belonging to head ``h``;
+    * ``max_logits[h]`` is head h's max attention logit ``S_h`` and
+      ``tau > 0`` the threshold;
+    * a head with ``S_h > tau`` has its rows multiplied by
+      ``sqrt(tau / S_h)``.  Applied to both the query and the key
+      projection, every logit of the head (bilinear in the two) is
+      multiplied by ``tau / S_h``, so its max becomes ``tau``; other heads
+      are left as they are.
+    """
+    W = np.array(W, dtype=np.float64)
+    for h, s in enumerate(np.asarray(max_logits, dtype=np.float64)):
+        if s > tau:
+            W[h * head_dim:(h + 1) * head_dim] *= np.sqrt(tau / s)
+    return W

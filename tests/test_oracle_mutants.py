@@ -4,8 +4,9 @@ Each mutant below is a copy of one oracle function with one plausible
 mistake: a flipped sign or swapped coefficient, a dropped term, a missing
 square, one iteration too few, no transpose back, the spectral instead of
 the Frobenius norm, no eps, a wrong momentum or Nesterov recurrence, a
-wrong update sign, an ignored per-matrix scale, or weight decay applied
-to the new weights.  With the mutant patched into ``oracle.muon_oracle``,
+wrong update sign, an ignored per-matrix scale, weight decay applied
+to the new weights, or a QK-Clip that scales by tau/S instead of its root,
+scales column blocks, or clips every head.  With the mutant patched into ``oracle.muon_oracle``,
 the pins of ``test_oracle_pins`` run again, and at least one of them must
 fail.  The unpatched oracle passes every one of them.
 
@@ -89,6 +90,21 @@ def _update(kind):
     return apply_update
 
 
+def _qk_clip(kind):
+    def qk_clip(W, head_dim, max_logits, tau):
+        W = np.array(W, dtype=np.float64)
+        for h, s in enumerate(np.asarray(max_logits, dtype=np.float64)):
+            if kind == "every head" or s > tau:
+                f = tau / s if kind == "no root" else np.sqrt(tau / s)
+                if kind == "columns":
+                    W[:, h * head_dim:(h + 1) * head_dim] *= f
+                else:
+                    W[h * head_dim:(h + 1) * head_dim] *= f
+        return W
+
+    return qk_clip
+
+
 MUTANTS = {
     "b sign flipped": ("newton_schulz", _ns(_step(A0, -B0, C0))),
     "a and c swapped": ("newton_schulz", _ns(_step(C0, B0, A0))),
@@ -104,6 +120,9 @@ MUTANTS = {
     "update sign": ("apply_update", _update("sign")),
     "scale ignored": ("apply_update", _update("scale_ignored")),
     "decay on the new weights": ("apply_update", _update("decay_after")),
+    "QK-Clip factor without the root": ("qk_clip", _qk_clip("no root")),
+    "QK-Clip on column blocks": ("qk_clip", _qk_clip("columns")),
+    "QK-Clip on every head": ("qk_clip", _qk_clip("every head")),
 }
 
 
@@ -133,6 +152,11 @@ def _pin_calls():
         calls.append((pins.test_singular_vectors_preserved, dict(shape=shape)))
     for j, value in [(3, 0.688140), (5, 1.132924)]:
         calls.append((pins.test_signed_partial_permutation, dict(j=j, value=value)))
+    for heads, head_dim, d_model in [(6, 4, 24), (5, 8, 16), (3, 16, 40)]:
+        calls.append((pins.test_qk_clip_brings_every_clipped_head_to_tau,
+                      dict(heads=heads, head_dim=head_dim, d_model=d_model)))
+    calls += [(pins.test_qk_clip_threshold_above_every_head_is_identity, {}),
+              (pins.test_qk_clip_power_of_four_factor, {})]
     return calls
 
 

@@ -338,3 +338,55 @@ def test_diagnostics_nonfinite_flags(bad, where, flags):
     _, _, _, ok = orc.muon_step_diag(rng.standard_normal((4, 6)), rng.standard_normal((4, 6)),
                                      np.zeros((4, 6)), mu=0.9, lr=0.02)
     assert ok["nonfinite"] == 0
+
+
+# ---------------------------------------------------------------- QK-Clip (reading R18)
+def _head_max_logits(Wq, Wk, X, head_dim):
+    """Per-head max attention logit of tokens X, q.k / sqrt(head_dim)."""
+    H = Wq.shape[0] // head_dim
+    out = np.empty(H)
+    for h in range(H):
+        rows = slice(h * head_dim, (h + 1) * head_dim)
+        Q = X @ Wq[rows].T
+        K = X @ Wk[rows].T
+        out[h] = np.max(Q @ K.T) / np.sqrt(head_dim)
+    return out
+
+
+@pytest.mark.parametrize("heads,head_dim,d_model", [(6, 4, 24), (5, 8, 16), (3, 16, 40)])
+def test_qk_clip_brings_every_clipped_head_to_tau(heads, head_dim, d_model):
+    """Clipping the query and the key projection of one attention layer with
+    the same per-head max logits: every head whose max logit exceeded tau
+    now has max logit tau (logits are bilinear in the two projections, each
+    scaled by sqrt(tau / S)); every other head keeps its rows bit for bit."""
+    rng = np.random.default_rng([90, heads, head_dim])
+    Wq = rng.standard_normal((heads * head_dim, d_model)) * rng.uniform(0.5, 3.0, (heads * head_dim, 1))
+    Wk = rng.standard_normal((heads * head_dim, d_model))
+    X = rng.standard_normal((12, d_model))
+    S = _head_max_logits(Wq, Wk, X, head_dim)
+    tau = float(np.median(S))
+    Wq2 = orc.qk_clip(Wq, head_dim, S, tau)
+    Wk2 = orc.qk_clip(Wk, head_dim, S, tau)
+    S2 = _head_max_logits(Wq2, Wk2, X, head_dim)
+    clipped = S > tau
+    assert 0 < clipped.sum() < heads
+    assert np.allclose(S2[clipped], tau, rtol=1e-12, atol=0)
+    assert np.array_equal(S2[~clipped], S[~clipped])
+    for h in np.flatnonzero(~clipped):
+        rows = slice(h * head_dim, (h + 1) * head_dim)
+        assert np.array_equal(Wq2[rows], Wq[rows]) and np.array_equal(Wk2[rows], Wk[rows])
+
+
+def test_qk_clip_threshold_above_every_head_is_identity():
+    rng = np.random.default_rng(91)
+    W = rng.standard_normal((12, 7))
+    S = np.array([1.0, 5.0, -2.0])
+    assert np.array_equal(orc.qk_clip(W, 4, S, 5.0), W)
+
+
+def test_qk_clip_power_of_four_factor():
+    """S = tau * 4^k scales the head's rows by exactly 2^-k."""
+    W = np.arange(24.0).reshape(6, 4)
+    out = orc.qk_clip(W, 2, [8.0, 2.0, 128.0], 2.0)
+    assert np.array_equal(out[0:2], W[0:2] / 2) and np.array_equal(out[2:4], W[2:4])
+    assert np.array_equal(out[4:6], W[4:6] / 8)
