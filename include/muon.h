@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 5
+#define MUON_ABI_VERSION 6
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -255,6 +255,39 @@ typedef enum muon_stage {
 
 muon_status_t muon_profile_enable(int32_t on);
 muon_status_t muon_profile_read(double* ms, int64_t* launches);
+
+/* QK-Clip: after a step, rescale attention query and key projections head by
+ * head from each head's max logit, to keep attention logits from growing
+ * without bound.  The synthesis note's results section (result 3, Kimi K2's
+ * MuonClip) describes this rescale after the Muon step without a formula or
+ * threshold; the reading implemented: rows h*head_dim .. (h+1)*head_dim-1
+ * of W belong to head h (the (out, in) layout of a projection), and when
+ * max_logit[h] > tau they are multiplied by sqrt(tau / max_logit[h])
+ * (float32 division and square root, correctly rounded; one rounding per
+ * element).  Clipping the query and the key projection of one attention
+ * layer with the same max_logit array scales every logit of a clipped head
+ * by tau / max_logit[h], so its max logit becomes tau; heads at or below
+ * tau (or with a NaN max logit) are not touched.  An infinite max logit
+ * zeroes the head's rows.
+ *   W          DEVICE, rows x cols float32 row-major, 16-byte aligned,
+ *              updated in place; disjoint from every other W of the call
+ *   rows, cols >= 1, <= MUON_MAX_DIM; rows a multiple of head_dim
+ *   head_dim   >= 1
+ *   max_logit  DEVICE, rows / head_dim float32 entries, 4-byte aligned,
+ *              read only (Q and K of one layer may share it)
+ * tau: finite, > 0.  mats is HOST memory read during the call.  One launch
+ * per 48 matrices (the descriptors travel as kernel arguments; no
+ * workspace); a head whose factor is 1 costs one read.  Stream-ordered:
+ * call it after muon_step on the same stream. */
+typedef struct muon_qk_clip_matrix {
+  float* W;
+  int64_t rows;
+  int64_t cols;
+  int32_t head_dim;
+  int32_t reserved;
+  const float* max_logit;
+} muon_qk_clip_matrix_t;
+muon_status_t muon_qk_clip(const muon_qk_clip_matrix_t* mats, int64_t n, float tau, void* stream);
 
 /* Bandwidth yardstick for the HBM-bound stages (the measurement side of the
  * boundary, not part of a step): copies `bytes` from src to dst (DEVICE

@@ -7,5 +7,5 @@ from .binding import (  # noqa: F401
     muon_step_static, MUON_STATIC_WORKSPACE_BYTES,
     muon_step_diag, diag_records, DIAG_FIELDS,
     muon_orthogonalize_workspace_bytes, muon_orthogonalize, muon_plan_query,
-    muon_profile_enable, muon_profile_read, muon_copy_probe, lib, LIB_PATH,
+    muon_profile_enable, muon_profile_read, muon_copy_probe, muon_qk_clip, lib, LIB_PATH,
 )

@@ -100,6 +100,17 @@ class muon_matrix_plan_t(ctypes.Structure):
     ]
 
 
+class muon_qk_clip_matrix_t(ctypes.Structure):
+    _fields_ = [
+        ("W", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("head_dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("max_logit", ctypes.c_void_p),
+    ]
+
+
 class MuonError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{muon_status_string(status)}: {message}")
@@ -148,6 +159,9 @@ def lib() -> ctypes.CDLL:
                 L.muon_profile_enable.argtypes = [ctypes.c_int32]
                 L.muon_profile_read.restype = ctypes.c_int
                 L.muon_profile_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64)]
+                L.muon_qk_clip.restype = ctypes.c_int
+                L.muon_qk_clip.argtypes = [P(muon_qk_clip_matrix_t), ctypes.c_int64, ctypes.c_float,
+                                           ctypes.c_void_p]
                 L.muon_copy_probe.restype = ctypes.c_int
                 L.muon_copy_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                               ctypes.c_void_p]
@@ -433,3 +447,24 @@ def muon_copy_probe(src, dst, variant: int = 0, stream=None) -> None:
     with torch.cuda.stream(st):
         _check(lib().muon_copy_probe(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
                                      int(variant), ctypes.c_void_p(st.cuda_stream)))
+
+
+def muon_qk_clip(matrices, tau: float, stream=None) -> None:
+    """QK-Clip after a step: for each (W, head_dim, max_logit) with W a float32
+    (heads * head_dim, cols) projection and max_logit a float32 tensor of
+    its heads' max logits, the rows of every head with max_logit > tau are
+    scaled by sqrt(tau / max_logit) in place."""
+    import torch
+
+    n = len(matrices)
+    arr = (muon_qk_clip_matrix_t * max(1, n))()
+    for k, (W, head_dim, S) in enumerate(matrices):
+        if not W.is_cuda or W.dtype != torch.float32 or W.dim() != 2 or not W.is_contiguous():
+            raise ValueError(f"matrix {k}: W must be a contiguous float32 2-D GPU tensor")
+        if not S.is_cuda or S.dtype != torch.float32 or not S.is_contiguous():
+            raise ValueError(f"matrix {k}: max_logit must be a contiguous float32 GPU tensor")
+        if W.shape[0] % int(head_dim) or S.numel() != W.shape[0] // int(head_dim):
+            raise ValueError(f"matrix {k}: rows must be heads * head_dim and max_logit hold one entry per head")
+        arr[k] = muon_qk_clip_matrix_t(W.data_ptr(), W.shape[0], W.shape[1], int(head_dim), 0, S.data_ptr())
+    st = _torch_stream(stream)
+    _check(lib().muon_qk_clip(arr, n, float(tau), ctypes.c_void_p(st.cuda_stream)))

@@ -413,6 +413,34 @@ __global__ __launch_bounds__(256) void diag_kernel(const MatDesc* __restrict__ d
   }
 }
 
+// ---------------------------------------------------------------- QK-Clip
+// After the step, QK-Clip (the Kimi K2 result in the results section of the
+// synthesis note) rescales the query and key projections head by head from
+// the head's max logit.  One work-group per (matrix, head): a head whose
+// max logit S is not above tau returns after reading S; otherwise its rows
+// (contiguous, head_dim * cols floats) are multiplied by sqrt(tau / S)
+// (float32 division and square root, both correctly rounded).
+__global__ __launch_bounds__(256) void qk_clip_kernel(const ClipBatch b) {
+  const int blk = blockIdx.x;
+  const int mi = find_mat(b.prefix, b.n, blk);
+  const ClipDesc& d = b.d[mi];
+  const int h = blk - b.prefix[mi];
+  const float s = gld<float>(d.max_logit + h);
+  if (!(s > b.tau)) return;
+  const float f = __fsqrt_rn(__fdiv_rn(b.tau, s));
+  float* w = d.W + static_cast<int64_t>(h) * d.head_elems;
+  if (d.vec) {
+    const int64_t n4 = d.head_elems >> 2;
+    for (int64_t i = threadIdx.x; i < n4; i += 256) {
+      float4 v = gld<float4>(w + 4 * i);
+      v.x *= f; v.y *= f; v.z *= f; v.w *= f;
+      gst(w + 4 * i, v);
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < d.head_elems; i += 256) gst(w + i, gld<float>(w + i) * f);
+  }
+}
+
 // ---------------------------------------------------------------- copy probe
 // Streaming copy of n16 16-byte words, the yardstick of the bandwidth-bound
 // stages (one read and one write per byte, the momentum pass's mix).  Each
@@ -490,6 +518,12 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, int varian
     hipLaunchKernelGGL((copy_probe_kernel<4, true>), grid, dim3(256), 0, s, a, b, n16);
   else
     hipLaunchKernelGGL((copy_probe_kernel<4, false>), grid, dim3(256), 0, s, a, b, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_clip(const ClipBatch& b, hipStream_t s) {
+  if (b.n <= 0 || b.prefix[b.n] <= 0) return hipSuccess;
+  hipLaunchKernelGGL(qk_clip_kernel, dim3(b.prefix[b.n]), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -878,6 +878,58 @@ muon_status_t muon_profile_read(double* ms, int64_t* launches) {
   return st;
 }
 
+muon_status_t muon_qk_clip(const muon_qk_clip_matrix_t* mats, int64_t n, float tau, void* stream) {
+  g_last_error.clear();
+  if (!finite(tau) || !(tau > 0.f)) return fail(MUON_ERR_INVALID_ARG, "muon: tau must be finite and > 0");
+  if (n < 0) return fail(MUON_ERR_INVALID_ARG, "muon: n < 0");
+  if (n == 0) return MUON_OK;
+  if (!mats) return fail(MUON_ERR_INVALID_ARG, "muon: mats is NULL");
+  if (n > (1 << 20)) return fail(MUON_ERR_UNSUPPORTED, "muon: more than 2^20 matrices");
+  std::vector<Range> rs;
+  int64_t heads_total = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const muon_qk_clip_matrix_t& m = mats[i];
+    const std::string id = "muon: QK-Clip matrix " + std::to_string(i);
+    if (!m.W || !m.max_logit) return fail(MUON_ERR_INVALID_ARG, id + " has a NULL W or max_logit");
+    if (m.rows < 1 || m.cols < 1 || m.head_dim < 1)
+      return fail(MUON_ERR_INVALID_ARG, id + " has rows, cols or head_dim < 1");
+    if (m.rows > MUON_MAX_DIM || m.cols > MUON_MAX_DIM)
+      return fail(MUON_ERR_UNSUPPORTED, id + " exceeds MUON_MAX_DIM");
+    if (m.rows % m.head_dim != 0) return fail(MUON_ERR_INVALID_ARG, id + ": rows is not a multiple of head_dim");
+    if ((reinterpret_cast<uintptr_t>(m.W) & 15u) || (reinterpret_cast<uintptr_t>(m.max_logit) & 3u))
+      return fail(MUON_ERR_ALIGN, id + ": W is not 16-byte or max_logit not 4-byte aligned");
+    const int64_t heads = m.rows / m.head_dim;
+    heads_total += heads;
+    if (heads_total > (int64_t{1} << 31) - 1) return fail(MUON_ERR_UNSUPPORTED, "muon: too many heads");
+    const uintptr_t w = reinterpret_cast<uintptr_t>(m.W), l = reinterpret_cast<uintptr_t>(m.max_logit);
+    rs.push_back({w, w + 4 * static_cast<uintptr_t>(m.rows * m.cols), true, "W", i});
+    rs.push_back({l, l + 4 * static_cast<uintptr_t>(heads), false, "max_logit", i});
+  }
+  muon_status_t st = check_aliasing(rs);
+  if (st != MUON_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t i0 = 0; i0 < n; i0 += kClipBatch) {
+    ClipBatch b;
+    memset(&b, 0, sizeof(b));
+    b.n = static_cast<int32_t>(std::min<int64_t>(kClipBatch, n - i0));
+    b.tau = tau;
+    int32_t acc = 0;
+    for (int k = 0; k < b.n; ++k) {
+      const muon_qk_clip_matrix_t& m = mats[i0 + k];
+      b.d[k].W = m.W;
+      b.d[k].max_logit = m.max_logit;
+      b.d[k].head_elems = static_cast<int64_t>(m.head_dim) * m.cols;
+      b.d[k].vec = (b.d[k].head_elems % 4 == 0) ? 1 : 0;
+      b.prefix[k] = acc;
+      acc += static_cast<int32_t>(m.rows / m.head_dim);
+    }
+    b.prefix[b.n] = acc;
+    const hipError_t e = launch_qk_clip(b, s);
+    if (e != hipSuccess) return hip_fail(e, "QK-Clip launch");
+  }
+  return MUON_OK;
+}
+
 muon_status_t muon_copy_probe(const void* src, void* dst, size_t bytes, int32_t variant, void* stream) {
   g_last_error.clear();
   if (!src || !dst) return fail(MUON_ERR_INVALID_ARG, "muon: src or dst is NULL");

@@ -218,6 +218,25 @@ hipError_t launch_ns_gemm(int mode, int cfg, const MatDesc* d, const int32_t* pr
                           const XcdSplit& split, int buf, int first, hipStream_t s);
 hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* prefix, int nmats,
                             const XcdSplit& split, int buf, int first, hipStream_t s);
+// QK-Clip: one batch of matrices per launch, passed by value (kernel
+// arguments), so the call needs no workspace.  Matrix i's heads are
+// work-groups prefix[i] .. prefix[i+1]-1; head h of matrix i is the
+// contiguous range W + h * head_elems of head_elems floats.
+constexpr int kClipBatch = 48;
+struct ClipDesc {
+  float* W;
+  const float* max_logit;   // one entry per head
+  int64_t head_elems;       // head_dim * cols
+  int32_t vec;              // head_elems % 4 == 0 (16-byte accesses)
+  int32_t pad;
+};
+struct ClipBatch {
+  ClipDesc d[kClipBatch];
+  int32_t prefix[kClipBatch + 1];
+  int32_t n;
+  float tau;
+};
+hipError_t launch_qk_clip(const ClipBatch& b, hipStream_t s);
 // Streaming copy of n16 16-byte words (bandwidth yardstick); variant as
 // muon_copy_probe documents.
 hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, int variant, hipStream_t s);

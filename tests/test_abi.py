@@ -36,7 +36,7 @@ def test_stage_names_match_header():
 
 
 def test_abi_version_and_strings():
-    assert mm.muon_abi_version() == 5
+    assert mm.muon_abi_version() == 6
     assert mm.muon_status_string(0) == "MUON_OK"
     assert mm.muon_status_string(-4) == "MUON_ERR_ALIAS"
 
@@ -292,3 +292,39 @@ def test_static_workspace_size_matches_header():
     src = open(os.path.join(ROOT, "include", "muon.h")).read()
     m = re.search(r"#define MUON_STATIC_WORKSPACE_BYTES \((\d+)u \* 1024u \* 1024u\)", src)
     assert m and int(m.group(1)) * 2**20 == bd.MUON_STATIC_WORKSPACE_BYTES
+
+
+def _clip_arr(entries):
+    arr = (bd.muon_qk_clip_matrix_t * max(1, len(entries)))()
+    for k, (w, r, c, hd, s) in enumerate(entries):
+        arr[k] = bd.muon_qk_clip_matrix_t(w, r, c, hd, 0, s)
+    return arr
+
+
+@pytest.mark.parametrize("entry,tau,status", [
+    ((BASE, 64, 32, 16, BASE * 2), 0.0, "MUON_ERR_INVALID_ARG"),          # tau must be > 0
+    ((BASE, 64, 32, 16, BASE * 2), float("inf"), "MUON_ERR_INVALID_ARG"),
+    ((BASE, 64, 32, 16, BASE * 2), float("nan"), "MUON_ERR_INVALID_ARG"),
+    ((0, 64, 32, 16, BASE * 2), 1.0, "MUON_ERR_INVALID_ARG"),             # NULL W
+    ((BASE, 64, 32, 16, 0), 1.0, "MUON_ERR_INVALID_ARG"),                 # NULL max_logit
+    ((BASE, 64, 32, 0, BASE * 2), 1.0, "MUON_ERR_INVALID_ARG"),           # head_dim 0
+    ((BASE, 64, 32, 24, BASE * 2), 1.0, "MUON_ERR_INVALID_ARG"),          # rows % head_dim
+    ((BASE, 0, 32, 16, BASE * 2), 1.0, "MUON_ERR_INVALID_ARG"),
+    ((BASE + 4, 64, 32, 16, BASE * 2), 1.0, "MUON_ERR_ALIGN"),
+    ((BASE, 64, 32, 16, BASE * 2 + 2), 1.0, "MUON_ERR_ALIGN"),
+    ((BASE, 64, 70000, 16, BASE * 2), 1.0, "MUON_ERR_UNSUPPORTED"),
+    ((BASE, 64, 32, 16, BASE + 64), 1.0, "MUON_ERR_ALIAS"),               # max_logit inside W
+])
+def test_qk_clip_argument_errors(entry, tau, status):
+    L = mm.lib()
+    assert mm.muon_status_string(L.muon_qk_clip(_clip_arr([entry]), 1, tau, None)) == status
+
+
+def test_qk_clip_cross_matrix_alias_and_shared_logits():
+    L = mm.lib()
+    # two matrices whose W overlap: refused
+    arr = _clip_arr([(BASE, 64, 32, 16, BASE * 3), (BASE + 1024, 64, 32, 16, BASE * 3)])
+    assert L.muon_qk_clip(arr, 2, 1.0, None) == mm.MUON_ERR_ALIAS
+    # n == 0 is a no-op; a NULL list with n > 0 is refused
+    assert L.muon_qk_clip(None, 0, 1.0, None) == mm.MUON_OK
+    assert L.muon_qk_clip(None, 1, 1.0, None) == mm.MUON_ERR_INVALID_ARG
