@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 6
+#define MUON_ABI_VERSION 7
 
 typedef enum muon_status {
   MUON_OK = 0,
@@ -149,6 +149,32 @@ muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams
  * per device, with that device current. */
 #define MUON_STATIC_WORKSPACE_BYTES (64u * 1024u * 1024u)
 muon_status_t muon_step_static(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* stream);
+
+/* A recorded step, for training loops that run the same step many times on
+ * the same buffers (the case where launching ~20 kernels per step from the
+ * host costs more than the kernels themselves, e.g. a single 256 x 256
+ * matrix).  muon_plan_create validates the call exactly as muon_step does,
+ * binds its device buffers, uploads the descriptor table into the workspace
+ * (synchronously, on `stream`) and records the step's launch sequence into
+ * a HIP graph; each muon_plan_step replays it on `stream` as one graph
+ * launch.  A replay is one Muon step on the bound buffers: it reads G's
+ * current contents (the caller writes each step's gradient into the bound
+ * G buffers) and updates W and B in place, with the hyper-parameters given
+ * at creation (create a new plan to change mu, lr, eps, ns_steps, nesterov,
+ * weight decay or any scale).  Results are bit-identical to muon_step on
+ * the same inputs.  The caller keeps every bound buffer, the workspace
+ * included, alive and otherwise untouched until the plan is destroyed and
+ * its last replay has completed; replays of one plan, like calls sharing a
+ * workspace, must be ordered (one stream, or synchronised).  A plan belongs
+ * to the device current at creation; muon_plan_step on another device is
+ * MUON_ERR_INVALID_ARG.  n must be >= 1.  The graph holds no memset node
+ * (the per-step counter is zeroed by a kernel). */
+typedef struct muon_plan_s* muon_plan_t;
+muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* workspace,
+                               size_t workspace_bytes, void* stream, muon_plan_t* out);
+muon_status_t muon_plan_step(muon_plan_t plan, void* stream);
+/* Frees the plan's graph (NULL is a no-op); does not wait for replays. */
+muon_status_t muon_plan_destroy(muon_plan_t plan);
 
 /* Per-matrix diagnostics of one step: the layer-wise quantities that the
  * practice checklist of the synthesis note asks a Muon run to record

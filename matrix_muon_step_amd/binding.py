@@ -140,6 +140,13 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
                 L.muon_step_static.restype = ctypes.c_int
                 L.muon_step_static.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t), ctypes.c_void_p]
+                L.muon_plan_create.restype = ctypes.c_int
+                L.muon_plan_create.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t), ctypes.c_void_p,
+                                               ctypes.c_size_t, ctypes.c_void_p, P(ctypes.c_void_p)]
+                L.muon_plan_step.restype = ctypes.c_int
+                L.muon_plan_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+                L.muon_plan_destroy.restype = ctypes.c_int
+                L.muon_plan_destroy.argtypes = [ctypes.c_void_p]
                 L.muon_step_diag.restype = ctypes.c_int
                 L.muon_step_diag.argtypes = [P(muon_matrix_t), ctypes.c_int64, P(muon_hparams_t),
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -323,6 +330,61 @@ def muon_step_static(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps
     hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
     st = _torch_stream(stream)
     _check(lib().muon_step_static(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(st.cuda_stream)))
+
+
+class MuonPlan:
+    """A recorded Muon step on fixed buffers (muon_plan_create).  step()
+    replays it; the plan keeps its tensors alive until close()."""
+
+    def __init__(self, handle, keep):
+        self._h = handle
+        self._keep = keep
+
+    def step(self, stream=None) -> None:
+        if not self._h:
+            raise RuntimeError("the plan is closed")
+        st = _torch_stream(stream)
+        _check(lib().muon_plan_step(self._h, ctypes.c_void_p(st.cuda_stream)))
+
+    def close(self) -> None:
+        """Frees the graph; call it once the last replay has completed."""
+        if self._h:
+            h, self._h = self._h, None
+            _check(lib().muon_plan_destroy(h))
+            self._keep = None
+
+    def __del__(self):
+        try:
+            if self._h:
+                lib().muon_plan_destroy(self._h)
+        except Exception:  # interpreter shutdown
+            pass
+
+
+def muon_plan_create(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7, workspace=None,
+                     stream=None, weight_decay=0.0) -> MuonPlan:
+    """Records one Muon step on these (W, G, B[, scale]) tensors; returns a
+    MuonPlan whose step() replays it (write each step's gradient into the
+    same G tensors)."""
+    import torch
+
+    entries, gd = _tensor_entries(matrices)
+    if not entries:
+        raise ValueError("a plan needs at least one matrix")
+    arr = raw_matrix_array(entries)
+    hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
+    need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
+    if need == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+    st = _torch_stream(stream)
+    with torch.cuda.stream(st):
+        if workspace is None:
+            workspace = _alloc_workspace(need, matrices[0][0].device)
+        ws_ptr, ws_len = _ws_args(workspace)
+        h = ctypes.c_void_p()
+        _check(lib().muon_plan_create(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
+                                      ctypes.c_void_p(st.cuda_stream), ctypes.byref(h)))
+    return MuonPlan(h.value, (list(matrices), workspace))
 
 
 def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,

@@ -441,6 +441,10 @@ __global__ __launch_bounds__(256) void qk_clip_kernel(const ClipBatch b) {
   }
 }
 
+// One counter set to zero (the per-call count of matrices marked for the
+// prep pass, when a recorded plan replays a call without its table upload).
+__global__ void zero_counter_kernel(int32_t* p) { gst(p, 0); }
+
 // ---------------------------------------------------------------- copy probe
 // Streaming copy of n16 16-byte words, the yardstick of the bandwidth-bound
 // stages (one read and one write per byte, the momentum pass's mix).  Each
@@ -524,6 +528,11 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, int varian
 hipError_t launch_qk_clip(const ClipBatch& b, hipStream_t s) {
   if (b.n <= 0 || b.prefix[b.n] <= 0) return hipSuccess;
   hipLaunchKernelGGL(qk_clip_kernel, dim3(b.prefix[b.n]), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_counter(int32_t* p, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(1), 0, s, p);
   return hipGetLastError();
 }
 

@@ -911,7 +911,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
     // position (c + 4 (k & 3)) mod NC, which keeps the transposing fragment
     // reads free of bank conflicts (measured on gfx950).  Load instruction q
     // fills positions 64q..64q+63 in order, one 16-byte chunk per lane.
-    static_assert(C::BM == 256 && C::BN == 256, "transposed operands assume 256-wide tiles");
+    static_assert(C::BM == C::BN && (C::BM == 128 || C::BM == 256), "transposed operands: 128- or 256-wide tiles");
     constexpr int NC = C::BM / 8;
     constexpr int RP = 2 * C::BM;
 #pragma unroll
@@ -1074,6 +1074,9 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
 using G256 = G32<256, 256, 2, 4, 4>;
 using W160 = G32<160, 256, 1, 4, 3>;
 using W320 = G32<320, 256, 2, 4, 4>;
+// G128: G256's arithmetic (32x32x16 products, same k order and epilogues,
+// hence the same bits) on 128 x 128 tiles of 2 x 2 waves of 64 x 64.
+using G128 = G32<128, 128, 2, 2, 4>;
 
 template <class C, int MODE>
 hipError_t launch(const MatDesc* d, const int32_t* prefix, int nmats, const XcdSplit& sp, int buf, int first,
@@ -1094,6 +1097,14 @@ hipError_t launch_ns_gemm32(int mode, int cfg, const MatDesc* d, const int32_t* 
     if (mode == BXM) return launch<G256, BXM>(d, prefix, nmats, split, buf, first, s);
     if (mode == BXL) return launch<G256, BXL>(d, prefix, nmats, split, buf, first, s);
     if (mode == BXD) return launch<G256, BXD>(d, prefix, nmats, split, buf, first, s);
+    return hipErrorInvalidValue;
+  }
+  if (cfg == kCfgG128) {
+    if (mode == GRAM) return launch<G128, GRAM>(d, prefix, nmats, split, buf, first, s);
+    if (mode == POLY) return launch<G128, POLY>(d, prefix, nmats, split, buf, first, s);
+    if (mode == BXM) return launch<G128, BXM>(d, prefix, nmats, split, buf, first, s);
+    if (mode == BXL) return launch<G128, BXL>(d, prefix, nmats, split, buf, first, s);
+    if (mode == BXD) return launch<G128, BXD>(d, prefix, nmats, split, buf, first, s);
     return hipErrorInvalidValue;
   }
   if (cfg == kCfgW160 && mode == BXM) return launch<W160, BXM>(d, prefix, nmats, split, buf, first, s);

@@ -139,6 +139,10 @@ MatCfg choose_cfg(int64_t m, int64_t n) {
   return best;
 }
 
+// A call whose 256-tile BX launch would have fewer tiles than this (two per
+// CU of the 256-CU MI355X) runs its 256-tile matrices on 128-tiles.
+constexpr int64_t kSmallCallTiles = 512;
+
 // Gram-side tile rows per group of the BX tile order (wide-tile kernels):
 // all of them, so the tiles of one long-side column run together and share
 // their X^T panel in L2.
@@ -162,25 +166,46 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
   off += align_up(sizeof(int32_t) * (kNumTables * (n + 1) + 1));
   plan.table_bytes = off;
 
-  int64_t total_partials = 0;
-  int64_t total_slots = 0;
+  // Kernel configurations: by shape (choose_cfg), then, for a call whose
+  // 256-tile BX launch would give the GPU fewer than two tiles per CU, the
+  // same arithmetic on 128-tiles (G128 computes exactly what G256 does, so
+  // the bits do not depend on the choice).
+  std::vector<MatCfg> cfgs(n);
+  int64_t g256_bx_tiles = 0;
   for (int64_t i = 0; i < n; ++i) {
     const Item& it = items[i];
     if (it.rows < 1 || it.cols < 1)
       return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has rows or cols < 1");
     if (it.rows > MUON_MAX_DIM || it.cols > MUON_MAX_DIM)
       return fail(MUON_ERR_UNSUPPORTED, "muon: matrix " + std::to_string(i) + " exceeds MUON_MAX_DIM");
-    const bool tr = it.rows > it.cols;
-    const int64_t m = tr ? it.cols : it.rows;
-    const int64_t nn = tr ? it.rows : it.cols;
+    const int64_t m = std::min(it.rows, it.cols), nn = std::max(it.rows, it.cols);
     if (m > MUON_MAX_GRAM)
       return fail(MUON_ERR_UNSUPPORTED, "muon: matrix " + std::to_string(i) + " has min(rows, cols) > MUON_MAX_GRAM");
     if (!finite(it.lr_scale) || !finite(it.lr_wd))
       return fail(MUON_ERR_INVALID_ARG, "muon: matrix " + std::to_string(i) + " has a non-finite lr*scale or lr*weight_decay");
+    cfgs[i] = m <= kSmallGram ? MatCfg{-1, -1, kSmallGram, round_up(nn, kSmallChunk)} : choose_cfg(m, nn);
+    if (cfgs[i].bx == kCfgG256)
+      g256_bx_tiles += (cfgs[i].m_pad / kCfgRows[kCfgG256]) * (cfgs[i].n_pad / kCfgCols[kCfgG256]);
+  }
+  if (g256_bx_tiles > 0 && g256_bx_tiles < kSmallCallTiles) {
+    for (int64_t i = 0; i < n; ++i) {
+      if (cfgs[i].bx != kCfgG256) continue;
+      const int64_t m = std::min(items[i].rows, items[i].cols), nn = std::max(items[i].rows, items[i].cols);
+      cfgs[i] = MatCfg{kCfgG128, kCfgG128, round_up(m, kCfgRows[kCfgG128]), round_up(nn, kCfgCols[kCfgG128])};
+    }
+  }
+
+  int64_t total_partials = 0;
+  int64_t total_slots = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const Item& it = items[i];
+    const bool tr = it.rows > it.cols;
+    const int64_t m = tr ? it.cols : it.rows;
+    const int64_t nn = tr ? it.rows : it.cols;
     MatDesc& d = plan.descs[i];
     memset(&d, 0, sizeof(d));
     const bool small = m <= kSmallGram;
-    const MatCfg cfg = small ? MatCfg{-1, -1, kSmallGram, round_up(nn, kSmallChunk)} : choose_cfg(m, nn);
+    const MatCfg cfg = cfgs[i];
     d.rows = it.rows;
     d.cols = it.cols;
     d.m = static_cast<int32_t>(m);
@@ -462,11 +487,29 @@ muon_status_t hip_fail(hipError_t e, const char* where) {
 // workspace, then every stage is one grouped launch over all matrices.
 // With `diag_out` (a device muon_diag_t array) the W-writing kernels also
 // sum the diagnostics and a last launch reduces them.
-// `pageable`: copy the table straight from this call's host memory (the
-// copy has consumed it when hipMemcpyAsync returns) instead of through the
-// pinned staging ring, which allocates pinned memory on first use.
+// How execute() gets the descriptor table into the workspace.
+enum Upload {
+  kUploadPinned,    // through the pinned staging ring (allocated on first use)
+  kUploadPageable,  // straight from this call's host memory (the copy has
+                    // consumed it when hipMemcpyAsync returns); allocates nothing
+  kUploadNone,      // already resident (a recorded plan): only the call's
+                    // counter is zeroed, by a kernel; no profiling events
+};
+
+// The descriptor table of a bound plan (descriptors, then the prefix tables,
+// then the zeroed counter of matrices marked for the prep pass).
+std::vector<unsigned char> make_table(const Plan& plan) {
+  const int n = static_cast<int>(plan.descs.size());
+  std::vector<unsigned char> table(plan.table_bytes, 0);
+  memcpy(table.data(), plan.descs.data(), sizeof(MatDesc) * n);
+  int32_t* pre = reinterpret_cast<int32_t*>(table.data() + align_up(sizeof(MatDesc) * n));
+  for (int k = 0; k < kNumTables; ++k)
+    memcpy(pre + k * (n + 1), plan.pre[k].data(), sizeof(int32_t) * (n + 1));
+  return table;
+}
+
 muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStream_t s,
-                      void* diag_out = nullptr, bool pageable = false) {
+                      void* diag_out = nullptr, Upload upload = kUploadPinned) {
   const int n = static_cast<int>(plan.descs.size());
   const uintptr_t base = reinterpret_cast<uintptr_t>(workspace);
   bind_workspace(plan, base);
@@ -474,30 +517,33 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   if (diag)
     for (MatDesc& d : plan.descs) d.flags |= kDiag;
 
-  std::vector<unsigned char> table(plan.table_bytes, 0);
-  memcpy(table.data(), plan.descs.data(), sizeof(MatDesc) * n);
   const size_t pre_off = align_up(sizeof(MatDesc) * n);
-  int32_t* pre = reinterpret_cast<int32_t*>(table.data() + pre_off);
-  for (int k = 0; k < kNumTables; ++k)
-    memcpy(pre + k * (n + 1), plan.pre[k].data(), sizeof(int32_t) * (n + 1));
-
   const MatDesc* d_desc = reinterpret_cast<const MatDesc*>(base);
   const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pre_off);
   auto ptab = [&](int k) { return d_pre + k * (n + 1); };
   auto ttot = [&](int k) { return static_cast<int>(plan.tot[k]); };
+  int32_t* d_prep_count = const_cast<int32_t*>(d_pre) + kNumTables * (n + 1);
+  const bool recorded = upload == kUploadNone;
+  // A recorded plan's launches carry no profiling events.
+  auto stage = [&](int st, auto&& f) -> hipError_t { return recorded ? f() : run_stage(st, s, f); };
 
   hipError_t e;
-  e = run_stage(MUON_STAGE_UPLOAD, s, [&] {
-    return pageable ? hipMemcpyAsync(workspace, table.data(), table.size(), hipMemcpyHostToDevice, s)
-                    : upload_table(table.data(), table.size(), workspace, s);
-  });
+  if (recorded) {
+    e = launch_zero_counter(d_prep_count, s);
+  } else {
+    const std::vector<unsigned char> table = make_table(plan);
+    e = stage(MUON_STAGE_UPLOAD, [&] {
+      return upload == kUploadPageable
+                 ? hipMemcpyAsync(workspace, table.data(), table.size(), hipMemcpyHostToDevice, s)
+                 : upload_table(table.data(), table.size(), workspace, s);
+    });
+  }
   if (e != hipSuccess) return hip_fail(e, "descriptor upload");
-  e = run_stage(MUON_STAGE_MOMENTUM, s, [&] { return launch_momentum(d_desc, ptab(kTabMom), n, ttot(kTabMom), mu, s); });
+  e = stage(MUON_STAGE_MOMENTUM, [&] { return launch_momentum(d_desc, ptab(kTabMom), n, ttot(kTabMom), mu, s); });
   if (e != hipSuccess) return hip_fail(e, "momentum launch");
-  int32_t* d_prep_count = const_cast<int32_t*>(d_pre) + kNumTables * (n + 1);
-  e = run_stage(MUON_STAGE_NORM, s, [&] { return launch_norm(d_desc, n, eps, d_prep_count, s); });
+  e = stage(MUON_STAGE_NORM, [&] { return launch_norm(d_desc, n, eps, d_prep_count, s); });
   if (e != hipSuccess) return hip_fail(e, "norm launch");
-  e = run_stage(MUON_STAGE_PREP, s, [&] {
+  e = stage(MUON_STAGE_PREP, [&] {
     return launch_prep(d_desc, ptab(kTabPrep), n, ttot(kTabPrep), mu, d_prep_count, s);
   });
   if (e != hipSuccess) return hip_fail(e, "prep launch");
@@ -513,7 +559,7 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
         const bool wide = cfg_wide(c);
         // 3: BX with the update applied; 4: the same with diagnostics
         const int kmode = (wide && last && mode == 2) ? (diag ? 4 : 3) : mode;
-        e = run_stage(kmode >= 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], s, [&] {
+        e = stage(kmode >= 3 ? MUON_STAGE_BX_UPDATE : stage_of_mode[mode], [&] {
           return wide ? launch_ns_gemm32(kmode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s)
                       : launch_ns_gemm(mode, c, d_desc, ptab(tab), n, sp, buf, it == 0, s);
         });
@@ -521,15 +567,15 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
       }
     }
     if (plan.tot[kTabSmallGram] > 0) {
-      e = run_stage(MUON_STAGE_GRAM, s, [&] {
+      e = stage(MUON_STAGE_GRAM, [&] {
         return launch_small_gram(d_desc, ptab(kTabSmallGram), n, ttot(kTabSmallGram), buf, s);
       });
       if (e != hipSuccess) return hip_fail(e, "small gram launch");
-      e = run_stage(MUON_STAGE_POLY, s, [&] {
+      e = stage(MUON_STAGE_POLY, [&] {
         return launch_small_poly(d_desc, ptab(kTabSmallPoly), n, ttot(kTabSmallPoly), s);
       });
       if (e != hipSuccess) return hip_fail(e, "small poly launch");
-      e = run_stage(MUON_STAGE_BX, s, [&] {
+      e = stage(MUON_STAGE_BX, [&] {
         return launch_small_bx(d_desc, ptab(kTabSmallGram), n, ttot(kTabSmallGram), buf, s);
       });
       if (e != hipSuccess) return hip_fail(e, "small bx launch");
@@ -537,13 +583,13 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
     buf ^= 1;
   }
   if (plan.tot[kTabUpd] > 0) {
-    e = run_stage(MUON_STAGE_UPDATE, s, [&] {
+    e = stage(MUON_STAGE_UPDATE, [&] {
       return launch_update(d_desc, ptab(kTabUpd), n, ttot(kTabUpd), buf, diag, s);
     });
     if (e != hipSuccess) return hip_fail(e, "update launch");
   }
   if (diag) {
-    e = run_stage(MUON_STAGE_DIAG, s, [&] { return launch_diag(d_desc, n, diag_out, s); });
+    e = stage(MUON_STAGE_DIAG, [&] { return launch_diag(d_desc, n, diag_out, s); });
     if (e != hipSuccess) return hip_fail(e, "diagnostics launch");
   }
   return MUON_OK;
@@ -688,13 +734,123 @@ static muon_status_t step_impl(const muon_matrix_t* mats, int64_t n, const muon_
   st = check_aliasing(rs);
   if (st != MUON_OK) return st;
   fill_ptrs(plan, items);
-  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream), diag, use_static);
+  return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream), diag,
+                 use_static ? kUploadPageable : kUploadPinned);
 }
 
 muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp,
                         void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   return step_impl(mats, n, hp, nullptr, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+struct muon_plan_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int device = -1;
+};
+
+extern "C" {
+
+muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* workspace,
+                               size_t workspace_bytes, void* stream, muon_plan_t* out) {
+  g_last_error.clear();
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "muon: out is NULL");
+  *out = nullptr;
+  if (n < 1) return fail(MUON_ERR_INVALID_ARG, "muon: a plan needs at least one matrix");
+  std::vector<Item> items;
+  muon_status_t st = items_from_step(mats, n, hp, true, items);
+  if (st != MUON_OK) return st;
+  Plan plan;
+  st = make_plan(items, hp->ns_steps, plan);
+  if (st != MUON_OK) return st;
+  st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != MUON_OK) return st;
+  std::vector<Range> rs;
+  const size_t gsz = hp->g_dtype == MUON_BF16 ? 2 : 4;
+  for (int64_t i = 0; i < n; ++i) {
+    const uintptr_t e = static_cast<uintptr_t>(items[i].rows * items[i].cols);
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].W), reinterpret_cast<uintptr_t>(items[i].W) + 4 * e, true, "W", i});
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].B), reinterpret_cast<uintptr_t>(items[i].B) + 4 * e, true, "B", i});
+    rs.push_back({reinterpret_cast<uintptr_t>(items[i].G), reinterpret_cast<uintptr_t>(items[i].G) + gsz * e, false, "G", i});
+  }
+  rs.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + plan.total_bytes, true, "workspace", -1});
+  st = check_aliasing(rs);
+  if (st != MUON_OK) return st;
+  fill_ptrs(plan, items);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  // The table, with the descriptors bound to the workspace, stays resident.
+  {
+    Plan bound = plan;
+    bind_workspace(bound, reinterpret_cast<uintptr_t>(workspace));
+    const std::vector<unsigned char> table = make_table(bound);
+    e = hipMemcpyAsync(workspace, table.data(), table.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "descriptor upload");
+  }
+  // Record the launch sequence on a private stream.
+  hipStream_t cs = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    hipStreamDestroy(cs);
+    return hip_fail(e, "hipStreamBeginCapture");
+  }
+  const std::string before = g_last_error;
+  st = execute(plan, workspace, hp->mu, hp->eps, cs, nullptr, kUploadNone);
+  const std::string launch_error = g_last_error;
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);
+  hipStreamDestroy(cs);
+  if (st != MUON_OK) {
+    if (graph) hipGraphDestroy(graph);
+    return fail(st, launch_error);
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(graph);
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  muon_plan_s* p = new muon_plan_s;
+  p->graph = graph;
+  p->exec = exec;
+  p->device = dev;
+  *out = p;
+  g_last_error = before;
+  return MUON_OK;
+}
+
+muon_status_t muon_plan_step(muon_plan_t plan, void* stream) {
+  g_last_error.clear();
+  if (!plan) return fail(MUON_ERR_INVALID_ARG, "muon: plan is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(MUON_ERR_INVALID_ARG, "muon: the plan was recorded on device " + std::to_string(plan->device) +
+                                          ", the current device is " + std::to_string(dev));
+  e = hipGraphLaunch(plan->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return MUON_OK;
+}
+
+muon_status_t muon_plan_destroy(muon_plan_t plan) {
+  g_last_error.clear();
+  if (!plan) return MUON_OK;
+  hipError_t e1 = hipGraphExecDestroy(plan->exec);
+  hipError_t e2 = hipGraphDestroy(plan->graph);
+  delete plan;
+  if (e1 != hipSuccess) return hip_fail(e1, "hipGraphExecDestroy");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipGraphDestroy");
+  return MUON_OK;
 }
 
 muon_status_t muon_step_static(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* stream) {

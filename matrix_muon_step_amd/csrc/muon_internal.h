@@ -72,12 +72,16 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) ^ (r >>
 //   T128: 128 x 128, 16x16x32   (Gram, polynomial, BX)
 // Every iterate / Gram buffer is zero padded to multiples of its matrix's
 // tile edges, so the GEMM kernels never bounds-check.
-enum GemmCfg : int32_t { kCfgG256 = 0, kCfgW160 = 1, kCfgT160 = 2, kCfgT128 = 3, kCfgW320 = 4, kNumCfg = 5 };
-constexpr int kCfgRows[kNumCfg] = {256, 160, 160, 128, 320};   // tile rows (Gram side)
-constexpr int kCfgCols[kNumCfg] = {256, 256, 160, 128, 256};   // tile columns (long side for BX)
-constexpr int kCfgWaves[kNumCfg] = {8, 4, 4, 4, 8};            // waves per work-group
+//   G128: 128 x 128, 32x32x16   (Gram, polynomial, BX; the G256 arithmetic
+//         on smaller tiles, for calls too small to fill the GPU with G256)
+enum GemmCfg : int32_t {
+  kCfgG256 = 0, kCfgW160 = 1, kCfgT160 = 2, kCfgT128 = 3, kCfgW320 = 4, kCfgG128 = 5, kNumCfg = 6
+};
+constexpr int kCfgRows[kNumCfg] = {256, 160, 160, 128, 320, 128};   // tile rows (Gram side)
+constexpr int kCfgCols[kNumCfg] = {256, 256, 160, 128, 256, 128};   // tile columns (long side for BX)
+constexpr int kCfgWaves[kNumCfg] = {8, 4, 4, 4, 8, 4};              // waves per work-group
 // Configurations served by the 32x32x16 wide-tile kernels.
-constexpr bool cfg_wide(int c) { return c == kCfgG256 || c == kCfgW160 || c == kCfgW320; }
+constexpr bool cfg_wide(int c) { return c == kCfgG256 || c == kCfgW160 || c == kCfgW320 || c == kCfgG128; }
 // Tile edge of the layout kernels (normalise/transpose, update).
 constexpr int kEwTile = 64;
 // Matrices whose Gram side m is at most this take the float32 path: with so
@@ -200,6 +204,9 @@ hipError_t launch_momentum(const MatDesc* d, const int32_t* prefix, int nmats, i
                            float mu, hipStream_t s);
 // prep_count: one int the norm pass increments per matrix it marks for the
 // prep pass (zero at the start of the call).
+// Sets one int of device memory to zero (a kernel, not a memset, so that it
+// can sit in a recorded graph).
+hipError_t launch_zero_counter(int32_t* p, hipStream_t s);
 hipError_t launch_norm(const MatDesc* d, int nmats, float eps, int32_t* prep_count, hipStream_t s);
 hipError_t launch_prep(const MatDesc* d, const int32_t* prefix, int nmats, int total, float mu,
                        const int32_t* prep_count, hipStream_t s);

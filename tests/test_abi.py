@@ -36,7 +36,7 @@ def test_stage_names_match_header():
 
 
 def test_abi_version_and_strings():
-    assert mm.muon_abi_version() == 6
+    assert mm.muon_abi_version() == 7
     assert mm.muon_status_string(0) == "MUON_OK"
     assert mm.muon_status_string(-4) == "MUON_ERR_ALIAS"
 
@@ -172,9 +172,29 @@ def test_plan_transpose_rule_and_padding():
             assert tr in (128, 160, 256, 320)
             assert m["m_pad"] % t == 0 and m["m_pad"] % tr == 0 and m["m"] <= m["m_pad"] < m["m"] + max(t, tr)
             assert m["n_pad"] % tc == 0 and m["n"] <= m["n_pad"] < m["n"] + tc
-    # Tile choice: exact fits are preferred (1600 = 10 x 160 = 5 x 320, 2048 = 8 x 256).
-    assert [m["tile"] for m in mats] == [160, 160, 160, 0, 0, 0, 256, 256, 128]
-    assert [m["bx_tile_rows"] for m in mats] == [320, 320, 320, 0, 0, 0, 256, 256, 128]
+    # Tile choice: exact fits are preferred (1600 = 10 x 160 = 5 x 320); the
+    # 256-tile matrices of this call (2048 x 7168, 768 x 3072: 260 BX tiles)
+    # run on 128-tiles, as every call with fewer than 512 such tiles does.
+    assert [m["tile"] for m in mats] == [160, 160, 160, 0, 0, 0, 128, 128, 128]
+    assert [m["bx_tile_rows"] for m in mats] == [320, 320, 320, 0, 0, 0, 128, 128, 128]
+
+
+def test_plan_small_call_uses_128_tiles():
+    """A call whose 256-tile BX launch would hold fewer than 512 tiles runs
+    those matrices on 128-tiles (same arithmetic); from 512 tiles on, 256."""
+    one = [(2048, 7168)]                      # 8 x 28 = 224 BX tiles of 256
+    _, mats = mm.muon_plan_query(one)
+    assert mats[0]["tile"] == 128 and mats[0]["bx_tile_rows"] == 128 and mats[0]["m_pad"] == 2048
+    _, mats = mm.muon_plan_query(one * 3)     # 672 tiles
+    assert all(m["tile"] == 256 and m["bx_tile_rows"] == 256 for m in mats)
+    # exactly at the threshold: 2 x (8 x 28) + 64 x ... -> 512 tiles keep 256
+    _, mats = mm.muon_plan_query(one * 2 + [(256, 256)] * 64)   # 448 + 64 = 512
+    assert all(m["tile"] == 256 for m in mats)
+    _, mats = mm.muon_plan_query(one * 2 + [(256, 256)] * 63)   # 511
+    assert all(m["tile"] == 128 for m in mats)
+    # the 1600-class (160/320 tiles) and float32-path matrices are unaffected
+    _, mats = mm.muon_plan_query([(1600, 1600), (40, 90)] + one)
+    assert [m["tile"] for m in mats] == [160, 0, 128]
 
 
 def test_plan_small_path_threshold():
@@ -204,8 +224,12 @@ def test_plan_tile_counts_and_workspace():
 
 
 def test_plan_mixed_tiles_launch_groups():
+    # 1600: 160-tile symmetric products and 320-row BX tiles; 2048 (a small
+    # call: 64 BX tiles of 256) on the 32x32 128-tiles; 100 x 300 on the
+    # 16x16 128-tiles: three configurations per stage.
     info, mats = mm.muon_plan_query([(1600, 1600), (2048, 2048), (100, 300)], ns_steps=5)
-    assert sorted(m["tile"] for m in mats) == [128, 160, 256]
+    assert [m["tile"] for m in mats] == [160, 128, 128]
+    assert [m["fused_update"] for m in mats] == [1, 1, 0]
     assert info["launches"] == 3 + _update_launch(mats) + 3 * 3 * 5
 
 
@@ -215,15 +239,14 @@ def _update_launch(mats):
 
 
 def test_plan_fused_update_flags():
-    """The wide-tile BX kernels (256 long-side columns) apply the update in
-    their last launch; the float32 path, the narrow tiles and ns_steps = 0
-    keep the separate update pass."""
+    """The wide-tile BX kernels (32x32x16 products: 256-, 128-, 320x256- and
+    160x256-tiles) apply the update in their last launch; the float32 path,
+    the 16x16 tiles and ns_steps = 0 keep the separate update pass."""
     shapes = [(2048, 7168), (7168, 2048), (1600, 1600), (100, 300), (33, 17)]
     info, mats = mm.muon_plan_query(shapes, ns_steps=5)
-    for m in mats:
-        assert m["fused_update"] == int(m["bx_tile_cols"] == 256 and m["fp32_path"] == 0)
-    assert [m["fused_update"] for m in mats][:2] == [1, 1]
-    assert [m["fused_update"] for m in mats][3:] == [0, 0]
+    assert [m["fused_update"] for m in mats] == [1, 1, 1, 0, 0]
+    big, _ = mm.muon_plan_query(shapes[:2] * 2, ns_steps=5)   # 896 BX tiles: 256-tiles
+    assert big["tile"] == 256
     info_w, _ = mm.muon_plan_query(shapes[:2], ns_steps=5)
     assert info_w["launches"] == 3 + 3 * 5
     _, mats0 = mm.muon_plan_query(shapes, ns_steps=0)
@@ -328,3 +351,26 @@ def test_qk_clip_cross_matrix_alias_and_shared_logits():
     # n == 0 is a no-op; a NULL list with n > 0 is refused
     assert L.muon_qk_clip(None, 0, 1.0, None) == mm.MUON_OK
     assert L.muon_qk_clip(None, 1, 1.0, None) == mm.MUON_ERR_INVALID_ARG
+
+
+def test_plan_create_rejects_before_any_gpu_call():
+    """muon_plan_create validates like muon_step (no GPU in this container:
+    every error below comes back before the first HIP call)."""
+    L = mm.lib()
+    hp = bd.hparams()
+    h = ctypes.c_void_p()
+    arr = bd.raw_matrix_array([good(0)])
+    assert L.muon_plan_create(arr, 1, ctypes.byref(hp), ctypes.c_void_p(BASE * 64), 1 << 40, None, None) \
+        == mm.MUON_ERR_INVALID_ARG                                       # out is NULL
+    assert L.muon_plan_create(arr, 0, ctypes.byref(hp), ctypes.c_void_p(BASE * 64), 1 << 40, None,
+                              ctypes.byref(h)) == mm.MUON_ERR_INVALID_ARG  # no matrix
+    assert L.muon_plan_create(arr, 1, ctypes.byref(hp), ctypes.c_void_p(BASE * 64), 16, None,
+                              ctypes.byref(h)) == mm.MUON_ERR_WORKSPACE
+    assert L.muon_plan_create(arr, 1, ctypes.byref(hp), ctypes.c_void_p(BASE * 64 + 8), 1 << 40, None,
+                              ctypes.byref(h)) == mm.MUON_ERR_WORKSPACE
+    bad = bd.raw_matrix_array([good(0), (BASE * 1 + 64, BASE * 6, BASE * 7, 64, 96, 1.0)])
+    assert L.muon_plan_create(bad, 2, ctypes.byref(hp), ctypes.c_void_p(BASE * 64), 1 << 40, None,
+                              ctypes.byref(h)) == mm.MUON_ERR_ALIAS
+    assert h.value is None
+    assert L.muon_plan_destroy(None) == mm.MUON_OK
+    assert L.muon_plan_step(None, None) == mm.MUON_ERR_INVALID_ARG

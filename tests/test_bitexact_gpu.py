@@ -154,9 +154,15 @@ def test_partial_permutation_maximum_sizes(mm, shape):
 
 
 def test_grouped_equals_one_by_one(mm):
+    """All 72 matrices of the GPT-2-small set in one call (256-tile
+    launches) against one call per matrix (each a small call, run on the
+    128-tiles, which compute the same arithmetic): identical bits."""
     print("[case] grouped == single", flush=True)
     w = synth.WORKLOADS["gpt2_small"]
-    idx = [0, 1, 4, 5, 6, 10, 11]
+    idx = list(range(len(w.matrices)))
+    _, grouped_plan = mm.muon_plan_query([(w.matrices[i].rows, w.matrices[i].cols) for i in idx])
+    _, single_plan = mm.muon_plan_query([(w.matrices[0].rows, w.matrices[0].cols)])
+    assert grouped_plan[0]["tile"] == 256 and single_plan[0]["tile"] == 128
     host = [synth.numpy_matrix(w, i, 0) for i in idx]
     grouped = [(dev(h["W0"]), dev(h["G"]), dev(h["B0"]), 1.0) for h in host]
     single = [(dev(h["W0"]), dev(h["G"]), dev(h["B0"]), 1.0) for h in host]
