@@ -496,9 +496,11 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
         nh[q] = pack_bf16(v[2 * q], v[2 * q + 1]);
         nl[q] = pack_bf16(v[2 * q] - bf_lo(nh[q]), v[2 * q + 1] - bf_hi(nh[q]));
       }
+      // The new pair is read again only by the next iteration's Gram
+      // product, after the whole launch: stream it past the caches.
       const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-      gst(pick(d.xt_hi, buf ^ 1) + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
-      gst(pick(d.xt_lo, buf ^ 1) + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
+      gst_stream(pick(d.xt_hi, buf ^ 1) + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
+      gst_stream(pick(d.xt_lo, buf ^ 1) + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
     } else if (tr) {
       // O^T = X'^T has W's orientation: W[gj][gi .. gi+7].
       if (gj < d.n) {

@@ -22,6 +22,13 @@ __device__ __forceinline__ void gst(void* p, T v) {
   __builtin_memcpy((__attribute__((address_space(1))) void*)p, &v, sizeof(T));
 }
 
+// A 16-byte store that streams past the caches (nontemporal): for results
+// the next kernel reads only after gigabytes of other traffic.
+typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void gst_stream(void* p, uint4 v) {
+  __builtin_nontemporal_store((u32x4_nt_t){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt_t*>(p));
+}
+
 // bf16 halves of a 32-bit word as float32 (low half = element 0).
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
