@@ -113,7 +113,8 @@ int64_t upper_tiles(int64_t mp, int t) {
 // relative sustained rate on gfx950, from measurements of these kernels:
 // 32x32 256-tiles 1.10, 320x256 BX tiles 1.04, 160x256 BX tiles 1.00,
 // 16x16 160-tiles 0.85, 128-tiles 0.70.  The choice depends on the shape
-// alone, so a matrix takes the same kernels (and gives the same bits)
+// alone; the one per-call change made afterwards (256-tiles to 128-tiles in
+// a small call) keeps the arithmetic, so a matrix gives the same bits
 // whatever else a call holds.
 MatCfg choose_cfg(int64_t m, int64_t n) {
   struct Cand { int sym, bx; };
