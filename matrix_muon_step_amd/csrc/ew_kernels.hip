@@ -53,24 +53,57 @@ __device__ __forceinline__ void write_pair_tile(const MatDesc& d, const float (&
 }
 
 // ---------------------------------------------------------------- momentum
-// One 64x64 tile of X (the short-side-major view of M, padded) per
-// work-group: B <- mu * B + G and M = B (or G + mu * B) for the tile's
-// elements of M, their sum of squares (partials[tile]) and, with
-// diagnostics, whether one is NaN or infinite (mom_bad[tile]).  For a
-// matrix whose normalisation is folded into the first iteration (kFold),
-// the tile also writes the bf16 pair of the unnormalised M as X^T.
-// Orthogonalise-only mode: M is read from G and nothing else is written.
+// X^T pair of the unnormalised M from one momentum tile held in LDS
+// (tile[r][c] = M at row r0 + r, column c0 + c of its own orientation;
+// kMomRows x kMomCols).  A row of X^T (long-side index j) takes the tile's
+// mom_tile_i values of the short side: 128 bytes of each array when M is
+// not transposed (rows j are M's columns), 256 bytes when it is.  Padding
+// (i < m_pad, j < n_pad past M's extent) is written as zeros.
+__device__ __forceinline__ void write_pair_mtile(const MatDesc& d, const float (&tile)[kMomRows][kMomCols + 1],
+                                                 int i0, int j0, bool tr) {
+  // Lanes of a wave: 16 (not transposed) or 32 (transposed) groups of four
+  // consecutive i, the rest of the wave on consecutive j; LDS reads of a wave
+  // fall on distinct banks (not transposed) or two-way (transposed).
+  const int lg = tr ? 5 : 4;
+  const int tx = threadIdx.x & ((1 << lg) - 1);
+  const int ty = threadIdx.x >> lg;
+  const int jstep = 256 >> lg;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int jl = ty + jstep * k;
+    if (j0 + jl >= d.n_pad || i0 + tx * 4 >= d.m_pad) continue;
+    float x[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) x[c4] = tr ? tile[jl][tx * 4 + c4] : tile[tx * 4 + c4][jl];
+    const uint32_t h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+    const uint2 hv = make_uint2(h0, h1);
+    const uint2 lv = make_uint2(pack_bf16(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
+                                pack_bf16(x[2] - bf_lo(h1), x[3] - bf_hi(h1)));
+    const int64_t off = static_cast<int64_t>(j0 + jl) * d.m_pad + i0 + tx * 4;
+    gst(d.xt_hi[0] + off, hv);
+    gst(d.xt_lo[0] + off, lv);
+  }
+}
+
+// One tile of kMomRows x kMomCols elements of M (its own orientation;
+// mom_tile_i x mom_tile_j of the padded short-side-major X) per work-group:
+// B <- mu * B + G and M = B (or G + mu * B) for the tile's elements of M,
+// their sum of squares (partials[tile]) and, with diagnostics, whether one
+// is NaN or infinite (mom_bad[tile]).  For a matrix whose normalisation is
+// folded into the first iteration (kFold), the tile also writes the bf16
+// pair of the unnormalised M as X^T.  Orthogonalise-only mode: M is read
+// from G and nothing else is written.
 __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict__ descs,
                                                        const int32_t* __restrict__ prefix, int nmats, float mu) {
   const int blk = blockIdx.x;
   const int mi = find_mat(prefix, nmats, blk);
   const MatDesc d = descs[mi];
   const int local = blk - prefix[mi];
-  const int tpr = (d.n_pad + kEwTile - 1) / kEwTile;
-  const int i0 = (local / tpr) * kEwTile;  // X rows (short side)
-  const int j0 = (local % tpr) * kEwTile;  // X cols (long side)
   const int flags = d.flags;
   const bool tr = flags & kTransposed;
+  const int tpr = (d.n_pad + mom_tile_j(tr) - 1) / mom_tile_j(tr);
+  const int i0 = (local / tpr) * mom_tile_i(tr);  // X rows (short side)
+  const int j0 = (local % tpr) * mom_tile_j(tr);  // X cols (long side)
   const bool ortho = flags & kOrthoOnly;
   const bool gbf = flags & kGBf16;
   const bool nest = flags & kNesterov;
@@ -79,14 +112,14 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
   const int64_t r0 = tr ? j0 : i0;  // region of M (its own orientation)
   const int64_t c0 = tr ? i0 : j0;
   const bool vec = (cols & 3) == 0;  // rows of M start 16-byte aligned
-  __shared__ float tile[kEwTile][kEwTile + 1];
-  const int tx = threadIdx.x & 15;   // column group of 4
-  const int ty = threadIdx.x >> 4;   // 0..15
+  __shared__ float tile[kMomRows][kMomCols + 1];
+  const int tx = threadIdx.x & 31;   // column group of 4 (32 per 512-byte row segment)
+  const int ty = threadIdx.x >> 5;   // 0..7
   float acc = 0.f;
   uint32_t bad = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int rl = ty + 16 * k;
+  for (int k = 0; k < kMomRows / 8; ++k) {
+    const int rl = ty + 8 * k;
     const int64_t r = r0 + rl;
     const int64_t c = c0 + tx * 4;
     float mv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -151,7 +184,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
     __syncthreads();
   }
   if (threadIdx.x == 0) gst(d.partials + local, ((red[0] + red[1]) + red[2]) + red[3]);
-  if (fold) write_pair_tile(d, tile, i0, j0, 1.f, tr);
+  if (fold) write_pair_mtile(d, tile, i0, j0, tr);
 }
 
 // ---------------------------------------------------------------- norm

@@ -229,7 +229,8 @@ muon_status_t make_plan(const std::vector<Item>& items, int ns_steps, Plan& plan
     d.s_chunks = small ? d.n_pad / kSmallChunk : 0;
     int64_t work[kNumTables] = {};
     work[kTabPrep] = ((d.m_pad + kEwTile - 1) / kEwTile) * ((d.n_pad + kEwTile - 1) / kEwTile);
-    work[kTabMom] = work[kTabPrep];  // one momentum work-group per 64x64 tile of padded X
+    work[kTabMom] = ((d.m_pad + mom_tile_i(tr) - 1) / mom_tile_i(tr)) *
+                    ((d.n_pad + mom_tile_j(tr) - 1) / mom_tile_j(tr));
     d.mom_blocks = static_cast<int32_t>(work[kTabMom]);
     total_partials += d.mom_blocks;
     work[kTabUpd] = fused ? 0 : ((it.rows + kEwTile - 1) / kEwTile) * ((it.cols + kEwTile - 1) / kEwTile);
