@@ -279,6 +279,25 @@ def test_bf16_gradients_small(mm):
     check_step_results(*run_workload(mm, w), w.lr)
 
 
+# The momentum pass works on tiles of 64 rows x 128 columns of M in M's own
+# orientation (the transposed case covers 128 Gram-side by 64 long-side
+# elements of X).  Shapes that end inside a tile in both directions, in both
+# orientations, with rows whose length is not a multiple of 4, plus the
+# float32 small-Gram path (m <= 64), for float32 and bf16 gradients, two
+# steps (the second starts from a non-zero momentum buffer).
+RAGGED_MOMENTUM = (synth.MatrixSpec(127, 129, "a"), synth.MatrixSpec(129, 127, "b"),
+                   synth.MatrixSpec(65, 255, "c"), synth.MatrixSpec(255, 65, "d"),
+                   synth.MatrixSpec(191, 1001, "e"), synth.MatrixSpec(1001, 191, "f"),
+                   synth.MatrixSpec(63, 4097, "g"), synth.MatrixSpec(4097, 63, "h"))
+
+
+@pytest.mark.parametrize("g_dtype", ["f32", "bf16"])
+def test_momentum_tiles_ragged(mm, g_dtype):
+    log_case(f"ragged momentum tiles, {g_dtype} gradients")
+    w = synth.Workload(41, "ragged_momentum", RAGGED_MOMENTUM, 8, 0.1, g_dtype, 2)
+    check_step_results(*run_workload(mm, w), w.lr)
+
+
 @pytest.mark.parametrize("scale", [1e-18, 1e-12, 1.0, 1e10, 1e16])
 @pytest.mark.parametrize("shape", [(300, 520), (520, 300)])
 def test_gradient_scale_folded_and_normalised_paths(mm, shape, scale):
