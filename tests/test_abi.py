@@ -223,6 +223,24 @@ def test_plan_tile_counts_and_workspace():
     assert info0["launches"] == 4
 
 
+def test_plan_momentum_tiles_follow_orientation():
+    """The momentum pass takes tiles of 64 rows x 128 columns of M in M's own
+    orientation: 64 x 128 of the padded short-side-major X when M is stored
+    as is, 128 x 64 when it is transposed (rows > cols)."""
+    def cdiv(a, b):
+        return -(-a // b)
+    shapes = [(1600, 6400), (6400, 1600), (1600, 1600), (65, 300), (300, 65), (63, 4097), (4097, 63)]
+    total = 0
+    for s in shapes:
+        info, (m,) = mm.muon_plan_query([s])
+        tr = s[0] > s[1]
+        ti, tj = (128, 64) if tr else (64, 128)
+        expect = cdiv(m["m_pad"], ti) * cdiv(m["n_pad"], tj)
+        assert info["ew_blocks"] == expect, (s, info["ew_blocks"], expect)
+        total += expect
+    assert mm.muon_plan_query(shapes)[0]["ew_blocks"] == total
+
+
 def test_plan_mixed_tiles_launch_groups():
     # 1600: 160-tile symmetric products and 320-row BX tiles; 2048 (a small
     # call: 64 BX tiles of 256) on the 32x32 128-tiles; 100 x 300 on the
