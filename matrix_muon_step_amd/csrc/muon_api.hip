@@ -660,6 +660,29 @@ void fill_ptrs(Plan& plan, const std::vector<Item>& items) {
   }
 }
 
+// Memory ranges of a step call (each matrix's W, B and G, the workspace the
+// plan uses and the optional diagnostics array) checked for overlaps that
+// the step forbids (see check_aliasing).
+muon_status_t check_step_aliasing(const std::vector<Item>& items, const muon_hparams_t* hp, const void* workspace,
+                                  size_t workspace_used, const muon_diag_t* diag) {
+  std::vector<Range> rs;
+  const size_t gsz = hp->g_dtype == MUON_BF16 ? 2 : 4;
+  const int64_t n = static_cast<int64_t>(items.size());
+  for (int64_t i = 0; i < n; ++i) {
+    const uintptr_t e = static_cast<uintptr_t>(items[i].rows * items[i].cols);
+    const uintptr_t w = reinterpret_cast<uintptr_t>(items[i].W), b = reinterpret_cast<uintptr_t>(items[i].B),
+                    g = reinterpret_cast<uintptr_t>(items[i].G);
+    rs.push_back({w, w + 4 * e, true, "W", i});
+    rs.push_back({b, b + 4 * e, true, "B", i});
+    rs.push_back({g, g + gsz * e, false, "G", i});
+  }
+  const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
+  rs.push_back({ws, ws + workspace_used, true, "workspace", -1});
+  if (diag)
+    rs.push_back({reinterpret_cast<uintptr_t>(diag), reinterpret_cast<uintptr_t>(diag + n), true, "diag", -1});
+  return check_aliasing(rs);
+}
+
 // ---------------------------------------------------------------- static workspace
 // Device address of `scratch` per device (looked up once per device).
 std::mutex g_scratch_mu;
@@ -722,18 +745,7 @@ static muon_status_t step_impl(const muon_matrix_t* mats, int64_t n, const muon_
   }
   st = check_workspace(plan, workspace, workspace_bytes);
   if (st != MUON_OK) return st;
-  std::vector<Range> rs;
-  const size_t gsz = hp->g_dtype == MUON_BF16 ? 2 : 4;
-  for (int64_t i = 0; i < n; ++i) {
-    const uintptr_t e = static_cast<uintptr_t>(items[i].rows * items[i].cols);
-    rs.push_back({reinterpret_cast<uintptr_t>(items[i].W), reinterpret_cast<uintptr_t>(items[i].W) + 4 * e, true, "W", i});
-    rs.push_back({reinterpret_cast<uintptr_t>(items[i].B), reinterpret_cast<uintptr_t>(items[i].B) + 4 * e, true, "B", i});
-    rs.push_back({reinterpret_cast<uintptr_t>(items[i].G), reinterpret_cast<uintptr_t>(items[i].G) + gsz * e, false, "G", i});
-  }
-  rs.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + plan.total_bytes, true, "workspace", -1});
-  if (diag)
-    rs.push_back({reinterpret_cast<uintptr_t>(diag), reinterpret_cast<uintptr_t>(diag + n), true, "diag", -1});
-  st = check_aliasing(rs);
+  st = check_step_aliasing(items, hp, workspace, plan.total_bytes, diag);
   if (st != MUON_OK) return st;
   fill_ptrs(plan, items);
   return execute(plan, workspace, hp->mu, hp->eps, static_cast<hipStream_t>(stream), diag,
@@ -770,16 +782,7 @@ muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t n, const muon_
   if (st != MUON_OK) return st;
   st = check_workspace(plan, workspace, workspace_bytes);
   if (st != MUON_OK) return st;
-  std::vector<Range> rs;
-  const size_t gsz = hp->g_dtype == MUON_BF16 ? 2 : 4;
-  for (int64_t i = 0; i < n; ++i) {
-    const uintptr_t e = static_cast<uintptr_t>(items[i].rows * items[i].cols);
-    rs.push_back({reinterpret_cast<uintptr_t>(items[i].W), reinterpret_cast<uintptr_t>(items[i].W) + 4 * e, true, "W", i});
-    rs.push_back({reinterpret_cast<uintptr_t>(items[i].B), reinterpret_cast<uintptr_t>(items[i].B) + 4 * e, true, "B", i});
-    rs.push_back({reinterpret_cast<uintptr_t>(items[i].G), reinterpret_cast<uintptr_t>(items[i].G) + gsz * e, false, "G", i});
-  }
-  rs.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + plan.total_bytes, true, "workspace", -1});
-  st = check_aliasing(rs);
+  st = check_step_aliasing(items, hp, workspace, plan.total_bytes, nullptr);
   if (st != MUON_OK) return st;
   fill_ptrs(plan, items);
   const hipStream_t s = static_cast<hipStream_t>(stream);
