@@ -8,6 +8,7 @@ the first call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -219,12 +220,14 @@ def _tensor_entries(matrices):
 
     entries = []
     g_dtype = None
+    device = None
     for k, mt in enumerate(matrices):
         W, G, B = mt[0], mt[1], mt[2]
         scale = float(mt[3]) if len(mt) > 3 else 1.0
         for name, t in (("W", W), ("G", G), ("B", B)):
             if not t.is_cuda:
                 raise ValueError(f"matrix {k}: {name} must be a GPU tensor")
+            device = _same_device(device, t, f"matrix {k}: {name}")
             if t.dim() != 2 or not t.is_contiguous():
                 raise ValueError(f"matrix {k}: {name} must be a contiguous 2-D tensor")
         if W.dtype != torch.float32 or B.dtype != torch.float32:
@@ -242,19 +245,47 @@ def _tensor_entries(matrices):
         if W.shape != G.shape or W.shape != B.shape:
             raise ValueError(f"matrix {k}: W, G and B shapes differ")
         entries.append((W.data_ptr(), G.data_ptr(), B.data_ptr(), W.shape[0], W.shape[1], scale))
-    return entries, (MUON_F32 if g_dtype is None else g_dtype)
+    return entries, (MUON_F32 if g_dtype is None else g_dtype), device
 
 
-def _torch_stream(stream):
-    """The torch stream object the call runs on: the current stream for
-    None, a torch stream as given, or an external HIP stream handle (int)."""
+def _same_device(device, t, what):
+    """The device of a call: every tensor of it on one GPU (the library
+    launches on the current device, which the call sets to that one)."""
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, other tensors of the call on {device}")
+    return t.device
+
+
+def _torch_stream(stream, device=None):
+    """The torch stream object the call runs on: the current stream of
+    `device` (default: the current device) for None, a torch stream as given
+    (it must belong to `device`), or an external HIP stream handle (int)."""
     import torch
 
     if stream is None:
-        return torch.cuda.current_stream()
+        return torch.cuda.current_stream(device)
     if isinstance(stream, int):
-        return torch.cuda.ExternalStream(stream)
+        return torch.cuda.ExternalStream(stream, device=device)
+    if device is not None and stream.device != device:
+        raise ValueError(f"the stream belongs to {stream.device}, the call's tensors to {device}")
     return stream
+
+
+@contextlib.contextmanager
+def _on(device, stream):
+    """Runs a call with `device` current and its stream entered (so that
+    allocations made for the call belong to that stream); yields the stream."""
+    import torch
+
+    if device is None:
+        st = _torch_stream(stream)
+        with torch.cuda.stream(st):
+            yield st
+        return
+    with torch.cuda.device(device):
+        st = _torch_stream(stream, device)
+        with torch.cuda.stream(st):
+            yield st
 
 
 def _alloc_workspace(nbytes: int, device):
@@ -280,7 +311,7 @@ def _ws_args(workspace):
 # ---------------------------------------------------------------- entry points
 def muon_workspace_bytes(matrices, mu=0.95, lr=0.02, eps=1e-7, ns_steps=5, nesterov=False,
                          weight_decay=0.0) -> int:
-    entries, gd = _tensor_entries(matrices)
+    entries, gd, _ = _tensor_entries(matrices)
     arr = raw_matrix_array(entries)
     hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
     nbytes = lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp))
@@ -298,9 +329,7 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
     handle (int).  The kernels run on that stream; the caller orders it after
     the work that produced G (and W, B).  A workspace allocated here belongs
     to that stream."""
-    import torch
-
-    entries, gd = _tensor_entries(matrices)
+    entries, gd, device = _tensor_entries(matrices)
     if not entries:
         return
     arr = raw_matrix_array(entries)
@@ -308,10 +337,9 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
     need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
-    st = _torch_stream(stream)
-    with torch.cuda.stream(st):
+    with _on(device, stream) as st:
         if workspace is None:
-            workspace = _alloc_workspace(need, matrices[0][0].device)
+            workspace = _alloc_workspace(need, device)
         ws_ptr, ws_len = _ws_args(workspace)
         _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
                                ctypes.c_void_p(st.cuda_stream)))
@@ -323,28 +351,29 @@ def muon_step_static(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps
     nothing (no torch allocation, no hipMalloc).  Raises MuonError
     (MUON_ERR_WORKSPACE) when the call needs more than
     MUON_STATIC_WORKSPACE_BYTES of workspace."""
-    entries, gd = _tensor_entries(matrices)
+    entries, gd, device = _tensor_entries(matrices)
     if not entries:
         return
     arr = raw_matrix_array(entries)
     hp = hparams(mu, lr, eps, ns_steps, nesterov, gd, weight_decay)
-    st = _torch_stream(stream)
-    _check(lib().muon_step_static(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(st.cuda_stream)))
+    with _on(device, stream) as st:
+        _check(lib().muon_step_static(arr, len(entries), ctypes.byref(hp), ctypes.c_void_p(st.cuda_stream)))
 
 
 class MuonPlan:
     """A recorded Muon step on fixed buffers (muon_plan_create).  step()
     replays it; the plan keeps its tensors alive until close()."""
 
-    def __init__(self, handle, keep):
+    def __init__(self, handle, keep, device):
         self._h = handle
         self._keep = keep
+        self._device = device
 
     def step(self, stream=None) -> None:
         if not self._h:
             raise RuntimeError("the plan is closed")
-        st = _torch_stream(stream)
-        _check(lib().muon_plan_step(self._h, ctypes.c_void_p(st.cuda_stream)))
+        with _on(self._device, stream) as st:
+            _check(lib().muon_plan_step(self._h, ctypes.c_void_p(st.cuda_stream)))
 
     def close(self) -> None:
         """Frees the graph; call it once the last replay has completed."""
@@ -366,9 +395,7 @@ def muon_plan_create(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps
     """Records one Muon step on these (W, G, B[, scale]) tensors; returns a
     MuonPlan whose step() replays it (write each step's gradient into the
     same G tensors)."""
-    import torch
-
-    entries, gd = _tensor_entries(matrices)
+    entries, gd, device = _tensor_entries(matrices)
     if not entries:
         raise ValueError("a plan needs at least one matrix")
     arr = raw_matrix_array(entries)
@@ -376,15 +403,14 @@ def muon_plan_create(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps
     need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
-    st = _torch_stream(stream)
-    with torch.cuda.stream(st):
+    with _on(device, stream) as st:
         if workspace is None:
-            workspace = _alloc_workspace(need, matrices[0][0].device)
+            workspace = _alloc_workspace(need, device)
         ws_ptr, ws_len = _ws_args(workspace)
         h = ctypes.c_void_p()
         _check(lib().muon_plan_create(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
                                       ctypes.c_void_p(st.cuda_stream), ctypes.byref(h)))
-    return MuonPlan(h.value, (list(matrices), workspace))
+    return MuonPlan(h.value, (list(matrices), workspace), device)
 
 
 def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
@@ -394,15 +420,15 @@ def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1
     diag_records() after the stream is synchronised."""
     import torch
 
-    entries, gd = _tensor_entries(matrices)
+    entries, gd, device = _tensor_entries(matrices)
     n = len(entries)
-    st = _torch_stream(stream)
-    with torch.cuda.stream(st):
-        if diag is None:
-            dev = matrices[0][0].device if n else torch.device("cuda")
-            diag = torch.zeros(max(1, n), 8, dtype=torch.int32, device=dev)
+    if diag is not None:
         if not diag.is_cuda or diag.dtype != torch.int32 or not diag.is_contiguous() or diag.numel() < 8 * n:
             raise ValueError("diag must be a contiguous int32 GPU tensor of at least n x 8 entries")
+        device = _same_device(device, diag, "diag")
+    with _on(device, stream) as st:
+        if diag is None:
+            diag = torch.zeros(max(1, n), 8, dtype=torch.int32, device=st.device)
         if not entries:
             return diag
         arr = raw_matrix_array(entries)
@@ -411,7 +437,7 @@ def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1
         if need == 0:
             raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
         if workspace is None:
-            workspace = _alloc_workspace(need, matrices[0][0].device)
+            workspace = _alloc_workspace(need, device)
         ws_ptr, ws_len = _ws_args(workspace)
         _check(lib().muon_step_diag(arr, n, ctypes.byref(hp), ctypes.c_void_p(diag.data_ptr()), ws_ptr, ws_len,
                                     ctypes.c_void_p(st.cuda_stream)))
@@ -449,18 +475,25 @@ def muon_orthogonalize(Ms, Os=None, ns_steps=5, eps=1e-7, workspace=None, stream
     n = len(Ms)
     if n == 0:
         return []
-    st = _torch_stream(stream)
-    with torch.cuda.stream(st):
+    device = None
+    for k, M in enumerate(Ms):
+        if M.dtype != torch.float32 or not M.is_cuda:
+            raise ValueError(f"matrix {k}: M must be a float32 GPU tensor")
+        device = _same_device(device, M, f"matrix {k}: M")
+    with _on(device, stream) as st:
         if Os is None:
             Os = [torch.empty_like(M) for M in Ms]
+        if len(Os) != n:
+            raise ValueError("Os must hold one output per input")
         for k, (M, O) in enumerate(zip(Ms, Os)):
-            if M.dtype != torch.float32 or O.dtype != torch.float32 or not M.is_cuda or not O.is_cuda:
-                raise ValueError(f"matrix {k}: M and O must be float32 GPU tensors")
+            if O.dtype != torch.float32 or not O.is_cuda:
+                raise ValueError(f"matrix {k}: O must be a float32 GPU tensor")
+            _same_device(device, O, f"matrix {k}: O")
             if M.shape != O.shape or M.dim() != 2 or not M.is_contiguous() or not O.is_contiguous():
                 raise ValueError(f"matrix {k}: M and O must be contiguous 2-D tensors of one shape")
         need = muon_orthogonalize_workspace_bytes([M.shape for M in Ms], ns_steps)
         if workspace is None:
-            workspace = _alloc_workspace(need, Ms[0].device)
+            workspace = _alloc_workspace(need, device)
         mp = (ctypes.c_void_p * n)(*[M.data_ptr() for M in Ms])
         op = (ctypes.c_void_p * n)(*[O.data_ptr() for O in Os])
         rows = (ctypes.c_int64 * n)(*[M.shape[0] for M in Ms])
@@ -500,13 +533,11 @@ def muon_profile_read():
 def muon_copy_probe(src, dst, variant: int = 0, stream=None) -> None:
     """Streaming device copy src -> dst (same byte size) with the library's
     bandwidth yardstick kernel; the HBM ceiling of the bandwidth-bound stages."""
-    import torch
-
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes or not src.is_cuda or not dst.is_cuda:
         raise ValueError("src and dst must be GPU tensors of the same byte size")
-    st = _torch_stream(stream)
-    with torch.cuda.stream(st):
+    device = _same_device(_same_device(None, src, "src"), dst, "dst")
+    with _on(device, stream) as st:
         _check(lib().muon_copy_probe(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
                                      int(variant), ctypes.c_void_p(st.cuda_stream)))
 
@@ -520,13 +551,15 @@ def muon_qk_clip(matrices, tau: float, stream=None) -> None:
 
     n = len(matrices)
     arr = (muon_qk_clip_matrix_t * max(1, n))()
+    device = None
     for k, (W, head_dim, S) in enumerate(matrices):
         if not W.is_cuda or W.dtype != torch.float32 or W.dim() != 2 or not W.is_contiguous():
             raise ValueError(f"matrix {k}: W must be a contiguous float32 2-D GPU tensor")
         if not S.is_cuda or S.dtype != torch.float32 or not S.is_contiguous():
             raise ValueError(f"matrix {k}: max_logit must be a contiguous float32 GPU tensor")
+        device = _same_device(_same_device(device, W, f"matrix {k}: W"), S, f"matrix {k}: max_logit")
         if W.shape[0] % int(head_dim) or S.numel() != W.shape[0] // int(head_dim):
             raise ValueError(f"matrix {k}: rows must be heads * head_dim and max_logit hold one entry per head")
         arr[k] = muon_qk_clip_matrix_t(W.data_ptr(), W.shape[0], W.shape[1], int(head_dim), 0, S.data_ptr())
-    st = _torch_stream(stream)
-    _check(lib().muon_qk_clip(arr, n, float(tau), ctypes.c_void_p(st.cuda_stream)))
+    with _on(device, stream) as st:
+        _check(lib().muon_qk_clip(arr, n, float(tau), ctypes.c_void_p(st.cuda_stream)))

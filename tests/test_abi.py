@@ -392,3 +392,17 @@ def test_plan_create_rejects_before_any_gpu_call():
     assert h.value is None
     assert L.muon_plan_destroy(None) == mm.MUON_OK
     assert L.muon_plan_step(None, None) == mm.MUON_ERR_INVALID_ARG
+
+
+def test_binding_rejects_tensors_on_two_devices():
+    """Every tensor of a call must sit on one device (the binding makes it
+    the current device for the call); a second device is refused on the
+    host before anything runs."""
+    import torch
+
+    a = torch.empty(2, 2)
+    b = torch.empty(2, 2, device="meta")
+    assert bd._same_device(None, a, "W") == a.device
+    assert bd._same_device(a.device, a, "G") == a.device
+    with pytest.raises(ValueError, match="meta"):
+        bd._same_device(a.device, b, "B")
