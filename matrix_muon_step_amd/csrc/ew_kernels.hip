@@ -478,6 +478,15 @@ __global__ __launch_bounds__(256) void qk_clip_kernel(const ClipBatch b) {
 // prep pass, when a recorded plan replays a call without its table upload).
 __global__ void zero_counter_kernel(int32_t* p) { gst(p, 0); }
 
+// A small descriptor table passed by value (kernel argument) and stored into
+// the workspace.
+struct TableArg {
+  uint32_t w[kTableArgBytes / 4];
+};
+__global__ __launch_bounds__(256) void table_write_kernel(uint32_t* __restrict__ dst, const TableArg t, int nwords) {
+  for (int i = threadIdx.x; i < nwords; i += 256) gst(dst + i, t.w[i]);
+}
+
 // ---------------------------------------------------------------- copy probe
 // Streaming copy of n16 16-byte words, the yardstick of the bandwidth-bound
 // stages (one read and one write per byte, the momentum pass's mix).  Each
@@ -561,6 +570,17 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t n16, int varian
 hipError_t launch_qk_clip(const ClipBatch& b, hipStream_t s) {
   if (b.n <= 0 || b.prefix[b.n] <= 0) return hipSuccess;
   hipLaunchKernelGGL(qk_clip_kernel, dim3(b.prefix[b.n]), dim3(256), 0, s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_write(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes > static_cast<size_t>(kTableArgBytes) || bytes % 4 != 0) return hipErrorInvalidValue;
+  if (bytes == 0) return hipSuccess;
+  TableArg t{};
+  const uint32_t* w = static_cast<const uint32_t*>(src);
+  for (size_t i = 0; i < bytes / 4; ++i) t.w[i] = w[i];
+  hipLaunchKernelGGL(table_write_kernel, dim3(1), dim3(256), 0, s, static_cast<uint32_t*>(dst), t,
+                     static_cast<int>(bytes / 4));
   return hipGetLastError();
 }
 

@@ -491,6 +491,8 @@ muon_status_t hip_fail(hipError_t e, const char* where) {
 // sum the diagnostics and a last launch reduces them.
 // How execute() gets the descriptor table into the workspace.
 enum Upload {
+  // (a table of at most kTableArgBytes goes as the argument of one kernel
+  // in the first two modes)
   kUploadPinned,    // through the pinned staging ring (allocated on first use)
   kUploadPageable,  // straight from this call's host memory (the copy has
                     // consumed it when hipMemcpyAsync returns); allocates nothing
@@ -535,6 +537,8 @@ muon_status_t execute(Plan& plan, void* workspace, float mu, float eps, hipStrea
   } else {
     const std::vector<unsigned char> table = make_table(plan);
     e = stage(MUON_STAGE_UPLOAD, [&] {
+      if (table.size() <= static_cast<size_t>(kTableArgBytes))
+        return launch_table_write(workspace, table.data(), table.size(), s);
       return upload == kUploadPageable
                  ? hipMemcpyAsync(workspace, table.data(), table.size(), hipMemcpyHostToDevice, s)
                  : upload_table(table.data(), table.size(), workspace, s);
