@@ -348,23 +348,23 @@ def bench_workload(w, steps, warmup, ns_steps, dev, headline, diag_steps=0, copy
         # graph launch each: one plan per gradient buffer, each with its own
         # workspace (a plan's descriptor table lives there).
         gsets = grads if grads is not None else [[G for _, G, _, _ in mats]]
-        plans = [mm.muon_plan_create([(W, g[i], B, sc) for i, (W, _, B, sc) in enumerate(mats)],
+        recorded = [mm.muon_plan_create([(W, g[i], B, sc) for i, (W, _, B, sc) in enumerate(mats)],
                                      mu=w.mu, lr=w.lr, ns_steps=ns_steps) for g in gsets]
         for k in range(warmup):
-            plans[k % len(plans)].step()
+            recorded[k % len(recorded)].step()
         torch.cuda.synchronize()
         g0 = torch.cuda.Event(enable_timing=True)
         g1 = torch.cuda.Event(enable_timing=True)
         g0.record(stream)
         for k in range(steps):
-            plans[k % len(plans)].step()
+            recorded[k % len(recorded)].step()
         g1.record(stream)
         torch.cuda.synchronize()
         gms = g0.elapsed_time(g1) / steps
-        for pl in plans:
+        for pl in recorded:
             pl.close()
         rec["recorded_plan"] = {"ms_per_step": round(gms, 4), "us_per_step": round(gms * 1e3, 2),
-                                "steps_per_s": round(1000.0 / gms, 2), "plans": len(plans)}
+                                "steps_per_s": round(1000.0 / gms, 2), "plans": len(recorded)}
         log(f"[bench] {w.name}: recorded plan replays, {gms * 1e3:.1f} us/step")
     if not headline:
         del mats, ws, grads
