@@ -210,19 +210,50 @@ __device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf1
       if (tri_keep<DOFF>(i, j)) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// After the barrier of a step: queue a future step's loads into the ring
-// slot just released (`dst`) and read the first k16 half of the next stage
-// (`src`).  The two slots always differ; __restrict__ lets the compiler
-// order the LDS reads against the in-flight direct-to-LDS loads without a
-// blanket wait.
-template <class C, bool TR, bool SELF>
-__device__ __forceinline__ void refill_and_read(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
-                                                const Slots<C>& sl, int kfut, bool queue,
-                                                LAS unsigned char* __restrict__ dst,
-                                                const LAS unsigned char* __restrict__ src, int wave,
-                                                const Frag<C>& f, bf16x8_t (&a)[C::BMB], bf16x8_t (&b)[C::BNB]) {
-  if (queue) issue_loads<C, SELF>(Aop, Bop, sl, kfut, dst, wave);
-  read_half<C, TR>(src, 0, f, a, b);
+// Loads of one step with this wave's A-load count NA known at compile time
+// (every configuration gives each wave the same number of B loads).
+template <class C, bool SELF, int NA>
+__device__ __forceinline__ void issue_loads_n(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                              const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
+                                              int wave) {
+  static_assert(C::QB % C::NW == 0, "B loads are spread evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+    __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.aoff[i] + k0 * sl.kmul),
+                                     (LAS void*)(dst + (wave + i * C::NW) * 1024), 16, 0, 0);
+  if constexpr (!SELF) {
+#pragma unroll
+    for (int i = 0; i < C::QBMAX; ++i)
+      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.boff[i] + k0 * sl.kmul),
+                                       (LAS void*)(dst + C::OPA + (wave + i * C::NW) * 1024), 16, 0, 0);
+  }
+}
+
+// After the barrier of a step: the loads of step kt + NSTAGE into the slot
+// just released and the reads of the next stage's first half, one after each
+// of the second half's products, so that the matrix core starts right after
+// the barrier (issuing the loads first, with their address set-up, left it
+// idle; the loads' own latency is never waited for: their stage is needed
+// NSTAGE - 1 steps later).  The slot being filled and the stage being read
+// always differ, so the reads need no wait on the loads.
+template <class C, int DOFF, int NLOAD>
+__device__ __forceinline__ void interleave_post() {
+  constexpr int NR = tri_reads<C, DOFF>();
+  constexpr int NM = tri_products<C, DOFF>();
+  constexpr int NL = NLOAD < NM ? NLOAD : NM;
+  constexpr int NRD = (NM - NL) < NR ? (NM - NL) : NR;
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < NRD; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  if constexpr (NM > NL + NRD) __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NRD, 0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Scheduling pattern for a block of first-half products and second-half
@@ -277,11 +308,10 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    refill_and_read<C, TR, SELF>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, true, cur,
-                           lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, wave, f, fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
+    issue_loads_n<C, SELF, (SELF ? PER : PER - C::QBMAX)>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, cur, wave);
+    read_half<C, TR>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, f, fa0, fb0);
     mfma_half<C, DOFF>(fa1, fb1, acc);
-    __builtin_amdgcn_sched_barrier(0);
+    interleave_post<C, DOFF, PER>();
   }
   // Drain phase: no refills; the steps still in flight land one by one.
   for (; kt + 1 < nk; ++kt) {
