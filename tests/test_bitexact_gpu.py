@@ -174,6 +174,30 @@ def test_grouped_equals_one_by_one(mm):
         assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])
 
 
+@pytest.mark.parametrize("count", [10, 11])
+def test_descriptor_upload_paths_bit_exact(mm, count):
+    """A call's descriptor table reaches the workspace as a kernel argument
+    up to 3 KB (10 matrices) and by a host-to-device copy above (11): both
+    grouped calls equal one call per matrix (each a 512-byte table),
+    bit for bit, W and B."""
+    print(f"[case] descriptor upload, {count} matrices", flush=True)
+    shapes = [(96 + 32 * (i % 4), 200 + 40 * i) for i in range(count)]
+    host = []
+    for i, (r, c) in enumerate(shapes):
+        rng = np.random.default_rng([91, i])
+        host.append((0.02 * rng.standard_normal((r, c))).astype(np.float32))
+    gs = [synth.numpy_gradient(r, c, 8, 0.1, "f32", [91, i, 0, 1]) for i, (r, c) in enumerate(shapes)]
+    grouped = [(dev(w0), dev(g), torch.zeros(w0.shape, device="cuda"), 1.0) for w0, g in zip(host, gs)]
+    single = [(dev(w0), dev(g), torch.zeros(w0.shape, device="cuda"), 1.0) for w0, g in zip(host, gs)]
+    for _ in range(2):
+        mm.muon_step(grouped)
+        for mt in single:
+            mm.muon_step([mt])
+    torch.cuda.synchronize()
+    for a, b in zip(grouped, single):
+        assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])
+
+
 def test_repeat_runs_identical_and_resume(mm):
     """Same inputs twice give identical bits; 4 steps == 2 steps + host round
     trip of (W, B) + 2 steps."""
