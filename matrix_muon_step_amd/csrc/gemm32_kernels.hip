@@ -112,29 +112,6 @@ struct Slots {
   int kmul;
 };
 
-// SELF: a diagonal tile of a symmetric product, whose B operand is the same
-// panel as its A operand: only the A half of the stage is loaded and the B
-// fragments are read from it.
-template <class C, bool SELF>
-__device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
-                                            const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
-                                            int wave) {
-#pragma unroll
-  for (int i = 0; i < C::QAMAX; ++i) {
-    const int q = wave + i * C::NW;
-    if (i < C::QAMAX - 1 || q < C::QA)
-      __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.aoff[i] + k0 * sl.kmul),
-                                       (LAS void*)(dst + q * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < C::QBMAX; ++i) {
-    const int q = wave + i * C::NW;
-    if (!SELF && (i < C::QBMAX - 1 || q < C::QB))
-      __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.boff[i] + k0 * sl.kmul),
-                                       (LAS void*)(dst + C::OPA + q * 1024), 16, 0, 0);
-  }
-}
-
 // LDS fragment addresses of a lane (bytes within a stage).  Row-major
 // operands: one base per k16 half, +2048 per 32-row block.  Transposed
 // (Gram) operands: one base per 32-row block; a k16 half adds 16 k-rows.
@@ -210,13 +187,18 @@ __device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf1
       if (tri_keep<DOFF>(i, j)) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Loads of one step with this wave's A-load count NA known at compile time
-// (every configuration gives each wave the same number of B loads).
-template <class C, bool SELF, int NA>
-__device__ __forceinline__ void issue_loads_n(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
-                                              const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
-                                              int wave) {
+// Direct-to-LDS loads of one step: this wave's PER loads (1 KB each, one
+// per 16 operand rows).  Every configuration gives each wave the same
+// number of B loads, so its A loads are PER - QBMAX (PER on a diagonal tile
+// of a symmetric product, which loads the A half only, SELF); with the
+// counts fixed at compile time the loads are issued without branches.
+template <class C, bool SELF, int PER>
+__device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
+                                            const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
+                                            int wave) {
   static_assert(C::QB % C::NW == 0, "B loads are spread evenly over the waves");
+  constexpr int NA = SELF ? PER : PER - C::QBMAX;
+  static_assert(NA >= 1 && NA <= C::QAMAX, "A loads of a wave");
 #pragma unroll
   for (int i = 0; i < NA; ++i)
     __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.aoff[i] + k0 * sl.kmul),
@@ -290,7 +272,7 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
                                           const Frag<C>& f, f32x16_t (&acc)[C::BMB][C::BNB]) {
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
-    if (st < nk) issue_loads<C, SELF>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
+    if (st < nk) issue_loads<C, SELF, PER>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
   wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -308,7 +290,7 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_loads_n<C, SELF, (SELF ? PER : PER - C::QBMAX)>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, cur, wave);
+    issue_loads<C, SELF, PER>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, cur, wave);
     read_half<C, TR>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, f, fa0, fb0);
     mfma_half<C, DOFF>(fa1, fb1, acc);
     interleave_post<C, DOFF, PER>();
@@ -342,7 +324,7 @@ __device__ __forceinline__ void load_loop(const __bf16* __restrict__ Aop, const 
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave) {
 #pragma unroll
   for (int st = 0; st < C::NSTAGE; ++st)
-    if (st < nk) issue_loads<C, SELF>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
+    if (st < nk) issue_loads<C, SELF, PER>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
   wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
   __builtin_amdgcn_s_barrier();
   int kt = 0;
@@ -350,7 +332,7 @@ __device__ __forceinline__ void load_loop(const __bf16* __restrict__ Aop, const 
     MUON_WAIT_VM((C::NSTAGE - 2) * PER);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_loads<C, SELF>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, lds + (kt % C::NSTAGE) * C::STAGEB, wave);
+    issue_loads<C, SELF, PER>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, lds + (kt % C::NSTAGE) * C::STAGEB, wave);
   }
   for (; kt + 1 < nk; ++kt) {
     wait_newer<PER>(nk - 2 - kt);
@@ -1042,14 +1024,13 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
       }
     }
   }
+  // (B loads are spread evenly over the waves: per is PER_FULL or one less.)
   if (!self && bx_pad) {
     if (per == PER_FULL) load_loop<C, PER_FULL, false>(Aop, Bop, sl, nk, lds, wave);
-    else if (per == PER_FULL - 1) load_loop<C, PER_FULL - 1, false>(Aop, Bop, sl, nk, lds, wave);
-    else load_loop<C, PER_FULL - 2, false>(Aop, Bop, sl, nk, lds, wave);
+    else load_loop<C, PER_FULL - 1, false>(Aop, Bop, sl, nk, lds, wave);
   } else if (!self) {
     if (per == PER_FULL) main_loop<C, PER_FULL, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-    else if (per == PER_FULL - 1) main_loop<C, PER_FULL - 1, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
-    else main_loop<C, PER_FULL - 2, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
+    else main_loop<C, PER_FULL - 1, TR, false, -1>(Aop, Bop, sl, nk, lds, wave, fr, acc);
   }
   // The epilogue's LDS tiles overlap the ring: a barrier first (the BX
   // epilogues take it themselves, after requesting their first inputs).
