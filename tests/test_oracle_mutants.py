@@ -5,8 +5,11 @@ mistake: a flipped sign or swapped coefficient, a dropped term, a missing
 square, one iteration too few, no transpose back, the spectral instead of
 the Frobenius norm, no eps, a wrong momentum or Nesterov recurrence, a
 wrong update sign, an ignored per-matrix scale, weight decay applied
-to the new weights, or a QK-Clip that scales by tau/S instead of its root,
-scales column blocks, or clips every head.  With the mutant patched into ``oracle.muon_oracle``,
+to the new weights, a QK-Clip that scales by tau/S instead of its root,
+scales column blocks, or clips every head, diagnostics that report the
+direction's RMS as the update's, the old weights' RMS, the squared
+momentum norm or swapped non-finite flags, or a step that orthogonalises
+the gradient instead of the momentum.  With the mutant patched into ``oracle.muon_oracle``,
 the pins of ``test_oracle_pins`` run again, and at least one of them must
 fail.  The unpatched oracle passes every one of them.
 
@@ -22,6 +25,7 @@ import test_oracle_pins as pins
 from oracle import muon_oracle as orc
 
 A0, B0, C0 = orc.NS_COEFFS
+ORIG_DIAGNOSTICS = orc.diagnostics
 
 
 def _ns(update, steps_adj=0, back=True, normalize=None):
@@ -90,6 +94,30 @@ def _update(kind):
     return apply_update
 
 
+def _diagnostics(kind):
+    def diagnostics(W_old, W_new, M, O):
+        d = ORIG_DIAGNOSTICS(W_old, W_new, M, O)
+        root_n = np.sqrt(float(np.asarray(W_new).size))
+        if kind == "update from direction":
+            d["update_rms"] = d["direction_rms"]
+        elif kind == "old weights":
+            d["weight_rms"] = float(np.linalg.norm(np.asarray(W_old, np.float64)) / root_n)
+        elif kind == "squared norm":
+            d["momentum_norm"] = d["momentum_norm"] ** 2
+        elif kind == "flags swapped":
+            f = d["nonfinite"]
+            d["nonfinite"] = ((f & 1) << 1) | ((f >> 1) & 1)
+        return d
+
+    return diagnostics
+
+
+def _step_on_gradient(W, G, B, mu, lr, scale=1.0, ns_steps=5, nesterov=False, eps=1e-7, weight_decay=0.0):
+    B_new, _ = orc.momentum(B, G, mu, nesterov)
+    O = orc.newton_schulz(np.asarray(G, np.float64), ns_steps, eps)
+    return orc.apply_update(W, O, lr, scale, weight_decay), B_new, O
+
+
 def _qk_clip(kind):
     def qk_clip(W, head_dim, max_logits, tau):
         W = np.array(W, dtype=np.float64)
@@ -123,6 +151,11 @@ MUTANTS = {
     "QK-Clip factor without the root": ("qk_clip", _qk_clip("no root")),
     "QK-Clip on column blocks": ("qk_clip", _qk_clip("columns")),
     "QK-Clip on every head": ("qk_clip", _qk_clip("every head")),
+    "update RMS from the direction": ("diagnostics", _diagnostics("update from direction")),
+    "weight RMS of the old weights": ("diagnostics", _diagnostics("old weights")),
+    "squared momentum norm": ("diagnostics", _diagnostics("squared norm")),
+    "non-finite flags swapped": ("diagnostics", _diagnostics("flags swapped")),
+    "direction from the gradient": ("muon_step", _step_on_gradient),
 }
 
 
@@ -157,6 +190,13 @@ def _pin_calls():
                       dict(heads=heads, head_dim=head_dim, d_model=d_model)))
     calls += [(pins.test_qk_clip_threshold_above_every_head_is_identity, {}),
               (pins.test_qk_clip_power_of_four_factor, {})]
+    calls += [(pins.test_step_follows_the_momentum_not_the_gradient, {}),
+              (pins.test_diagnostics_rank_one_closed_form, {}),
+              (pins.test_diagnostics_decay_only, {})]
+    for n in (4, 9):
+        calls.append((pins.test_diagnostics_scaled_orthogonal, dict(n=n)))
+    for bad, where, flags in [(np.nan, "G", 3), (np.nan, "W", 2)]:
+        calls.append((pins.test_diagnostics_nonfinite_flags, dict(bad=bad, where=where, flags=flags)))
     return calls
 
 

@@ -264,6 +264,27 @@ def test_weight_decay_acts_on_old_weights_outside_direction():
     assert rel(W0, W - lr * s * svd_closed_form(G, 5)) <= 1e-12
 
 
+# ------------------------------------------------------------------ the step as a whole
+def test_step_follows_the_momentum_not_the_gradient():
+    # With a zero gradient the buffer still drives the step: B' = mu B and
+    # M = B', so for a rank-one B = s u v^T the direction is
+    # p^5(mu s / (mu s + eps)) u v^T and W' = W - lr * scale * that.  A step
+    # that orthogonalised G instead of the momentum would not move W.
+    rng = np.random.default_rng(16)
+    u = rng.standard_normal(5)
+    u /= np.linalg.norm(u)
+    v = rng.standard_normal(8)
+    v /= np.linalg.norm(v)
+    s, mu, lr, sc = 2.0, 0.9, 0.1, 0.5
+    Bm = s * np.outer(u, v)
+    W = rng.standard_normal((5, 8))
+    W2, B2, O = orc.muon_step(W, np.zeros((5, 8)), Bm, mu=mu, lr=lr, scale=sc)
+    q = p_iter(mu * s / (mu * s + EPS), 5)
+    assert np.allclose(B2, mu * Bm, rtol=0, atol=1e-15)
+    assert np.allclose(O, q * np.outer(u, v), rtol=0, atol=1e-12)
+    assert np.allclose(W2, W - lr * sc * q * np.outer(u, v), rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------ diagnostics
 def test_diagnostics_rank_one_closed_form():
     # M = s u v^T: ||M||_F = s, and every singular value of the normalised
