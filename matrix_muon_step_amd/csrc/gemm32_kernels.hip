@@ -386,15 +386,46 @@ __device__ __forceinline__ void unit_pos(int p, int lane, int& jl, int& il) {
   }
 }
 
+// The descriptor fields the BX epilogue uses, read once into registers.
+// Its stores go through pointers the compiler cannot tell apart from the
+// descriptor table, so a field read through the table would be loaded
+// again after every store, and waited for, which also drains the LDS reads
+// in flight.
+struct BxArgs {
+  const __bf16* hi_in;  // the pair this launch reads (X^T, ping-pong slot buf)
+  const __bf16* lo_in;
+  __bf16* hi_out;       // the new pair (slot buf ^ 1)
+  __bf16* lo_out;
+  float* W;
+  int64_t cols;
+  int32_t m, n, flags;
+  float lr_scale, lr_wd;
+};
+__device__ __forceinline__ BxArgs bx_args(const MatDesc& d, int buf) {
+  BxArgs a;
+  a.hi_in = pick(d.xt_hi, buf);
+  a.lo_in = pick(d.xt_lo, buf);
+  a.hi_out = pick(d.xt_hi, buf ^ 1);
+  a.lo_out = pick(d.xt_lo, buf ^ 1);
+  a.W = d.W;
+  a.cols = d.cols;
+  a.m = d.m;
+  a.n = d.n;
+  a.flags = d.flags;
+  a.lr_scale = d.lr_scale;
+  a.lr_wd = d.lr_wd;
+  return a;
+}
+
 // Row group p0 + q of a W-column unit at Gram-side column gi0 -> x[q].
 template <int W, int NG>
-__device__ __forceinline__ void bx_load_group(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
+__device__ __forceinline__ void bx_load_group(const BxArgs& d, int m_pad, int gi0, int wj0, int lane,
                                               XIn<NG>& x, int q, int p0) {
   int jl, il;
   unit_pos<W>(p0 + q, lane, jl, il);
   const int64_t off = static_cast<int64_t>(wj0 + jl) * m_pad + gi0 + il;
-  x.hi[q] = gld<uint4>(pick(d.xt_hi, buf) + off);
-  x.lo[q] = gld<uint4>(pick(d.xt_lo, buf) + off);
+  x.hi[q] = gld<uint4>(d.hi_in + off);
+  x.lo[q] = gld<uint4>(d.lo_in + off);
 }
 
 // Accumulators of one 32-row block -> T columns co..co+31.
@@ -464,7 +495,7 @@ __device__ __forceinline__ void upd1(float* wp, float o, float ls, float lwd, bo
 // requested group by group, so about one unit of inputs is in flight at
 // any time.  The X-major pass covers Gram-side columns 8 q0 .. 8 (q0 + NG).
 template <class C, int MODE, int W, int NG, int W2, int NG2, bool MERGED>
-__device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, int gi0, int wj0, int lane,
+__device__ __forceinline__ void bx_pass(const BxArgs& d, int m_pad, int gi0, int wj0, int lane,
                                         float* T, const XIn<NG>& x, int p0, int q0, DiagAcc& da,
                                         XIn<(NG2 > 0 ? NG2 : 1)>& nx, int gi0n, int p0n, float s1) {
   constexpr bool DG = MODE == BXD;
@@ -480,7 +511,7 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
     if constexpr (NG2 > 0) {
 #pragma unroll
       for (int q = p * NG2 / NG; q < (p + 1) * NG2 / NG; ++q)
-        bx_load_group<W2>(d, buf, m_pad, gi0n, wj0, lane, nx, q, p0n);
+        bx_load_group<W2>(d, m_pad, gi0n, wj0, lane, nx, q, p0n);
     }
     int jl, il;
     unit_pos<W>(p0 + p, lane, jl, il);
@@ -511,8 +542,8 @@ __device__ __forceinline__ void bx_pass(const MatDesc& d, int buf, int m_pad, in
       // The new pair is read again only by the next iteration's Gram
       // product, after the whole launch: stream it past the caches.
       const int64_t off = static_cast<int64_t>(gj) * m_pad + gi;
-      gst_stream(pick(d.xt_hi, buf ^ 1) + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
-      gst_stream(pick(d.xt_lo, buf ^ 1) + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
+      gst_stream(d.hi_out + off, make_uint4(nh[0], nh[1], nh[2], nh[3]));
+      gst_stream(d.lo_out + off, make_uint4(nl[0], nl[1], nl[2], nl[3]));
     } else if (tr) {
       // O^T = X'^T has W's orientation: W[gj][gi .. gi+7].
       if (gj < d.n) {
@@ -624,7 +655,7 @@ constexpr int kEarly = 4;
 // passes run while the next unit's inputs are requested, then the next
 // unit's accumulators go to T (after this unit's last read of T).
 template <class C, int MODE, int PH, int K>
-__device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
+__device__ __forceinline__ void bx_units(const BxArgs& d, int m_pad, int wi0, int wj0, int lane, float* T,
                                          const f32x16_t (&acc)[C::BMB][C::BNB],
                                          const XIn<Units<C, PH>::width(K) / 8>& cur, DiagAcc& da, float s1) {
   using U = Units<C, PH>;
@@ -633,13 +664,13 @@ __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, i
   if constexpr (K + 1 < U::N) {
     constexpr int W2 = U::width(K + 1);
     XIn<W2 / 8> nxt;
-    bx_pass<C, MODE, W, W / 8, W2, W2 / 8, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, nxt,
+    bx_pass<C, MODE, W, W / 8, W2, W2 / 8, false>(d, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, nxt,
                                                   wi0 + 32 * U::start(K + 1), 0, s1);
     bx_stage_unit<C, PH, K + 1>(lane, acc, T);
-    bx_units<C, MODE, PH, K + 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, nxt, da, s1);
+    bx_units<C, MODE, PH, K + 1>(d, m_pad, wi0, wj0, lane, T, acc, nxt, da, s1);
   } else {
     XIn<1> none;
-    bx_pass<C, MODE, W, W / 8, 32, 0, false>(d, buf, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, none, 0, 0, s1);
+    bx_pass<C, MODE, W, W / 8, 32, 0, false>(d, m_pad, gi0, wj0, lane, T, cur, 0, 0, da, none, 0, 0, s1);
   }
 }
 
@@ -647,19 +678,19 @@ __device__ __forceinline__ void bx_units(const MatDesc& d, int buf, int m_pad, i
 // accumulators go to T (freeing their registers), its inputs are
 // requested, then the units run in turn.
 template <class C, int MODE, int PH>
-__device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane, float* T,
+__device__ __forceinline__ void bx_epilogue(const BxArgs& d, int m_pad, int wi0, int wj0, int lane, float* T,
                                             const f32x16_t (&acc)[C::BMB][C::BNB], DiagAcc& da, float s1) {
   using U = Units<C, PH>;
   constexpr int W = U::width(0);
   XIn<W / 8> x0;
   constexpr int E = kEarly < W / 8 ? kEarly : W / 8;
 #pragma unroll
-  for (int q = 0; q < E; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
+  for (int q = 0; q < E; ++q) bx_load_group<W>(d, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
   __syncthreads();  // every wave is done with the ring that T overlaps
   bx_stage_unit<C, PH, 0>(lane, acc, T);
 #pragma unroll
-  for (int q = E; q < W / 8; ++q) bx_load_group<W>(d, buf, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
-  bx_units<C, MODE, PH, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, x0, da, s1);
+  for (int q = E; q < W / 8; ++q) bx_load_group<W>(d, m_pad, wi0 + 32 * U::start(0), wj0, lane, x0, q, 0);
+  bx_units<C, MODE, PH, 0>(d, m_pad, wi0, wj0, lane, T, acc, x0, da, s1);
 }
 
 // The epilogue of a wave pair that splits a tile's Gram-side rows at an odd
@@ -672,7 +703,7 @@ __device__ __forceinline__ void bx_epilogue(const MatDesc& d, int buf, int m_pad
 // pairs (0,1), (2,3), shared block 4; H = 1: pairs (1,2), (3,4), shared
 // block 0.
 template <class C, int MODE, int H>
-__device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, int m_pad, int wi0, int wj0, int lane,
+__device__ __forceinline__ void bx_epilogue_merged(const BxArgs& d, int m_pad, int wi0, int wj0, int lane,
                                                    float* T, float* Tm, const f32x16_t (&acc)[C::BMB][C::BNB],
                                                    DiagAcc& da, float s1) {
   static_assert(C::BMB == 5, "merged epilogue: two pairs and one shared block per wave");
@@ -681,22 +712,22 @@ __device__ __forceinline__ void bx_epilogue_merged(const MatDesc& d, int buf, in
   const int gm = wi0 + 32 * MB - 32 * H;  // first column of the shared line
   XIn<8> x0, x1;
 #pragma unroll
-  for (int q = 0; q < kEarly; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
+  for (int q = 0; q < kEarly; ++q) bx_load_group<64>(d, m_pad, g0, wj0, lane, x0, q, 0);
   __syncthreads();  // every wave is done with the ring that T overlaps
   bx_stage_acc<C>(lane, acc[I0], T);
   bx_stage_acc<C>(lane, acc[I0 + 1], T + 32);
 #pragma unroll
-  for (int q = kEarly; q < 8; ++q) bx_load_group<64>(d, buf, m_pad, g0, wj0, lane, x0, q, 0);
-  bx_pass<C, MODE, 64, 8, 64, 8, false>(d, buf, m_pad, g0, wj0, lane, T, x0, 0, 0, da, x1, g1, 0, s1);
+  for (int q = kEarly; q < 8; ++q) bx_load_group<64>(d, m_pad, g0, wj0, lane, x0, q, 0);
+  bx_pass<C, MODE, 64, 8, 64, 8, false>(d, m_pad, g0, wj0, lane, T, x0, 0, 0, da, x1, g1, 0, s1);
   bx_stage_acc<C>(lane, acc[I1], T);
   bx_stage_acc<C>(lane, acc[I1 + 1], T + 32);
   XIn<4> xm;
-  bx_pass<C, MODE, 64, 8, 64, 4, false>(d, buf, m_pad, g1, wj0, lane, T, x1, 0, 0, da, xm, gm, 4 * H, s1);
+  bx_pass<C, MODE, 64, 8, 64, 4, false>(d, m_pad, g1, wj0, lane, T, x1, 0, 0, da, xm, gm, 4 * H, s1);
   __syncthreads();
   bx_stage_acc<C>(lane, acc[MB], Tm + 32 * H);
   __syncthreads();
   XIn<1> none;
-  bx_pass<C, MODE, 64, 4, 32, 0, true>(d, buf, m_pad, gm, wj0, lane, Tm, xm, 4 * H, 4 * H, da, none, 0, 0, s1);
+  bx_pass<C, MODE, 64, 4, 32, 0, true>(d, m_pad, gm, wj0, lane, Tm, xm, 4 * H, 4 * H, da, none, 0, 0, s1);
 }
 
 // Epilogue of a symmetric product (Gram, polynomial) for one wave's sub-tile
@@ -1049,6 +1080,7 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
   const int wj0 = tj * C::BN + wc * C::WN;   // first global column
   if constexpr (MODE >= BXM) {
     float* T = reinterpret_cast<float*>(smem) + wave * (C::SLICEB / 4);
+    const BxArgs ba = bx_args(d, buf);
     DiagAcc da;
     if constexpr (C::NWM == 2 && C::WM % 64 == 32 && C::BM % 64 == 0) {
       // The two waves of a column share the line at row WM - 32 of the tile.
@@ -1062,14 +1094,14 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm32_kernel(
         __syncthreads();
         if (need_xmajor) __syncthreads();
       } else if (wr == 0)
-        bx_epilogue_merged<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
+        bx_epilogue_merged<C, MODE, 0>(ba, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
       else
-        bx_epilogue_merged<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
+        bx_epilogue_merged<C, MODE, 1>(ba, m_pad, wi0, wj0, lane, T, Tm, acc, da, s1);
     } else if (((wi0 >> 5) & 1) == 0) {
       // Wave-uniform: whether the wave's first block starts a 64-row line.
-      bx_epilogue<C, MODE, 0>(d, buf, m_pad, wi0, wj0, lane, T, acc, da, s1);
+      bx_epilogue<C, MODE, 0>(ba, m_pad, wi0, wj0, lane, T, acc, da, s1);
     } else {
-      bx_epilogue<C, MODE, 1>(d, buf, m_pad, wi0, wj0, lane, T, acc, da, s1);
+      bx_epilogue<C, MODE, 1>(ba, m_pad, wi0, wj0, lane, T, acc, da, s1);
     }
     if constexpr (MODE == BXD) diag_flush(da, d.diag_part + local * C::NW + wave, lane);
     return;

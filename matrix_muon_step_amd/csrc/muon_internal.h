@@ -23,10 +23,12 @@ __device__ __forceinline__ void gst(void* p, T v) {
 }
 
 // A 16-byte store that streams past the caches (nontemporal): for results
-// the next kernel reads only after gigabytes of other traffic.
+// the next kernel reads only after gigabytes of other traffic.  Through the
+// global address space, as gst.
 typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void gst_stream(void* p, uint4 v) {
-  __builtin_nontemporal_store((u32x4_nt_t){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt_t*>(p));
+  __builtin_nontemporal_store((u32x4_nt_t){v.x, v.y, v.z, v.w},
+                              (__attribute__((address_space(1))) u32x4_nt_t*)p);
 }
 
 // bf16 halves of a 32-bit word as float32 (low half = element 0).
