@@ -187,37 +187,40 @@ __device__ __forceinline__ void mfma_half(const bf16x8_t (&a)[C::BMB], const bf1
       if (tri_keep<DOFF>(i, j)) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Direct-to-LDS loads of one step: this wave's PER loads (1 KB each, one
-// per 16 operand rows).  Every configuration gives each wave the same
-// number of B loads, so its A loads are PER - QBMAX (PER on a diagonal tile
-// of a symmetric product, which loads the A half only, SELF); with the
-// counts fixed at compile time the loads are issued without branches.
-template <class C, bool SELF, int PER>
+// Direct-to-LDS loads of one step: loads FROM..TO-1 of this wave's PER
+// (1 KB each, one per 16 operand rows), A loads first.  Every configuration
+// gives each wave the same number of B loads, so its A loads are
+// PER - QBMAX (PER on a diagonal tile of a symmetric product, which loads the
+// A half only, SELF); with the counts fixed at compile time the loads are
+// issued without branches.
+template <class C, bool SELF, int PER, int FROM = 0, int TO = PER>
 __device__ __forceinline__ void issue_loads(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                             const Slots<C>& sl, int k0, LAS unsigned char* __restrict__ dst,
                                             int wave) {
   static_assert(C::QB % C::NW == 0, "B loads are spread evenly over the waves");
   constexpr int NA = SELF ? PER : PER - C::QBMAX;
   static_assert(NA >= 1 && NA <= C::QAMAX, "A loads of a wave");
+  static_assert(0 <= FROM && FROM <= TO && TO <= PER, "load range");
+  constexpr int A0 = FROM < NA ? FROM : NA, A1 = TO < NA ? TO : NA;
+  constexpr int B0 = (FROM > NA ? FROM : NA) - NA, B1 = (TO > NA ? TO : NA) - NA;
 #pragma unroll
-  for (int i = 0; i < NA; ++i)
+  for (int i = A0; i < A1; ++i)
     __builtin_amdgcn_global_load_lds((const GAS void*)(Aop + sl.aoff[i] + k0 * sl.kmul),
                                      (LAS void*)(dst + (wave + i * C::NW) * 1024), 16, 0, 0);
   if constexpr (!SELF) {
 #pragma unroll
-    for (int i = 0; i < C::QBMAX; ++i)
+    for (int i = B0; i < B1; ++i)
       __builtin_amdgcn_global_load_lds((const GAS void*)(Bop + sl.boff[i] + k0 * sl.kmul),
                                        (LAS void*)(dst + C::OPA + (wave + i * C::NW) * 1024), 16, 0, 0);
   }
 }
 
-// After the barrier of a step: the loads of step kt + NSTAGE into the slot
-// just released and the reads of the next stage's first half, one after each
-// of the second half's products, so that the matrix core starts right after
-// the barrier (issuing the loads first, with their address set-up, left it
-// idle; the loads' own latency is never waited for: their stage is needed
-// NSTAGE - 1 steps later).  The slot being filled and the stage being read
-// always differ, so the reads need no wait on the loads.
+// After the barrier of a step: the first loads of step kt + NSTAGE into the
+// slot just released and the reads of the next stage's first half, one after
+// each of the second half's products, so that the matrix core starts right
+// after the barrier (the loads' own latency is never waited for: their
+// stage is needed NSTAGE - 1 steps later).  The slot being filled and the
+// stage being read always differ, so the reads need no wait on the loads.
 template <class C, int DOFF, int NLOAD>
 __device__ __forceinline__ void interleave_post() {
   constexpr int NR = tri_reads<C, DOFF>();
@@ -238,21 +241,29 @@ __device__ __forceinline__ void interleave_post() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Scheduling pattern for a block of first-half products and second-half
-// fragment reads: one LDS read after each product, so the reads stream out
-// while the matrix core works and the products never wait on them.
-template <class C, int DOFF>
+// Scheduling pattern for a block of first-half products: one second-half
+// fragment read after each product, so the reads stream out while the matrix
+// core works and the products never wait on them, then NLOAD operand loads,
+// one after each remaining product.
+template <class C, int DOFF, int NLOAD = 0>
 __device__ __forceinline__ void interleave() {
   constexpr int NR = tri_reads<C, DOFF>();     // fragment reads of a half
   constexpr int NM = tri_products<C, DOFF>();  // products of a half
   constexpr int NP = NR < NM ? NR : NM;
+  constexpr int NL = (NM - NP) < NLOAD ? (NM - NP) : NLOAD;
 #pragma unroll
   for (int q = 0; q < NP; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
-  if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+#pragma unroll
+  for (int q = 0; q < NL; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one operand load
+  }
+  if constexpr (NM > NP + NL) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP - NL, 0);
   if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+  if constexpr (NLOAD > NL) __builtin_amdgcn_sched_group_barrier(0x010, NLOAD - NL, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -263,6 +274,15 @@ __device__ __forceinline__ void interleave() {
 // refilled with step kt+NSTAGE; the first half of stage kt+1 is read while
 // the second half of step kt is multiplied.  The barrier's wait is thus
 // covered by queued matrix-core work and the next step's first reads.
+// A wave's loads of a step are issued in two parts: H1 = PER/2 right after
+// the barrier that frees their slot, the rest among the first-half products
+// of the next step, before the next barrier.  Issued all at once after the
+// barrier, they held up the products queued behind them in the wave's
+// in-order stream, and the second wave of each SIMD, which the matrix core
+// serves after the first, finished its step alone (measured per wave with
+// the shader clock: 2040 cycles per step against 1280 of products per SIMD,
+// 1840 with the split).  The second part still lands NSTAGE - 2 steps before
+// its stage is read.
 // PER (this wave's loads per step) is a template parameter and the steady
 // phase has a fixed number of steps in flight, so the loop body has no
 // branches and every wait count is an immediate.
@@ -270,34 +290,62 @@ template <class C, int PER, bool TR, bool SELF, int DOFF>
 __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave,
                                           const Frag<C>& f, f32x16_t (&acc)[C::BMB][C::BNB]) {
+  constexpr int NS = C::NSTAGE;
+  constexpr int H1 = PER / 2;  // loads of a step issued right after its slot's barrier
+  // Prologue: steps 0..NS-2 whole, the first part of step NS-1 (its second
+  // part goes with the first products, as in the steady phase).
 #pragma unroll
-  for (int st = 0; st < C::NSTAGE; ++st)
+  for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue_loads<C, SELF, PER>(Aop, Bop, sl, st * 32, lds + st * C::STAGEB, wave);
-  wait_newer<PER>(nk - 1 < C::NSTAGE - 1 ? nk - 1 : C::NSTAGE - 1);
+  if (NS - 1 < nk) issue_loads<C, SELF, PER, 0, H1>(Aop, Bop, sl, (NS - 1) * 32, lds + (NS - 1) * C::STAGEB, wave);
+  if (nk >= NS) MUON_WAIT_VM((NS - 2) * PER + H1);
+  else wait_newer<PER>(nk - 1);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   bf16x8_t fa0[C::BMB], fb0[C::BNB], fa1[C::BMB], fb1[C::BNB];
   read_half<C, TR>(lds, 0, f, fa0, fb0);
   int kt = 0;
-  // Steady phase: every step refills its slot and leaves NSTAGE-2 later
-  // steps in flight.
-  for (; kt < nk - C::NSTAGE; ++kt) {
-    LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
+  // Steady phase: the first products of step kt carry the second part of
+  // step kt+NS-1 (into the slot freed at the previous barrier), the barrier
+  // is followed by the first part of step kt+NS.  Every wait leaves NS-2
+  // whole later steps in flight.
+  for (; kt < nk - NS; ++kt) {
+    LAS unsigned char* cur = lds + (kt % NS) * C::STAGEB;
     mfma_half<C, DOFF>(fa0, fb0, acc);
     read_half<C, TR>(cur, 1, f, fa1, fb1);
-    interleave<C, DOFF>();
-    MUON_WAIT_VM((C::NSTAGE - 2) * PER);
+    issue_loads<C, SELF, PER, H1, PER>(Aop, Bop, sl, (kt + NS - 1) * 32, lds + ((kt + NS - 1) % NS) * C::STAGEB,
+                                       wave);
+    interleave<C, DOFF, PER - H1>();
+    MUON_WAIT_VM((NS - 2) * PER);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage kt are done
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_loads<C, SELF, PER>(Aop, Bop, sl, (kt + C::NSTAGE) * 32, cur, wave);
-    read_half<C, TR>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, f, fa0, fb0);
+    issue_loads<C, SELF, PER, 0, H1>(Aop, Bop, sl, (kt + NS) * 32, cur, wave);
+    read_half<C, TR>(lds + ((kt + 1) % NS) * C::STAGEB, 0, f, fa0, fb0);
     mfma_half<C, DOFF>(fa1, fb1, acc);
-    interleave_post<C, DOFF, PER>();
+    interleave_post<C, DOFF, H1>();
+  }
+  // The step that carries the second part of the last step (nk >= NS).
+  if (kt + NS - 1 < nk) {
+    LAS unsigned char* cur = lds + (kt % NS) * C::STAGEB;
+    mfma_half<C, DOFF>(fa0, fb0, acc);
+    read_half<C, TR>(cur, 1, f, fa1, fb1);
+    issue_loads<C, SELF, PER, H1, PER>(Aop, Bop, sl, (kt + NS - 1) * 32, lds + ((kt + NS - 1) % NS) * C::STAGEB,
+                                       wave);
+    interleave<C, DOFF, PER - H1>();
+    MUON_WAIT_VM((NS - 2) * PER);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_half<C, TR>(lds + ((kt + 1) % NS) * C::STAGEB, 0, f, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half<C, DOFF>(fa1, fb1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    ++kt;
   }
   // Drain phase: no refills; the steps still in flight land one by one.
   for (; kt + 1 < nk; ++kt) {
-    LAS unsigned char* cur = lds + (kt % C::NSTAGE) * C::STAGEB;
+    LAS unsigned char* cur = lds + (kt % NS) * C::STAGEB;
     mfma_half<C, DOFF>(fa0, fb0, acc);
     read_half<C, TR>(cur, 1, f, fa1, fb1);
     interleave<C, DOFF>();
@@ -305,12 +353,12 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    read_half<C, TR>(lds + ((kt + 1) % C::NSTAGE) * C::STAGEB, 0, f, fa0, fb0);
+    read_half<C, TR>(lds + ((kt + 1) % NS) * C::STAGEB, 0, f, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_half<C, DOFF>(fa1, fb1, acc);
     __builtin_amdgcn_sched_barrier(0);
   }
-  read_half<C, TR>(lds + ((nk - 1) % C::NSTAGE) * C::STAGEB, 1, f, fa1, fb1);
+  read_half<C, TR>(lds + ((nk - 1) % NS) * C::STAGEB, 1, f, fa1, fb1);
   mfma_half<C, DOFF>(fa0, fb0, acc);
   mfma_half<C, DOFF>(fa1, fb1, acc);
 }
@@ -318,7 +366,9 @@ __device__ __forceinline__ void main_loop(const __bf16* __restrict__ Aop, const 
 // The main loop of a wave with nothing to compute: its sub-tile lies wholly
 // below the diagonal of a diagonal tile of a symmetric product (SELF: A half
 // only), or wholly in the padding rows of a BX tile.  Its share of the stage
-// loads, waits and barriers exactly as main_loop, and nothing else.
+// loads (each step's whole, right after the barrier that frees its slot, and
+// landed by the barrier that publishes it) and the same barriers as
+// main_loop, and nothing else.
 template <class C, int PER, bool SELF>
 __device__ __forceinline__ void load_loop(const __bf16* __restrict__ Aop, const __bf16* __restrict__ Bop,
                                           const Slots<C>& sl, int nk, LAS unsigned char* lds, int wave) {
