@@ -546,7 +546,6 @@ __global__ __launch_bounds__(C::kThreads, C::MINB) void ns_gemm_kernel(const Mat
     // 8g + j (j = (lane & 15) >> 2, the source-row index of the transposing
     // read), so output lane l gets row (l & 15) at 4 consecutive k; the
     // second read is 4 k-rows on.
-    constexpr int NC = T / 8;
     const int aa = lane & 3, j = (lane & 15) >> 2;
     const int krow = 8 * lq + j;
 #pragma unroll
