@@ -163,17 +163,21 @@ muon_status_t muon_step_static(const muon_matrix_t* mats, int64_t n, const muon_
  * at creation (create a new plan to change mu, lr, eps, ns_steps, nesterov,
  * weight decay or any scale).  Results are bit-identical to muon_step on
  * the same inputs.  The caller keeps every bound buffer, the workspace
- * included, alive and otherwise untouched until the plan is destroyed and
- * its last replay has completed; replays of one plan, like calls sharing a
- * workspace, must be ordered (one stream, or synchronised).  A plan belongs
+ * included, alive and otherwise untouched until muon_plan_destroy has
+ * returned (it waits for the last replay); replays of one plan are ordered
+ * one after another by the library, and other work on the bound buffers
+ * must be ordered against them by the caller.  A plan belongs
  * to the device current at creation; muon_plan_step on another device is
  * MUON_ERR_INVALID_ARG.  n must be >= 1.  The graph holds no memset node
  * (the per-step counter is zeroed by a kernel). */
 typedef struct muon_plan_s* muon_plan_t;
 muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t n, const muon_hparams_t* hp, void* workspace,
                                size_t workspace_bytes, void* stream, muon_plan_t* out);
+/* A replay on `stream` is ordered after the plan's previous replay,
+ * whichever stream that ran on. */
 muon_status_t muon_plan_step(muon_plan_t plan, void* stream);
-/* Frees the plan's graph (NULL is a no-op); does not wait for replays. */
+/* Waits for the plan's last replay to end, then frees its graph (NULL is a
+ * no-op); afterwards the caller may release the bound buffers. */
 muon_status_t muon_plan_destroy(muon_plan_t plan);
 
 /* Per-matrix diagnostics of one step: the layer-wise quantities that the

@@ -302,9 +302,16 @@ def _alloc_workspace(nbytes: int, device):
     return ws
 
 
-def _ws_args(workspace):
+def _ws_args(workspace, device=None):
+    """Pointer and byte size of a workspace tensor; a caller-supplied one must
+    be a contiguous GPU tensor on the call's device (the library can only
+    check its size and alignment)."""
     if workspace is None:
         return ctypes.c_void_p(0), 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("the workspace must be a contiguous GPU tensor")
+    if device is not None and workspace.device != device:
+        raise ValueError(f"the workspace is on {workspace.device}, the call's tensors on {device}")
     return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
 
@@ -340,7 +347,7 @@ def muon_step(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
     with _on(device, stream) as st:
         if workspace is None:
             workspace = _alloc_workspace(need, device)
-        ws_ptr, ws_len = _ws_args(workspace)
+        ws_ptr, ws_len = _ws_args(workspace, device)
         _check(lib().muon_step(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
                                ctypes.c_void_p(st.cuda_stream)))
 
@@ -364,10 +371,11 @@ class MuonPlan:
     """A recorded Muon step on fixed buffers (muon_plan_create).  step()
     replays it; the plan keeps its tensors alive until close()."""
 
-    def __init__(self, handle, keep, device):
+    def __init__(self, handle, keep, device, own_workspace=None):
         self._h = handle
         self._keep = keep
         self._device = device
+        self._own_ws = own_workspace  # allocated by muon_plan_create, freed with the plan
 
     def step(self, stream=None) -> None:
         if not self._h:
@@ -376,11 +384,13 @@ class MuonPlan:
             _check(lib().muon_plan_step(self._h, ctypes.c_void_p(st.cuda_stream)))
 
     def close(self) -> None:
-        """Frees the graph; call it once the last replay has completed."""
+        """Frees the graph once the last replay has ended (muon_plan_destroy
+        waits for it), then releases the tensors the plan kept alive."""
         if self._h:
             h, self._h = self._h, None
             _check(lib().muon_plan_destroy(h))
             self._keep = None
+            self._own_ws = None
 
     def __del__(self):
         try:
@@ -403,14 +413,15 @@ def muon_plan_create(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps
     need = int(lib().muon_workspace_bytes(arr, len(entries), ctypes.byref(hp)))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
+    own = None
     with _on(device, stream) as st:
         if workspace is None:
-            workspace = _alloc_workspace(need, device)
-        ws_ptr, ws_len = _ws_args(workspace)
+            workspace = own = _alloc_workspace(need, device)
+        ws_ptr, ws_len = _ws_args(workspace, device)
         h = ctypes.c_void_p()
         _check(lib().muon_plan_create(arr, len(entries), ctypes.byref(hp), ws_ptr, ws_len,
                                       ctypes.c_void_p(st.cuda_stream), ctypes.byref(h)))
-    return MuonPlan(h.value, (list(matrices), workspace), device)
+    return MuonPlan(h.value, (list(matrices), workspace), device, own)
 
 
 def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1e-7,
@@ -438,7 +449,7 @@ def muon_step_diag(matrices, mu=0.95, lr=0.02, ns_steps=5, nesterov=False, eps=1
             raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error())
         if workspace is None:
             workspace = _alloc_workspace(need, device)
-        ws_ptr, ws_len = _ws_args(workspace)
+        ws_ptr, ws_len = _ws_args(workspace, device)
         _check(lib().muon_step_diag(arr, n, ctypes.byref(hp), ctypes.c_void_p(diag.data_ptr()), ws_ptr, ws_len,
                                     ctypes.c_void_p(st.cuda_stream)))
     return diag
@@ -498,7 +509,7 @@ def muon_orthogonalize(Ms, Os=None, ns_steps=5, eps=1e-7, workspace=None, stream
         op = (ctypes.c_void_p * n)(*[O.data_ptr() for O in Os])
         rows = (ctypes.c_int64 * n)(*[M.shape[0] for M in Ms])
         cols = (ctypes.c_int64 * n)(*[M.shape[1] for M in Ms])
-        ws_ptr, ws_len = _ws_args(workspace)
+        ws_ptr, ws_len = _ws_args(workspace, device)
         _check(lib().muon_orthogonalize(mp, op, rows, cols, n, int(ns_steps), float(eps), ws_ptr, ws_len,
                                         ctypes.c_void_p(st.cuda_stream)))
     return Os
@@ -553,6 +564,8 @@ def muon_qk_clip(matrices, tau: float, stream=None) -> None:
     arr = (muon_qk_clip_matrix_t * max(1, n))()
     device = None
     for k, (W, head_dim, S) in enumerate(matrices):
+        if int(head_dim) < 1:
+            raise ValueError(f"matrix {k}: head_dim must be >= 1")
         if not W.is_cuda or W.dtype != torch.float32 or W.dim() != 2 or not W.is_contiguous():
             raise ValueError(f"matrix {k}: W must be a contiguous float32 2-D GPU tensor")
         if not S.is_cuda or S.dtype != torch.float32 or not S.is_contiguous():

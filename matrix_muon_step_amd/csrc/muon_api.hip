@@ -767,6 +767,7 @@ muon_status_t muon_step(const muon_matrix_t* mats, int64_t n, const muon_hparams
 struct muon_plan_s {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  hipEvent_t done = nullptr;  // recorded after each replay: the last one in flight
   int device = -1;
 };
 
@@ -828,9 +829,23 @@ muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t n, const muon_
     hipGraphDestroy(graph);
     return hip_fail(e, "hipGraphInstantiate");
   }
+  // Recorded once here (on the creation stream, idle since the table
+  // upload), then after every replay.
+  hipEvent_t done = nullptr;
+  e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+  if (e == hipSuccess) {
+    e = hipEventRecord(done, s);
+    if (e != hipSuccess) hipEventDestroy(done);
+  }
+  if (e != hipSuccess) {
+    hipGraphExecDestroy(exec);
+    hipGraphDestroy(graph);
+    return hip_fail(e, "plan event");
+  }
   muon_plan_s* p = new muon_plan_s;
   p->graph = graph;
   p->exec = exec;
+  p->done = done;
   p->device = dev;
   *out = p;
   g_last_error = before;
@@ -846,17 +861,29 @@ muon_status_t muon_plan_step(muon_plan_t plan, void* stream) {
   if (dev != plan->device)
     return fail(MUON_ERR_INVALID_ARG, "muon: the plan was recorded on device " + std::to_string(plan->device) +
                                           ", the current device is " + std::to_string(dev));
-  e = hipGraphLaunch(plan->exec, static_cast<hipStream_t>(stream));
+  // After the previous replay, on whatever stream it ran; the event then
+  // marks this one.
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  e = hipStreamWaitEvent(s, plan->done, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  e = hipGraphLaunch(plan->exec, s);
   if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  e = hipEventRecord(plan->done, s);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MUON_OK;
 }
 
 muon_status_t muon_plan_destroy(muon_plan_t plan) {
   g_last_error.clear();
   if (!plan) return MUON_OK;
+  // The graph is freed once its last replay (hence every replay) has ended.
+  hipError_t e0 = hipEventSynchronize(plan->done);
+  hipError_t e3 = hipEventDestroy(plan->done);
   hipError_t e1 = hipGraphExecDestroy(plan->exec);
   hipError_t e2 = hipGraphDestroy(plan->graph);
   delete plan;
+  if (e0 != hipSuccess) return hip_fail(e0, "hipEventSynchronize");
+  if (e3 != hipSuccess) return hip_fail(e3, "hipEventDestroy");
   if (e1 != hipSuccess) return hip_fail(e1, "hipGraphExecDestroy");
   if (e2 != hipSuccess) return hip_fail(e2, "hipGraphDestroy");
   return MUON_OK;

@@ -406,3 +406,24 @@ def test_binding_rejects_tensors_on_two_devices():
     assert bd._same_device(a.device, a, "G") == a.device
     with pytest.raises(ValueError, match="meta"):
         bd._same_device(a.device, b, "B")
+
+
+def test_binding_rejects_host_workspace():
+    """A caller-supplied workspace must be a contiguous GPU tensor on the
+    call's device: a host tensor would reach the kernels as a host address.
+    Refused on the host before anything runs."""
+    import torch
+
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bd._ws_args(torch.empty(1024, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bd._ws_args(torch.empty(1024, dtype=torch.uint8, device="meta"))
+    assert bd._ws_args(None)[1] == 0
+
+
+def test_binding_rejects_zero_head_dim():
+    import torch
+
+    W = torch.empty(4, 8)
+    with pytest.raises(ValueError, match="head_dim"):
+        bd.muon_qk_clip([(W, 0, torch.empty(1))], 1.0)

@@ -100,3 +100,35 @@ def test_two_plans_interleaved_on_a_side_stream(mm):
                 assert torch.equal(W, Wr) and torch.equal(B, Br)
     for p in plans:
         p.close()
+
+
+def test_plan_own_workspace_outlives_a_side_stream_replay(mm):
+    """A plan whose workspace the binding allocated (on the current stream)
+    is replayed on a side stream and closed without a synchronisation;
+    close() returns once the replay has ended (muon_plan_destroy waits for
+    it) and only then releases the workspace.  The current stream then
+    allocates a buffer of the workspace's size and fills it with a snapshot
+    of the workspace (so that, were the block handed out too early, the
+    replay would read stale iterates, never a different descriptor table).
+    The replay's results equal the eager step's."""
+    print("[case] plan workspace, side-stream replay, early close", flush=True)
+    shapes = [(768, 3072), (3072, 768), (256, 256)]
+    w0 = [(0.02 * np.random.default_rng([87, i]).standard_normal(s)).astype(np.float32) for i, s in enumerate(shapes)]
+    gs = [dev(g) for g in _grads(shapes, 0)]
+    ref = [(dev(w), g.clone(), torch.zeros(s, device="cuda")) for w, g, s in zip(w0, gs, shapes)]
+    mine = [(dev(w), g.clone(), torch.zeros(s, device="cuda")) for w, g, s in zip(w0, gs, shapes)]
+    mm.muon_step([(W, G, B, 1.0) for W, G, B in ref])
+    plan = mm.muon_plan_create([(W, G, B, 1.0) for W, G, B in mine])
+    torch.cuda.synchronize()
+    snapshot = plan._own_ws.clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    plan.step(stream=side)
+    plan.close()
+    del plan
+    filler = torch.empty_like(snapshot)
+    filler.copy_(snapshot)
+    torch.cuda.synchronize()
+    for (W, _, B), (Wr, _, Br) in zip(mine, ref):
+        assert torch.equal(W, Wr) and torch.equal(B, Br)
