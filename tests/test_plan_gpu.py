@@ -132,3 +132,40 @@ def test_plan_own_workspace_outlives_a_side_stream_replay(mm):
     torch.cuda.synchronize()
     for (W, _, B), (Wr, _, Br) in zip(mine, ref):
         assert torch.equal(W, Wr) and torch.equal(B, Br)
+
+
+def test_plan_replays_on_alternating_streams_are_ordered(mm):
+    """Replays of one plan on two streams, alternating, with no
+    synchronisation between them: the library orders each replay after the
+    previous one, so three replays equal three eager steps on the same
+    gradient."""
+    print("[case] plan replays alternating streams", flush=True)
+    shapes = [(512, 640), (640, 512), (96, 300)]
+    w0 = [(0.02 * np.random.default_rng([88, i]).standard_normal(s)).astype(np.float32) for i, s in enumerate(shapes)]
+    gs = [dev(g) for g in _grads(shapes, 1)]
+    ref = [(dev(w), g.clone(), torch.zeros(s, device="cuda")) for w, g, s in zip(w0, gs, shapes)]
+    mine = [(dev(w), g.clone(), torch.zeros(s, device="cuda")) for w, g, s in zip(w0, gs, shapes)]
+    for _ in range(3):
+        mm.muon_step([(W, G, B, 1.0) for W, G, B in ref])
+    plan = mm.muon_plan_create([(W, G, B, 1.0) for W, G, B in mine])
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    plan.step(stream=s1)
+    plan.step(stream=s2)
+    plan.step(stream=s1)
+    plan.close()
+    torch.cuda.synchronize()
+    for (W, _, B), (Wr, _, Br) in zip(mine, ref):
+        assert torch.equal(W, Wr) and torch.equal(B, Br)
+
+
+def test_plan_destroyed_without_replay(mm):
+    """A plan closed without any replay leaves its buffers untouched."""
+    shapes = [(256, 256)]
+    W = torch.full(shapes[0], 0.5, device="cuda")
+    G = torch.ones(shapes[0], device="cuda")
+    B = torch.zeros(shapes[0], device="cuda")
+    plan = mm.muon_plan_create([(W, G, B, 1.0)])
+    plan.close()
+    torch.cuda.synchronize()
+    assert torch.all(W == 0.5) and torch.all(B == 0)
