@@ -768,6 +768,7 @@ struct muon_plan_s {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   hipEvent_t done = nullptr;  // recorded after each replay: the last one in flight
+  hipStream_t last = nullptr;  // the stream `done` was last recorded on
   int device = -1;
 };
 
@@ -846,6 +847,7 @@ muon_status_t muon_plan_create(const muon_matrix_t* mats, int64_t n, const muon_
   p->graph = graph;
   p->exec = exec;
   p->done = done;
+  p->last = s;
   p->device = dev;
   *out = p;
   g_last_error = before;
@@ -861,15 +863,18 @@ muon_status_t muon_plan_step(muon_plan_t plan, void* stream) {
   if (dev != plan->device)
     return fail(MUON_ERR_INVALID_ARG, "muon: the plan was recorded on device " + std::to_string(plan->device) +
                                           ", the current device is " + std::to_string(dev));
-  // After the previous replay, on whatever stream it ran; the event then
-  // marks this one.
+  // After the previous replay: stream order covers one on this stream, an
+  // event wait one on another stream; the event then marks this one.
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  e = hipStreamWaitEvent(s, plan->done, 0);
-  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  if (s != plan->last) {
+    e = hipStreamWaitEvent(s, plan->done, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
   e = hipGraphLaunch(plan->exec, s);
   if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
   e = hipEventRecord(plan->done, s);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  plan->last = s;
   return MUON_OK;
 }
 
